@@ -1,0 +1,163 @@
+"""Pins for the oracle's Markov-head draft (CPU only).
+
+Each test checks the oracle against something other than itself: an explicit
+V x V transition product, pure-Python loops on tiny sizes, one-hot special
+cases, a planted Markov chain whose tokens are known by construction, and the
+Gumbel-max theorem (sampled frequencies follow softmax(z / T)).
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import dspark_oracle as O
+from draft_head_step_amd.inputs import CONFIGS, f32_to_bf16_bits, make_workload
+
+
+def _bf16(x):
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_bf16_decode_exact():
+    vals = np.array([1.0, -2.5, 5.0, 0.0, 3.140625, -0.0078125], dtype=np.float32)
+    assert np.array_equal(O.bf16_to_f64(_bf16(vals)), vals.astype(np.float64))
+
+
+def test_bias_is_row_of_explicit_transition_matrix():
+    # The Markov bias W1[x] W2 is row x of the full V x V low-rank transition matrix W1 W2.
+    wl = make_workload(CONFIGS["tiny"])
+    W1 = O.bf16_to_f64(wl["W1"])                                   # [V, r]
+    W2 = O.bf16_to_f64(wl["W2"]).T                                 # [r, V]
+    M = W1 @ W2                                                    # [V, V] dense transition
+    prev = np.array([0, 17, 4095, 2048, 17], dtype=np.int64)
+    got = O.markov_bias(wl["W1"], wl["W2"], prev)
+    np.testing.assert_allclose(got, M[prev], rtol=0, atol=1e-15)
+
+
+def test_bias_pure_python_loops_and_storage_convention():
+    # W2 is stored [V, r]: element (i, v) of the r x V matrix lives at flat index v*r + i.
+    rng = np.random.default_rng(7)
+    V, r = 7, 3
+    W1 = _bf16(rng.integers(-4, 5, size=(V, r)))
+    W2 = _bf16(rng.integers(-4, 5, size=(V, r)))
+    w1 = O.bf16_to_f64(W1)
+    flat = O.bf16_to_f64(W2).reshape(-1)
+    for x in range(V):
+        want = [sum(w1[x, i] * flat[v * r + i] for i in range(r)) for v in range(V)]
+        got = O.markov_bias(W1, W2, np.array([x]))[0]
+        assert list(got) == want
+
+
+def test_one_hot_embedding_row_selects_w2_row():
+    rng = np.random.default_rng(3)
+    V, r = 64, 16
+    W2 = _bf16(rng.standard_normal((V, r)))
+    for i in (0, 5, 15):
+        W1 = np.zeros((V, r), dtype=np.float32)
+        W1[11, i] = 1.0
+        got = O.markov_bias(_bf16(W1), W2, np.array([11]))[0]
+        assert np.array_equal(got, O.bf16_to_f64(W2)[:, i])       # row i of the r x V matrix
+
+
+def test_planted_chain_follows_permutation():
+    # W1 = identity embedding, W2 row t puts +5 on pi(t): the draft must walk
+    # pi(anchor), pi^2(anchor), ...; a wrong index (x_k instead of x_{k-1}) or a
+    # transposed W2 (which would follow pi^-1) breaks it.
+    V = r = 32
+    gamma = 6
+    rng = np.random.default_rng(11)
+    pi = rng.permutation(V)
+    W1 = np.eye(V, r, dtype=np.float32)
+    W2 = np.zeros((V, r), dtype=np.float32)     # stored [V, r]: (i, v) at [v, i]
+    for t in range(V):
+        W2[pi[t], t] = 5.0
+    R = 5
+    base = rng.uniform(-1, 1, size=(R, gamma, V)).astype(np.float32)
+    anchors = rng.integers(0, V, size=R).astype(np.int32)
+    out = O.markov_draft(_bf16(W1), _bf16(W2), base, anchors)
+    for m in range(R):
+        x = anchors[m]
+        for k in range(gamma):
+            x = pi[x]
+            assert out["tokens"][m, k] == x
+
+
+def test_zero_w1_gives_plain_argmax_of_base():
+    rng = np.random.default_rng(5)
+    R, g, V, r = 3, 4, 50, 8
+    W1 = np.zeros((V, r), dtype=np.uint16)
+    W2 = _bf16(rng.standard_normal((V, r)))
+    base = rng.standard_normal((R, g, V)).astype(np.float32)
+    out = O.markov_draft(W1, W2, base, np.array([1, 2, 3], dtype=np.int32))
+    for m, k in itertools.product(range(R), range(g)):
+        row = [float(v) for v in base[m, k]]
+        best = max(range(V), key=lambda v: (row[v], -v))
+        assert out["tokens"][m, k] == best
+
+
+def test_argmax_ties_go_to_smallest_id():
+    z = np.array([[0.0, 3.0, 1.0, 3.0, 3.0]])
+    x, _, margin = O.select(z, O.GREEDY)
+    assert x[0] == 1 and margin[0] == 0.0
+
+
+def test_margin_is_top1_minus_top2():
+    z = np.array([[0.5, 2.0, -1.0, 1.25]])
+    _, _, margin = O.select(z, O.GREEDY)
+    assert margin[0] == 0.75
+
+
+@pytest.mark.parametrize("T", [1.0, 0.5])
+def test_gumbel_max_follows_softmax(T):
+    # Gumbel-max theorem: argmax(z/T + G) ~ softmax(z/T).  Chi-square goodness of fit.
+    from draft_head_step_amd.inputs import open_uniforms
+    from scipy.stats import chi2
+    rng = np.random.Generator(np.random.PCG64(123))
+    V, n = 8, 400_000
+    z = np.array([0.0, 1.0, -0.5, 2.0, 0.3, -2.0, 1.5, 0.7])
+    u = open_uniforms(rng, (n, V))
+    x, _, _ = O.select(np.broadcast_to(z, (n, V)), O.SAMPLE, T, u)
+    p = np.exp(z / T) / np.exp(z / T).sum()
+    counts = np.bincount(x, minlength=V)
+    stat = ((counts - n * p) ** 2 / (n * p)).sum()
+    assert stat < chi2.ppf(1 - 1e-4, V - 1)
+
+
+def test_low_temperature_sampling_reduces_to_greedy():
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal((20, 100)) * 3
+    from draft_head_step_amd.inputs import open_uniforms
+    u = open_uniforms(np.random.Generator(np.random.PCG64(1)), (20, 100))
+    xg, _, _ = O.select(z, O.GREEDY)
+    xs, _, _ = O.select(z, O.SAMPLE, 1e-6, u)
+    assert np.array_equal(xg, xs)
+
+
+def test_gumbel_extremes_are_finite():
+    u = np.array([2.0 ** -24, 0.5, 1 - 2.0 ** -24], dtype=np.float32)
+    g = O.gumbel(u)
+    assert np.all(np.isfinite(g)) and g[0] < g[1] < g[2]
+    # closed forms: -ln(-ln(1/2)) = -ln(ln 2)
+    assert g[1] == pytest.approx(-np.log(np.log(2.0)), abs=1e-15)
+
+
+def test_forced_replay_uses_given_previous_tokens():
+    wl = make_workload(CONFIGS["tiny"], w_std=0.3)
+    own = O.markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"])
+    again = O.markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"], prev_tokens=own["tokens"])
+    assert np.array_equal(own["tokens"], again["tokens"])
+    # Force a different x_1 for request 0: step 2 must use it.
+    forced = own["tokens"].copy()
+    forced[0, 0] = (forced[0, 0] + 1) % wl["V"]
+    rep = O.markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"], prev_tokens=forced, keep_bias=True)
+    want = O.markov_bias(wl["W1"], wl["W2"], np.array([forced[0, 0]]))[0]
+    np.testing.assert_array_equal(rep["bias"][0, 1], want)
+
+
+def test_bias_dominant_variant_moves_the_argmax():
+    # In the bias-dominant tiny workload the Markov term changes some tokens
+    # relative to argmax(base): the head is not a no-op there.
+    wl = make_workload(CONFIGS["tiny"], w_std=0.3)
+    out = O.markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"])
+    plain = np.argmax(wl["base"], axis=2)
+    assert (out["tokens"] != plain).any()
