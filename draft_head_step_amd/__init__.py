@@ -1,0 +1,251 @@
+"""DSpark drafter hot path on MI355X: thin Python binding over libdspark.so.
+
+The binding only marshals arguments: it checks tensor dtypes, devices and
+shapes, allocates outputs and workspaces with PyTorch (device memory is all
+PyTorch is used for), and calls the C ABI declared in include/dspark.h on the
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels.  If the library is missing or fails to load, every entry point
+raises: there is no fallback path.
+
+Entry points (same names as the C ABI):
+  dspark_markov_draft, dspark_confidence, dspark_survival, dspark_schedule,
+  dspark_markov_draft_workspace, dspark_schedule_workspace.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "DsparkError", "GREEDY", "SAMPLE", "lib", "lib_path",
+    "dspark_markov_draft", "dspark_confidence", "dspark_survival", "dspark_schedule",
+    "dspark_markov_draft_workspace", "dspark_schedule_workspace", "ScheduleInfo",
+]
+
+GREEDY = 0
+SAMPLE = 1
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.environ.get("DSPARK_LIB", os.path.join(_PKG, "libdspark.so"))
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({_status_name(status)}): {detail}")
+        self.status = status
+
+
+class StepEvents(ctypes.Structure):
+    _fields_ = [("begin", ctypes.POINTER(ctypes.c_void_p)),
+                ("end", ctypes.POINTER(ctypes.c_void_p)),
+                ("count", ctypes.c_int)]
+
+
+class ScheduleInfo(ctypes.Structure):
+    """Host mirror of dspark_schedule_info (32 bytes)."""
+    _fields_ = [("B_star", ctypes.c_int32), ("m_star", ctypes.c_int32),
+                ("tau_fx", ctypes.c_uint64), ("tau", ctypes.c_double), ("theta", ctypes.c_double)]
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().dspark_status_string(s).decode()
+    except Exception:  # noqa: BLE001 - only used to format an error
+        return "?"
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdspark.so once; raise if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"libdspark.so not found at {path}; build it with "
+                          "`python -m draft_head_step_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.dspark_status_string.argtypes = [i32]
+    L.dspark_status_string.restype = ctypes.c_char_p
+    L.dspark_last_error.argtypes = []
+    L.dspark_last_error.restype = ctypes.c_char_p
+    L.dspark_markov_draft_workspace.argtypes = [i32, i32, i32, i32]
+    L.dspark_markov_draft_workspace.restype = sz
+    L.dspark_markov_draft.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                      vp, sz, ctypes.POINTER(StepEvents), vp]
+    L.dspark_markov_draft.restype = i32
+    L.dspark_confidence.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.dspark_confidence.restype = i32
+    L.dspark_survival.argtypes = [vp, i32, i32, vp, vp]
+    L.dspark_survival.restype = i32
+    L.dspark_schedule_workspace.argtypes = [i32, i32]
+    L.dspark_schedule_workspace.restype = sz
+    L.dspark_schedule.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.dspark_schedule.restype = i32
+    _LIB = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DsparkError(status, where, lib().dspark_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, dtypes, shape, device):
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def dspark_markov_draft_workspace(R: int, gamma: int, V: int, r: int) -> int:
+    return int(lib().dspark_markov_draft_workspace(R, gamma, V, r))
+
+
+def dspark_schedule_workspace(R: int, gamma: int) -> int:
+    return int(lib().dspark_schedule_workspace(R, gamma))
+
+
+def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: float = 1.0,
+                        uniforms=None, tokens=None, bias_out=None, workspace=None,
+                        events=None, stream=None):
+    """gamma-step Markov-head draft.  Shapes: W1, W2 [V, r] bf16; base [R, gamma, V] fp32;
+    anchors [R] int32; uniforms [R, gamma, V] fp32 (SAMPLE only).  Returns tokens [R, gamma] int32.
+
+    ``events`` is an optional pair (begin, end) of sequences of hipEvent_t handles (ints),
+    recorded around each step's fused kernel."""
+    torch = _torch()
+    L = lib()
+    R, gamma, V = base.shape
+    r = W1.shape[1]
+    dev = base.device
+    _need(W1, "W1", _bf16_types(), (V, r), dev)
+    _need(W2, "W2", _bf16_types(), (V, r), dev)
+    _need(base, "base", (torch.float32,), (R, gamma, V), dev)
+    _need(anchors, "anchors", (torch.int32,), (R,), dev)
+    if uniforms is not None:
+        _need(uniforms, "uniforms", (torch.float32,), (R, gamma, V), dev)
+    if tokens is None:
+        tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+    _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
+    if bias_out is not None:
+        _need(bias_out, "bias_out", (torch.float32,), (R, gamma, V), dev)
+    need = int(L.dspark_markov_draft_workspace(R, gamma, V, r))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ev = None
+    if events is not None:
+        b, e = events
+        ev = StepEvents((ctypes.c_void_p * len(b))(*b), (ctypes.c_void_p * len(e))(*e),
+                        min(len(b), len(e)))
+    st = L.dspark_markov_draft(_ptr(W1), _ptr(W2), _ptr(base), _ptr(anchors), R, gamma, V, r,
+                               int(mode), float(temperature), _ptr(uniforms), _ptr(tokens),
+                               _ptr(bias_out), _ptr(workspace), workspace.numel(),
+                               ctypes.byref(ev) if ev is not None else None, _stream(stream))
+    _check(st, "dspark_markov_draft")
+    return tokens
+
+
+def dspark_confidence(h, W1, anchors, tokens, w_conf, sts_temp=None, conf=None, surv=None,
+                      want_surv: bool = True, stream=None):
+    """Confidence head + STS (+ survival).  Returns (conf [R, gamma] fp32, surv or None)."""
+    torch = _torch()
+    L = lib()
+    R, gamma, d = h.shape
+    V, r = W1.shape
+    dev = h.device
+    _need(h, "h", _bf16_types(), (R, gamma, d), dev)
+    _need(W1, "W1", _bf16_types(), (V, r), dev)
+    _need(anchors, "anchors", (torch.int32,), (R,), dev)
+    _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
+    _need(w_conf, "w_conf", (torch.float32,), (d + r,), dev)
+    if sts_temp is not None:
+        _need(sts_temp, "sts_temp", (torch.float32,), (gamma,), dev)
+    if conf is None:
+        conf = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    _need(conf, "conf", (torch.float32,), (R, gamma), dev)
+    if surv is None and want_surv:
+        surv = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    if surv is not None:
+        _need(surv, "surv", (torch.float32,), (R, gamma), dev)
+    st = L.dspark_confidence(_ptr(h), _ptr(W1), _ptr(anchors), _ptr(tokens), _ptr(w_conf),
+                             _ptr(sts_temp), R, gamma, d, V, r, _ptr(conf), _ptr(surv),
+                             _stream(stream))
+    _check(st, "dspark_confidence")
+    return conf, surv
+
+
+def dspark_survival(conf, surv=None, stream=None):
+    torch = _torch()
+    R, gamma = conf.shape
+    _need(conf, "conf", (torch.float32,), (R, gamma), conf.device)
+    if surv is None:
+        surv = torch.empty_like(conf)
+    _need(surv, "surv", (torch.float32,), (R, gamma), conf.device)
+    _check(lib().dspark_survival(_ptr(conf), R, gamma, _ptr(surv), _stream(stream)),
+           "dspark_survival")
+    return surv
+
+
+def dspark_schedule(surv, sps, lengths=None, order=None, want_order: bool = False, info=None,
+                    want_info: bool = False, workspace=None, stream=None):
+    """Prefix scheduler.  Returns (lengths [R] int32, order [R*gamma] int32 or None,
+    info uint8[32] device tensor or None; decode with schedule_info())."""
+    torch = _torch()
+    L = lib()
+    R, gamma = surv.shape
+    dev = surv.device
+    _need(surv, "surv", (torch.float32,), (R, gamma), dev)
+    if sps.dim() != 1 or sps.dtype != torch.float32 or sps.device != dev or not sps.is_contiguous():
+        raise ValueError("sps must be a contiguous 1-D float32 tensor on the same device")
+    if lengths is None:
+        lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+    _need(lengths, "lengths", (torch.int32,), (R,), dev)
+    if order is None and want_order:
+        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
+    if order is not None:
+        _need(order, "order", (torch.int32,), (R * gamma,), dev)
+    if info is None and want_info:
+        info = torch.zeros((32,), dtype=torch.uint8, device=dev)
+    need = int(L.dspark_schedule_workspace(R, gamma))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = L.dspark_schedule(_ptr(surv), _ptr(sps), R, gamma, sps.numel(), _ptr(lengths),
+                           _ptr(order), _ptr(info), _ptr(workspace), workspace.numel(),
+                           _stream(stream))
+    _check(st, "dspark_schedule")
+    return lengths, order, info
+
+
+def schedule_info(info_tensor) -> ScheduleInfo:
+    """Copy a device dspark_schedule_info to the host (synchronises)."""
+    raw = bytes(info_tensor.cpu().numpy().tobytes())
+    return ScheduleInfo.from_buffer_copy(raw)

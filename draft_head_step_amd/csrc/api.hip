@@ -1,0 +1,138 @@
+// C ABI entry points: host-side argument validation, then kernel launches.
+// Every check below runs before anything is enqueued; a failing check returns
+// a status and leaves the stream untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "dspark_internal.h"
+
+namespace dspark {
+namespace {
+thread_local char g_last_error[512] = "";
+}  // namespace
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dspark_status fail(dspark_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dspark_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DSPARK_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return DSPARK_OK;
+}
+
+}  // namespace dspark
+
+using dspark::aligned16;
+using dspark::fail;
+
+extern "C" {
+
+const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_EINVAL: return "invalid argument";
+    case DSPARK_EWORKSPACE: return "workspace too small";
+    case DSPARK_EUNSUPPORTED: return "unsupported size";
+    case DSPARK_EDEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* dspark_last_error(void) { return dspark::g_last_error; }
+
+size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r) {
+  if (R <= 0 || gamma <= 0 || V < 2 || r <= 0) return 0;
+  return dspark::plan_markov(R, gamma, V, r).ws_bytes;
+}
+
+dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                  const int32_t* anchors, int R, int gamma, int V, int r,
+                                  int mode, float temperature, const float* uniforms,
+                                  int32_t* tokens, float* bias_out, void* workspace,
+                                  size_t ws_bytes, const dspark_step_events* events,
+                                  void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!W1 || !W2 || !base || !anchors || !tokens)
+    return fail(DSPARK_EINVAL, "markov_draft: NULL required pointer");
+  if (R <= 0 || gamma <= 0 || r <= 0 || V < 2)
+    return fail(DSPARK_EINVAL, "markov_draft: need R, gamma, r > 0 and V >= 2 (got %d %d %d %d)",
+                R, gamma, r, V);
+  if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLE)
+    return fail(DSPARK_EINVAL, "markov_draft: unknown mode %d", mode);
+  if (mode == DSPARK_SAMPLE) {
+    if (!uniforms) return fail(DSPARK_EINVAL, "markov_draft: SAMPLE needs uniforms");
+    if (!(temperature > 0.0f) || !isfinite(temperature))
+      return fail(DSPARK_EINVAL, "markov_draft: SAMPLE needs a positive finite temperature");
+  } else if (uniforms) {
+    return fail(DSPARK_EINVAL, "markov_draft: uniforms given in GREEDY mode");
+  }
+  if (!aligned16(W1) || !aligned16(W2))
+    return fail(DSPARK_EINVAL, "markov_draft: W1 and W2 must be 16-byte aligned");
+  if (r > DSPARK_MAX_RANK || r % 16 != 0)
+    return fail(DSPARK_EUNSUPPORTED, "markov_draft: r must be a multiple of 16 and <= %d (got %d)",
+                DSPARK_MAX_RANK, r);
+  if (events && (events->count < gamma))
+    return fail(DSPARK_EINVAL, "markov_draft: events->count < gamma");
+  const size_t need = dspark_markov_draft_workspace(R, gamma, V, r);
+  if (!workspace || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "markov_draft: workspace needs %zu bytes (got %zu)", need,
+                workspace ? ws_bytes : (size_t)0);
+  return dspark::launch_markov_draft(W1, W2, base, anchors, R, gamma, V, r, mode, temperature,
+                                     uniforms, tokens, bias_out, workspace, events,
+                                     reinterpret_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
+                                const int32_t* tokens, const float* w_conf,
+                                const float* sts_temp, int R, int gamma, int d, int V, int r,
+                                float* conf, float* surv, void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!h || !W1 || !anchors || !tokens || !w_conf || !conf)
+    return fail(DSPARK_EINVAL, "confidence: NULL required pointer");
+  if (R <= 0 || gamma <= 0 || d <= 0 || V <= 0 || r <= 0)
+    return fail(DSPARK_EINVAL, "confidence: sizes must be positive");
+  return dspark::launch_confidence(h, W1, anchors, tokens, w_conf, sts_temp, R, gamma, d, V, r,
+                                   conf, surv, reinterpret_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_survival(const float* conf, int R, int gamma, float* surv, void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!conf || !surv) return fail(DSPARK_EINVAL, "survival: NULL required pointer");
+  if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "survival: sizes must be positive");
+  if (conf == surv) return fail(DSPARK_EINVAL, "survival: conf and surv may not alias");
+  return dspark::launch_survival(conf, R, gamma, surv, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t dspark_schedule_workspace(int R, int gamma) {
+  if (R <= 0 || gamma <= 0) return 0;
+  if ((long long)R * gamma > DSPARK_MAX_CANDIDATES) return 0;
+  return dspark::schedule_workspace_bytes(R, gamma);
+}
+
+dspark_status dspark_schedule(const float* surv, const float* sps, int R, int gamma, int B_max,
+                              int32_t* lengths, int32_t* order, dspark_schedule_info* info,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!surv || !sps || !lengths) return fail(DSPARK_EINVAL, "schedule: NULL required pointer");
+  if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "schedule: sizes must be positive");
+  if ((long long)B_max < (long long)R * (1LL + gamma))
+    return fail(DSPARK_EINVAL, "schedule: B_max %d < R * (1 + gamma)", B_max);
+  if ((long long)R * gamma > DSPARK_MAX_CANDIDATES)
+    return fail(DSPARK_EUNSUPPORTED, "schedule: R * gamma above %d", DSPARK_MAX_CANDIDATES);
+  const size_t need = dspark_schedule_workspace(R, gamma);
+  if (!workspace || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "schedule: workspace needs %zu bytes (got %zu)", need,
+                workspace ? ws_bytes : (size_t)0);
+  return dspark::launch_schedule(surv, sps, R, gamma, lengths, order, info, workspace,
+                                 reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

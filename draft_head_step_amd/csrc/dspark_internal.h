@@ -1,0 +1,51 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dspark.h"
+
+namespace dspark {
+
+// Sets the thread-local error text and returns `st`.
+dspark_status fail(dspark_status st, const char* fmt, ...);
+
+// Maps a HIP error (e.g. from hipGetLastError after a launch) to a status.
+dspark_status check_launch(const char* what);
+
+// ---- Markov-head step (fused gather + MFMA bias GEMM + bias-add + select) ----
+
+struct MarkovPlan {
+  int rk;          // compiled rank bucket (64, 128, 256, 512)
+  int nw;          // waves per workgroup; each wave owns 32 requests
+  int n_rblocks;   // ceil(R / (32 * nw))
+  int n_chunks;    // ceil(V / 32): 32-column chunks of V
+  int n_vgroups;   // groups of consecutive chunks, one per workgroup (per R block)
+  int cpg;         // chunks per group
+  size_t ws_bytes; // partial (max, argmax) pairs: R * n_vgroups * 8 bytes
+};
+
+MarkovPlan plan_markov(int R, int gamma, int V, int r);
+
+dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                  const int32_t* anchors, int R, int gamma, int V, int r,
+                                  int mode, float temperature, const float* uniforms,
+                                  int32_t* tokens, float* bias_out, void* workspace,
+                                  const dspark_step_events* events, hipStream_t stream);
+
+// ---- confidence head + survival ----
+dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
+                                const int32_t* tokens, const float* w_conf, const float* sts_temp,
+                                int R, int gamma, int d, int V, int r, float* conf, float* surv,
+                                hipStream_t stream);
+dspark_status launch_survival(const float* conf, int R, int gamma, float* surv, hipStream_t stream);
+
+// ---- prefix scheduler ----
+size_t schedule_workspace_bytes(int R, int gamma);
+dspark_status launch_schedule(const float* surv, const float* sps, int R, int gamma,
+                              int32_t* lengths, int32_t* order, dspark_schedule_info* info,
+                              void* workspace, hipStream_t stream);
+
+}  // namespace dspark

@@ -4,9 +4,10 @@ This module only draws random numbers and packs them into the layouts the C-ABI
 expects.  It holds none of the method's arithmetic, so both the CPU oracle's
 tests and the GPU path can take their inputs from here.
 
-Every array is drawn from ``numpy.random.Generator(PCG64(seed))`` in a fixed
-order (W1, W2, base, boosts, h, w_conf, anchors, uniforms), so a workload is
-reproducible on any machine.  bf16 tensors are produced from float32 draws by
+Every tensor is drawn from its own ``numpy.random.Generator(PCG64)`` streams:
+element chunks of 2^22 values each take the child seed (seed, tensor tag,
+chunk index), so a workload is reproducible on any machine and independent of
+how many threads fill it.  bf16 tensors are produced from float32 draws by
 round-to-nearest-even and are returned as raw ``uint16`` bit patterns.
 
 Layouts (row-major unless stated):
@@ -31,6 +32,8 @@ Markov rank 512 and block size 5).
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
 import numpy as np
@@ -99,19 +102,69 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return rounded.astype(np.uint16)
 
 
-def _normal_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    x *= np.float32(std)
-    return f32_to_bf16_bits(x)
+CHUNK = 1 << 22
+TAGS = {"W1": 1, "W2": 2, "base": 3, "boost": 4, "h": 5, "w_conf": 6, "anchors": 7,
+        "uniforms": 8, "conf": 9}
 
 
-def open_uniforms(rng: np.random.Generator, shape) -> np.ndarray:
-    """u = (floor(U * 2^23) + 0.5) * 2^-23, exactly representable and inside [2^-24, 1 - 2^-24]."""
-    k = rng.integers(0, 1 << 23, size=shape, dtype=np.int32)
+def _gen(seed: int, tag: str, idx: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, TAGS[tag], idx])))
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _fill(shape, dtype, seed: int, tag: str, draw) -> np.ndarray:
+    """Fill an array chunk by chunk; chunk i comes from draw(generator(seed, tag, i), n)."""
+    out = np.empty(shape, dtype=dtype)
+    flat = out.reshape(-1)
+    n = flat.size
+    nch = (n + CHUNK - 1) // CHUNK
+
+    def work(i):
+        lo = i * CHUNK
+        hi = min(n, lo + CHUNK)
+        flat[lo:hi] = draw(_gen(seed, tag, i), hi - lo)
+
+    if nch <= 1:
+        for i in range(nch):
+            work(i)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nch)))
+    return out
+
+
+def _normal_f32(std: float):
+    def draw(g, n):
+        x = g.standard_normal(size=n, dtype=np.float32)
+        x *= np.float32(std)
+        return x
+    return draw
+
+
+def _normal_bf16(seed, tag, shape, std: float) -> np.ndarray:
+    nf = _normal_f32(std)
+    return _fill(shape, np.uint16, seed, tag, lambda g, n: f32_to_bf16_bits(nf(g, n)))
+
+
+def _open_uniform_draw(g, n):
+    k = g.integers(0, 1 << 23, size=n, dtype=np.int32)
     u = k.astype(np.float32)
     u += np.float32(0.5)
     u *= np.float32(2.0 ** -23)
     return u
+
+
+def open_uniforms(rng: np.random.Generator, shape) -> np.ndarray:
+    """u = (floor(U * 2^23) + 0.5) * 2^-23, exactly representable and inside [2^-24, 1 - 2^-24]."""
+    n = int(np.prod(shape))
+    return _open_uniform_draw(rng, n).reshape(shape)
 
 
 def sps_table(kind: str, b_max: int) -> np.ndarray:
@@ -139,7 +192,6 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, R: Optional[int] =
     seed = cfg.seed if seed is None else seed
     R = cfg.R if R is None else R
     g = cfg.gamma
-    rng = np.random.Generator(np.random.PCG64(seed))
     out = {"cfg": cfg, "R": R, "gamma": g, "seed": seed}
     b_max = cfg.sps_bmax if cfg.sps_bmax else R * (1 + g)
     b_max = max(b_max, R * (1 + g))
@@ -147,7 +199,7 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, R: Optional[int] =
         mu = np.asarray(cfg.beta_means, dtype=np.float64)
         a = cfg.beta_conc * mu
         b = cfg.beta_conc * (1.0 - mu)
-        conf = rng.beta(a[None, :], b[None, :], size=(R, g)).astype(np.float32)
+        conf = _gen(seed, "conf").beta(a[None, :], b[None, :], size=(R, g)).astype(np.float32)
         out["conf"] = conf
         out["sps"] = sps_table(cfg.sps_kind, b_max)
         out["B_max"] = b_max
@@ -155,22 +207,21 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, R: Optional[int] =
     V, r, d = cfg.V, cfg.r, cfg.d
     ws = cfg.w_std if w_std is None else w_std
     out.update(V=V, r=r, d=d, mode=cfg.mode, temperature=cfg.temperature)
-    out["W1"] = _normal_bf16(rng, (V, r), ws)
-    out["W2"] = _normal_bf16(rng, (V, r), ws)
-    base = rng.standard_normal(size=(R, g, V), dtype=np.float32)
-    base *= np.float32(cfg.base_std)
+    out["W1"] = _normal_bf16(seed, "W1", (V, r), ws)
+    out["W2"] = _normal_bf16(seed, "W2", (V, r), ws)
+    base = _fill((R, g, V), np.float32, seed, "base", _normal_f32(cfg.base_std))
     if cfg.boost_count:
+        rng = _gen(seed, "boost")
         for m in range(R):
             for k in range(g):
                 ids = rng.choice(V, size=cfg.boost_count, replace=False)
                 base[m, k, ids] += np.float32(cfg.boost_value)
     out["base"] = base
-    out["h"] = _normal_bf16(rng, (R, g, d), cfg.h_std)
-    w = rng.standard_normal(size=(d + r,), dtype=np.float32)
-    w *= np.float32(cfg.wconf_std)
-    out["w_conf"] = w
-    out["anchors"] = rng.integers(0, V, size=(R,), dtype=np.int32)
-    out["uniforms"] = open_uniforms(rng, (R, g, V)) if cfg.mode == SAMPLE else None
+    out["h"] = _normal_bf16(seed, "h", (R, g, d), cfg.h_std)
+    out["w_conf"] = _normal_f32(cfg.wconf_std)(_gen(seed, "w_conf"), d + r)
+    out["anchors"] = _gen(seed, "anchors").integers(0, V, size=(R,), dtype=np.int32)
+    out["uniforms"] = (_fill((R, g, V), np.float32, seed, "uniforms", _open_uniform_draw)
+                       if cfg.mode == SAMPLE else None)
     out["sts"] = None if cfg.sts is None else np.asarray(cfg.sts, dtype=np.float32)
     out["sps"] = sps_table(cfg.sps_kind, b_max)
     out["B_max"] = b_max

@@ -1,0 +1,194 @@
+/*
+ * dspark.h -- C ABI of the DSpark drafter hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The path: a gamma-step Markov-head refinement of a parallel backbone's base
+ * logits, the confidence head with per-position temperature calibration, the
+ * prefix survival products, and the hardware-aware prefix scheduler that picks
+ * per-request verification lengths maximising tau * SPS(B).
+ *
+ * Sources (the DSpark pages):
+ *   [P1] DSpark explainer (zhichai.net/topic/178208222): section 二 "design 1"
+ *        (Markov-head equation), section 二 "design 2" (confidence head, STS,
+ *        hardware-aware prefix scheduler), section 三 challenges 1-2 (asynchronous
+ *        top-K scheduling, global search without early stop).
+ *   [P3] DSpark news summary (10100.com/article/149061879), part 01 and Figure 1
+ *        (anchor as first predicted position, Markov rank 256, survival products).
+ *   [P4] DeepSeek-V4-Pro DSpark integration note (demingchina.com/news/12928)
+ *        (markov_w1/markov_w2 logits bias, rank 512, block size 5, fp32
+ *        confidences, greedy draft sampling).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers into caller-owned memory on the
+ *     current HIP device, row-major, densely packed.  bf16 tensors are passed
+ *     as raw 16-bit patterns (uint16_t).  The library keeps no pointer after
+ *     the call returns and allocates no device memory: scratch comes from a
+ *     caller-provided workspace whose size the *_workspace() queries return.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without synchronising the host, so calls can be
+ *     captured in HIP graphs.  Calls on different streams with distinct
+ *     outputs and workspaces may run concurrently.
+ *   - Host-visible argument checks run before anything is enqueued; a failing
+ *     check returns a status other than DSPARK_OK and enqueues nothing.  Token
+ *     ids inside device buffers (anchors, tokens) must lie in [0, V): that is a
+ *     precondition the host cannot check.
+ *   - dspark_last_error() returns a thread-local description of the last
+ *     failure on the calling thread.
+ *
+ * Notation: R requests, gamma draft positions per request, V vocabulary size,
+ * r Markov rank, d backbone hidden size.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = 1,       /* NULL required pointer, non-positive size, bad mode or temperature */
+  DSPARK_EWORKSPACE = 2,   /* workspace NULL or smaller than the query says */
+  DSPARK_EUNSUPPORTED = 3, /* valid but outside what the kernels are built for (see each call) */
+  DSPARK_EDEVICE = 4       /* a HIP launch or runtime call failed; see dspark_last_error() */
+} dspark_status;
+
+typedef enum {
+  DSPARK_GREEDY = 0, /* x_k = argmax_v z_v */
+  DSPARK_SAMPLE = 1  /* x_k = argmax_v (z_v / T - ln(-ln u_v))  (Gumbel-max) */
+} dspark_mode;
+
+/* Limits of this build. */
+#define DSPARK_MAX_RANK 512          /* r <= 512 and r % 16 == 0 */
+#define DSPARK_MAX_CANDIDATES (1 << 23) /* R * gamma, keeps the fixed-point tau sum exact */
+
+/* Optional per-step timing hooks for dspark_markov_draft.  When non-NULL, the
+ * library records begin[k] on `stream` immediately before the fused step
+ * kernel of position k+1 and end[k] immediately after it (k = 0..gamma-1).
+ * Each entry is a hipEvent_t created by the caller; count must be >= gamma. */
+typedef struct {
+  void* const* begin;
+  void* const* end;
+  int count;
+} dspark_step_events;
+
+/* Result summary of dspark_schedule, written to DEVICE memory (32 bytes). */
+typedef struct {
+  int32_t B_star;   /* chosen verification budget B* = R + m* */
+  int32_t m_star;   /* number of draft tokens admitted, summed over requests */
+  uint64_t tau_fx;  /* tau* in fixed point, units of 2^-40 */
+  double tau;       /* tau* = tau_fx * 2^-40 (double rounding of tau_fx, then exact scale) */
+  double theta;     /* Theta* = tau * SPS(B*) */
+} dspark_schedule_info;
+
+/* Bytes of workspace dspark_markov_draft needs for these sizes (0 if invalid). */
+size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
+
+/*
+ * Markov-head draft: the gamma sequential refinement steps of [P1] section 二
+ * design 1 (Markov-head equation B(x_{k-1}, .) = W1[x_{k-1}] W2), with x_0 the
+ * anchor ([P3] part 01) and the logits bias added to the backbone's base
+ * logits ([P4]).  For k = 1..gamma and every request m:
+ *     e      = W1[x_{k-1}, :]                         (r values)
+ *     z_v    = base[m, k-1, v] + sum_i e_i * W2(i, v)  (fp32, bf16 products, fp32 accumulation)
+ *     x_k    = argmax_v z_v                            (GREEDY)
+ *            = argmax_v z_v / T - ln(-ln u[m,k-1,v])   (SAMPLE)
+ * Equal maxima resolve to the smallest token id.
+ *
+ *   W1        [V, r] bf16   Markov embedding table (row t = W1[t]).
+ *   W2        [V, r] bf16   the r x V projection stored column by column:
+ *                           element (i, v) at W2[v * r + i].
+ *   base      [R, gamma, V] fp32 backbone base logits.
+ *   anchors   [R] int32     anchor token of each request (x_0), in [0, V).
+ *   mode      DSPARK_GREEDY or DSPARK_SAMPLE.
+ *   temperature  > 0 and finite when mode == DSPARK_SAMPLE; ignored for GREEDY.
+ *   uniforms  [R, gamma, V] fp32 in (0, 1), required iff SAMPLE (NULL for GREEDY).
+ *   tokens    [R, gamma] int32 output, tokens[m * gamma + k - 1] = x_k.
+ *   bias_out  optional [R, gamma, V] fp32 output of the Markov bias of every
+ *             step (a debugging aid; pass NULL on the hot path).
+ *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...).
+ *   events    optional timing hooks (NULL on the hot path).
+ * Errors: EINVAL for NULL required pointers, R/gamma/V/r <= 0, V < 2, a bad
+ * mode, a non-positive or non-finite temperature in SAMPLE mode, or uniforms
+ * given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or r % 16 != 0;
+ * EWORKSPACE if the workspace is too small; EDEVICE on a launch failure.
+ */
+dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                  const int32_t* anchors, int R, int gamma, int V, int r,
+                                  int mode, float temperature, const float* uniforms,
+                                  int32_t* tokens, float* bias_out, void* workspace,
+                                  size_t ws_bytes, const dspark_step_events* events,
+                                  void* stream);
+
+/*
+ * Confidence head with STS calibration, [P1] section 二 design 2 (confidence
+ * head equation, sequential temperature scaling) and [P4] (fp32 scores):
+ *     s_{m,k} = sum_{i<d} w[i] h[m,k-1,i] + sum_{i<r} w[d+i] W1[x_{k-1}, i]
+ *     c_{m,k} = 1 / (1 + exp(-s_{m,k} / T_k))
+ * with x_0 = anchors[m] and x_k = tokens[m, k-1].  Optionally also the prefix
+ * survival a_{m,j} = c_{m,1} * ... * c_{m,j}, multiplied left to right in fp32.
+ *
+ *   h         [R, gamma, d] bf16 backbone hidden states.
+ *   W1        [V, r] bf16 (as in dspark_markov_draft).
+ *   anchors   [R] int32; tokens [R, gamma] int32 (the draft).
+ *   w_conf    [d + r] fp32, ordered [w_h; w_e].
+ *   sts_temp  optional [gamma] fp32 positive temperatures T_k (NULL => 1).
+ *   conf      [R, gamma] fp32 output c.
+ *   surv      optional [R, gamma] fp32 output a (NULL to skip).
+ * Errors: EINVAL for NULL required pointers or non-positive sizes; EDEVICE on a
+ * launch failure.  Temperatures are device data: they must be positive.
+ */
+dspark_status dspark_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
+                                const int32_t* tokens, const float* w_conf,
+                                const float* sts_temp, int R, int gamma, int d, int V, int r,
+                                float* conf, float* surv, void* stream);
+
+/*
+ * Prefix survival alone ([P1] section 二 design 2, scheduler definitions):
+ * surv[m, j] = conf[m, 0] * ... * conf[m, j], sequential fp32 products.
+ * conf and surv are [R, gamma] fp32 device arrays (they may not alias).
+ */
+dspark_status dspark_survival(const float* conf, int R, int gamma, float* surv, void* stream);
+
+/* Bytes of workspace dspark_schedule needs (0 if invalid). */
+size_t dspark_schedule_workspace(int R, int gamma);
+
+/*
+ * Hardware-aware prefix scheduler, [P1] section 二 design 2 (objective
+ * Theta = tau * SPS(B), B = sum_r (1 + l_r), tau = sum_r (1 + sum_{j<=l_r} a_{r,j}),
+ * global sort of candidates by survival) and section 三 challenge 2 (no early
+ * stop: every budget is evaluated).  Candidates (r, j) carry id r*gamma + j-1
+ * and key a_{r,j}; they are ordered by key descending, equal keys by id
+ * ascending.  With q = rint(a * 2^40) and S_m the exact integer sum of the
+ * first m ordered q's, Theta_m = double(R*2^40 + S_m) * 2^-40 * double(sps[R+m-1])
+ * for m = 0..R*gamma; m* is the smallest m attaining the maximum, and l_r is
+ * the number of request r's candidates among the first m* ordered ones.
+ *
+ *   surv      [R, gamma] fp32 survival probabilities, each in [0, 1] (device data).
+ *   sps       [B_max] fp32, sps[B-1] = SPS(B) >= 0, the engine's profiled steps/s.
+ *   B_max     >= R * (1 + gamma).
+ *   lengths   [R] int32 output l_r.
+ *   order     optional [R * gamma] int32 output, the sorted candidate ids.
+ *   info      optional dspark_schedule_info output (device memory).
+ *   workspace >= dspark_schedule_workspace(R, gamma) bytes.
+ * Errors: EINVAL for NULL required pointers, non-positive sizes or
+ * B_max < R*(1+gamma); EUNSUPPORTED if R*gamma > DSPARK_MAX_CANDIDATES;
+ * EWORKSPACE; EDEVICE.
+ */
+dspark_status dspark_schedule(const float* surv, const float* sps, int R, int gamma, int B_max,
+                              int32_t* lengths, int32_t* order, dspark_schedule_info* info,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* dspark_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* dspark_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,111 @@
+"""Helpers for the GPU parity tests: move seeded workloads to the device and
+compare the HIP path with the CPU oracle to the stated tolerances.
+
+Tolerances (the oracle computes in fp64 unless the method fixes fp32):
+  * draft tokens: exact wherever the oracle's top-1 / top-2 margin exceeds 1e-2
+    on the forced sequence (the oracle replays each request with the GPU's
+    previous tokens); elsewhere the GPU token must score within 1e-2 of the max;
+  * Markov bias: |b_gpu - b_ref| <= 1e-3 * max(|b_ref|, rms of the b_ref row);
+  * confidences: within 1e-4 absolute (on the forced sequence);
+  * survival, sort order, lengths, B*, tau and Theta: bit-exact given the same
+    confidences / survivals.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import draft_head_step_amd as D
+from oracle import dspark_oracle as O
+
+MARGIN = 1e-2
+BIAS_RTOL = 1e-3
+CONF_ATOL = 1e-4
+
+
+def dev_bf16(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def to_device(wl: dict, device="cuda:0") -> dict:
+    g = {}
+    for k in ("W1", "W2", "h"):
+        if wl.get(k) is not None:
+            g[k] = dev_bf16(wl[k], device)
+    for k in ("base", "uniforms", "w_conf", "sts", "sps", "conf"):
+        if wl.get(k) is not None:
+            g[k] = torch.from_numpy(np.ascontiguousarray(wl[k])).to(device)
+    if wl.get("anchors") is not None:
+        g["anchors"] = torch.from_numpy(wl["anchors"]).to(device)
+    return g
+
+
+def run_draft(wl, g, bias=False):
+    R, gm, V = wl["base"].shape
+    bias_out = torch.empty((R, gm, V), dtype=torch.float32, device=g["base"].device) if bias else None
+    tok = D.dspark_markov_draft(g["W1"], g["W2"], g["base"], g["anchors"], wl["mode"],
+                                wl["temperature"], g.get("uniforms"), bias_out=bias_out)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), (bias_out.cpu().numpy() if bias else None)
+
+
+def check_draft(wl, gpu_tokens, rows=None, gpu_bias=None):
+    """Forced-sequence comparison of tokens (and optionally bias) on `rows`."""
+    R, gm, V = wl["base"].shape
+    rows = np.arange(R) if rows is None else np.asarray(rows)
+    n_clear = n_amb = 0
+    for k in range(gm):
+        prev = wl["anchors"][rows] if k == 0 else gpu_tokens[rows, k - 1]
+        u = None if wl["uniforms"] is None else wl["uniforms"][rows, k]
+        x, s, margin = O.step_scores(wl["W1"], wl["W2"], wl["base"][rows, k], prev, wl["mode"],
+                                     wl["temperature"], u)
+        gt = gpu_tokens[rows, k]
+        assert np.all((gt >= 0) & (gt < V)), "token id out of range"
+        clear = margin > MARGIN
+        bad = clear & (gt != x)
+        assert not bad.any(), (f"step {k}: {bad.sum()} tokens differ where the margin exceeds "
+                               f"{MARGIN}; rows {rows[bad][:8]}, gpu {gt[bad][:8]}, oracle {x[bad][:8]}")
+        smax = s.max(axis=1)
+        sg = s[np.arange(len(rows)), gt]
+        assert np.all(smax - sg <= MARGIN), f"step {k}: a GPU token scores more than {MARGIN} below the max"
+        n_clear += int(clear.sum())
+        n_amb += int((~clear).sum())
+        if gpu_bias is not None:
+            ref = O.markov_bias(wl["W1"], wl["W2"], prev)
+            got = gpu_bias[rows, k].astype(np.float64)
+            rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
+            tol = BIAS_RTOL * np.maximum(np.abs(ref), rms)
+            err = np.abs(got - ref)
+            assert np.all(err <= tol), f"step {k}: bias error {float((err / tol).max()):.3g} x tolerance"
+    return n_clear, n_amb
+
+
+def run_confidence(wl, g, gpu_tokens_dev):
+    conf, surv = D.dspark_confidence(g["h"], g["W1"], g["anchors"], gpu_tokens_dev, g["w_conf"],
+                                     g.get("sts"))
+    torch.cuda.synchronize()
+    return conf.cpu().numpy(), surv.cpu().numpy()
+
+
+def check_confidence(wl, gpu_tokens, conf, surv):
+    ref = O.confidence(wl["h"], wl["W1"], wl["anchors"], gpu_tokens, wl["w_conf"], wl["sts"])
+    err = np.abs(conf.astype(np.float64) - ref)
+    assert err.max() <= CONF_ATOL, f"confidence error {err.max():.3g}"
+    # survival is bit-exact given the GPU's confidences
+    assert np.array_equal(surv, O.survival(conf)), "survival differs from the fp32 running product"
+
+
+def run_schedule(g_surv, g_sps):
+    lengths, order, info = D.dspark_schedule(g_surv, g_sps, want_order=True, want_info=True)
+    torch.cuda.synchronize()
+    return lengths.cpu().numpy(), order.cpu().numpy(), D.schedule_info(info)
+
+
+def check_schedule(surv_np, sps_np, lengths, order, info):
+    ref = O.schedule(surv_np, sps_np)
+    assert np.array_equal(order, ref["order"]), "sort order differs"
+    assert np.array_equal(lengths, ref["lengths"]), "lengths differ"
+    assert info.m_star == ref["m_star"] and info.B_star == ref["B_star"]
+    assert info.tau_fx == ref["tau_fx"]
+    assert info.tau == ref["tau"] and info.theta == ref["theta"]
+    return ref

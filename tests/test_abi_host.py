@@ -1,0 +1,141 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, sizes its workspaces, and rejects invalid arguments on the host
+before anything is enqueued.
+
+The argument-check cases pass placeholder (never dereferenced) pointers; they
+only run where no GPU is visible, so a check that wrongly passed could not
+reach a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_head_step_amd as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+no_gpu = pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                            reason="placeholder-pointer checks run only where no GPU is visible")
+
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED = 0, 1, 2, 3
+P = 0x10000          # 16-byte aligned placeholder address, never dereferenced
+GREEDY, SAMPLE = 0, 1
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = D.lib()
+    names = _header_functions()
+    assert {"dspark_markov_draft", "dspark_confidence", "dspark_survival", "dspark_schedule"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in dspark.h but not exported"
+
+
+def test_status_strings():
+    L = D.lib()
+    assert L.dspark_status_string(0) == b"ok"
+    assert L.dspark_status_string(2) == b"workspace too small"
+    assert L.dspark_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries():
+    assert D.dspark_markov_draft_workspace(0, 5, 100, 64) == 0
+    assert D.dspark_markov_draft_workspace(4, 5, 1, 64) == 0
+    ws = D.dspark_markov_draft_workspace(256, 5, 129280, 512)
+    assert ws >= 256 * 8 and ws % 8 == 0
+    assert D.dspark_schedule_workspace(0, 7) == 0
+    assert D.dspark_schedule_workspace(1 << 20, 16) == 0       # above the candidate limit
+    assert D.dspark_schedule_workspace(256, 5) >= 1
+    big = D.dspark_schedule_workspace(8192, 7)
+    assert big >= 5 * 8192 * 7 * 4
+
+
+def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, mode=GREEDY, T=1.0, u=None,
+           tokens=P, ws=P, ws_bytes=1 << 30, events=None):
+    L = D.lib()
+    return L.dspark_markov_draft(W1, W2, base, anchors, R, g, V, r, mode, T, u, tokens, None, ws,
+                                 ws_bytes, events, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(W1=None), EINVAL), (dict(W2=None), EINVAL), (dict(base=None), EINVAL),
+    (dict(anchors=None), EINVAL), (dict(tokens=None), EINVAL),
+    (dict(R=0), EINVAL), (dict(g=-1), EINVAL), (dict(V=1), EINVAL), (dict(r=0), EINVAL),
+    (dict(mode=2), EINVAL),
+    (dict(mode=SAMPLE, u=None), EINVAL),
+    (dict(mode=SAMPLE, u=P, T=0.0), EINVAL),
+    (dict(mode=SAMPLE, u=P, T=-1.0), EINVAL),
+    (dict(mode=SAMPLE, u=P, T=float("inf")), EINVAL),
+    (dict(mode=SAMPLE, u=P, T=float("nan")), EINVAL),
+    (dict(mode=GREEDY, u=P), EINVAL),
+    (dict(W1=P + 4), EINVAL),
+    (dict(r=40), EUNSUPPORTED), (dict(r=1024), EUNSUPPORTED),
+    (dict(ws=None), EWORKSPACE), (dict(ws_bytes=8), EWORKSPACE),
+])
+def test_markov_draft_rejects(kw, want):
+    assert _draft(**kw) == want
+    assert D.lib().dspark_last_error() != b""
+
+
+@no_gpu
+def test_markov_draft_rejects_short_event_list():
+    ev = D.StepEvents(None, None, 3)
+    assert _draft(events=ctypes.byref(ev)) == EINVAL
+
+
+@no_gpu
+@pytest.mark.parametrize("idx", range(6))
+def test_confidence_rejects_null(idx):
+    # h, W1, anchors, tokens, w_conf and conf are required (sts_temp and surv are optional)
+    args = [P] * 6
+    args[idx] = None
+    h, W1, anchors, tokens, w_conf, conf = args
+    L = D.lib()
+    assert L.dspark_confidence(h, W1, anchors, tokens, w_conf, None, 4, 5, 256, 4096, 64, conf,
+                               None, None) == EINVAL
+
+
+@no_gpu
+def test_confidence_rejects_sizes():
+    L = D.lib()
+    assert L.dspark_confidence(P, P, P, P, P, None, 4, 5, 0, 4096, 64, P, None, None) == EINVAL
+
+
+@no_gpu
+def test_survival_rejects():
+    L = D.lib()
+    assert L.dspark_survival(None, 4, 5, P, None) == EINVAL
+    assert L.dspark_survival(P, 0, 5, P + 64, None) == EINVAL
+    assert L.dspark_survival(P, 4, 5, P, None) == EINVAL       # aliasing
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(surv=None), EINVAL), (dict(sps=None), EINVAL), (dict(lengths=None), EINVAL),
+    (dict(R=0), EINVAL), (dict(B_max=23), EINVAL),
+    (dict(R=1 << 21, g=8, B_max=(1 << 21) * 9), EUNSUPPORTED),
+    (dict(ws=None), EWORKSPACE), (dict(ws_bytes=1), EWORKSPACE),
+])
+def test_schedule_rejects(kw, want):
+    a = dict(surv=P, sps=P, R=4, g=5, B_max=24, lengths=P, ws=P, ws_bytes=1 << 20)
+    a.update(kw)
+    L = D.lib()
+    st = L.dspark_schedule(a["surv"], a["sps"], a["R"], a["g"], a["B_max"], a["lengths"], None,
+                           None, a["ws"], a["ws_bytes"], None)
+    assert st == want
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("DSPARK_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(D, "_LIB", None)
+    with pytest.raises(ImportError):
+        D.lib()

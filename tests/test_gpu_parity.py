@@ -1,0 +1,211 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances are stated in gpu_helpers.  Every workload is seeded; the large ones
+use the full sizes of the benchmarked configurations, with the draft checked on
+sampled requests (the oracle recomputes those requests' steps one by one on
+the GPU's token sequence).
+"""
+import dataclasses
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+sys.path.insert(0, os.path.dirname(__file__))
+import gpu_helpers as H  # noqa: E402
+
+import draft_head_step_amd as D  # noqa: E402
+from draft_head_step_amd.inputs import CONFIGS, GREEDY, SAMPLE, Config, make_workload  # noqa: E402
+from oracle import dspark_oracle as O  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _full_path_check(wl, rows=None, bias_rows=True):
+    g = H.to_device(wl, DEV)
+    toks, bias = H.run_draft(wl, g, bias=bias_rows)
+    n_clear, n_amb = H.check_draft(wl, toks, rows, bias)
+    tok_dev = torch.from_numpy(toks).to(DEV)
+    conf, surv = H.run_confidence(wl, g, tok_dev)
+    H.check_confidence(wl, toks, conf, surv)
+    lengths, order, info = H.run_schedule(torch.from_numpy(surv).to(DEV), g["sps"])
+    H.check_schedule(surv, wl["sps"], lengths, order, info)
+    return toks, n_clear, n_amb
+
+
+# --------------------------------------------------------------------------- tiny
+
+def test_tiny_greedy_end_to_end():
+    _say("case tiny greedy")
+    wl = make_workload(CONFIGS["tiny"])
+    _, n_clear, _ = _full_path_check(wl)
+    assert n_clear > 0
+
+
+def test_tiny_bias_dominant_moves_tokens():
+    _say("case tiny bias-dominant")
+    wl = make_workload(CONFIGS["tiny"], w_std=0.3)
+    toks, _, _ = _full_path_check(wl)
+    assert (toks != np.argmax(wl["base"], axis=2)).any()
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_tiny_sampling(T):
+    _say(f"case tiny sample T={T}")
+    cfg = dataclasses.replace(CONFIGS["tiny"], mode=SAMPLE, temperature=T)
+    wl = make_workload(cfg, w_std=0.2)
+    _full_path_check(wl)
+
+
+def test_deterministic_repeat():
+    _say("case determinism")
+    wl = make_workload(CONFIGS["tiny"], w_std=0.3)
+    g = H.to_device(wl, DEV)
+    a, ba = H.run_draft(wl, g, bias=True)
+    b, bb = H.run_draft(wl, g, bias=True)
+    assert np.array_equal(a, b) and np.array_equal(ba.view(np.uint32), bb.view(np.uint32))
+
+
+# --------------------------------------------------------------------------- edges
+
+EDGE = [
+    # R, gamma, V, r, d, mode
+    (1, 1, 2, 16, 8, GREEDY),
+    (33, 3, 1001, 48, 40, SAMPLE),      # V % 4 != 0 (scalar epilogue), r below its bucket
+    (5, 2, 4099, 128, 24, GREEDY),
+    (70, 4, 3000, 256, 100, SAMPLE),    # partial R blocks, d % 8 != 0
+    (3, 6, 64, 512, 16, GREEDY),        # V smaller than a chunk group, r = 512
+    (300, 2, 777, 64, 64, GREEDY),      # two 256-request blocks, last one partial
+]
+
+
+@pytest.mark.parametrize("R,g,V,r,d,mode", EDGE)
+def test_edge_shapes(R, g, V, r, d, mode):
+    _say(f"case edge R={R} g={g} V={V} r={r} d={d} mode={mode}")
+    cfg = Config("edge", R=R, gamma=g, V=V, r=r, d=d, mode=mode, temperature=0.9, w_std=0.2,
+                 base_std=1.0, wconf_std=0.1, seed=100 + R)
+    wl = make_workload(cfg)
+    _full_path_check(wl)
+
+
+def test_unaligned_base_uses_scalar_path():
+    _say("case unaligned base")
+    cfg = Config("edge", R=6, gamma=3, V=4096, r=64, d=32, w_std=0.2, seed=7)
+    wl = make_workload(cfg)
+    g = H.to_device(wl, DEV)
+    R, gm, V = wl["base"].shape
+    big = torch.empty(R * gm * V + 1, dtype=torch.float32, device=DEV)
+    base = big[1:].view(R, gm, V)
+    base.copy_(g["base"])
+    tok = D.dspark_markov_draft(g["W1"], g["W2"], base, g["anchors"], GREEDY)
+    toks = tok.cpu().numpy()
+    H.check_draft(wl, toks)
+
+
+def test_exact_ties_resolve_to_smallest_id():
+    _say("case ties")
+    R, gm, V, r = 40, 2, 5000, 64
+    rng = np.random.default_rng(3)
+    base = rng.uniform(-1, 1, size=(R, gm, V)).astype(np.float32)
+    for m in range(R):
+        for k in range(gm):
+            ids = np.sort(rng.choice(V, size=4, replace=False))
+            base[m, k, ids] = 7.5
+    wl = {"W1": np.zeros((V, r), np.uint16), "W2": np.zeros((V, r), np.uint16), "base": base,
+          "anchors": rng.integers(0, V, size=R).astype(np.int32), "mode": GREEDY,
+          "temperature": 1.0, "uniforms": None}
+    g = H.to_device(wl, DEV)
+    toks, _ = H.run_draft(wl, g)
+    want = np.argmax(base, axis=2)
+    assert np.array_equal(toks, want)
+
+
+# --------------------------------------------------------------------------- scheduler
+
+def _sched_case(c, sps):
+    gs = torch.from_numpy(c).to(DEV)
+    surv = D.dspark_survival(gs)
+    torch.cuda.synchronize()
+    s = surv.cpu().numpy()
+    assert np.array_equal(s, O.survival(c))
+    lengths, order, info = H.run_schedule(surv, torch.from_numpy(sps).to(DEV))
+    return H.check_schedule(s, sps, lengths, order, info)
+
+
+@pytest.mark.parametrize("R,g", [(1, 1), (4, 5), (1000, 2), (4096, 4), (3277, 5), (5000, 7)])
+def test_schedule_sizes_and_paths(R, g):
+    # 4096 x 4 = 16384 is the largest single-tile (LDS) case; 3277 x 5 = 16385 the
+    # smallest tiled (workspace) case.
+    _say(f"case schedule R={R} g={g}")
+    rng = np.random.default_rng(R * 31 + g)
+    c = rng.beta(6, 1.5, size=(R, g)).astype(np.float32)
+    from draft_head_step_amd.inputs import sps_table
+    _sched_case(c, sps_table("staircase", R * (1 + g)))
+
+
+def test_schedule_ties_and_saturation():
+    _say("case schedule ties")
+    rng = np.random.default_rng(9)
+    R, g = 2000, 6
+    c = rng.choice(np.array([1.0, 0.5, 0.0, 0.75], np.float32), size=(R, g))
+    B = np.arange(1, R * (1 + g) + 1)
+    _sched_case(c, (0.999 ** (B / 64.0)).astype(np.float32))
+
+
+@pytest.mark.parametrize("K", [1, 100, 777])
+def test_schedule_capacity_step_is_top_k(K):
+    _say(f"case schedule top-K K={K}")
+    rng = np.random.default_rng(K)
+    R, g = 300, 5
+    c = rng.uniform(0.05, 1, size=(R, g)).astype(np.float32)
+    K = max(K, R)
+    sps = (np.arange(1, R * (1 + g) + 1) <= K).astype(np.float32)
+    ref = _sched_case(c, sps)
+    assert ref["B_star"] == K
+
+
+def test_sched_stress_workload():
+    _say("case sched_stress")
+    wl = make_workload(CONFIGS["sched_stress"])
+    _sched_case(wl["conf"], wl["sps"])
+
+
+# --------------------------------------------------------------------------- full sizes
+
+def _sample_rows(R, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, R - 1], rng.choice(R, size=min(n, R), replace=False)]))
+
+
+def test_qwen3_8b_full():
+    _say("case qwen3_8b (R=64, V=151936, r=256)")
+    wl = make_workload(CONFIGS["qwen3_8b"])
+    _full_path_check(wl)
+
+
+def test_dsv4_full():
+    _say("case dsv4 (R=256, V=129280, r=512, sampling)")
+    wl = make_workload(CONFIGS["dsv4"])
+    _full_path_check(wl, rows=_sample_rows(256, 24, 1))
+
+
+def test_long_block_full():
+    _say("case long_block (R=1024, gamma=16, V=129280, r=256)")
+    wl = make_workload(CONFIGS["long_block"])
+    g = H.to_device(wl, DEV)
+    toks, _ = H.run_draft(wl, g, bias=False)
+    H.check_draft(wl, toks, _sample_rows(1024, 8, 2))
+    del g["base"]
+    tok_dev = torch.from_numpy(toks).to(DEV)
+    conf, surv = H.run_confidence(wl, g, tok_dev)
+    H.check_confidence(wl, toks, conf, surv)
+    lengths, order, info = H.run_schedule(torch.from_numpy(surv).to(DEV), g["sps"])
+    H.check_schedule(surv, wl["sps"], lengths, order, info)
