@@ -1,0 +1,203 @@
+"""Benchmark: draft tokens/s of the DSpark drafter hot path on one MI355X.
+
+One step = one call of each entry point over one batch that is already
+resident in HBM: dspark_markov_draft (gamma fused refinement steps), then
+dspark_confidence (confidence head, STS, survival), then dspark_schedule
+(global sort + tau * SPS(B) search).  The default workload is the
+DeepSeek-V4-shaped drafter: R = 256 requests, gamma = 5, V = 129280,
+Markov rank r = 512, hidden d = 7168, Gumbel-max sampling at T = 1.
+
+Prints one JSON line with the throughput, the roofline position of the
+dominant kernel (the fused Markov step, timed live with HIP events on the
+stream it runs on), and the CPU oracle's throughput on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+METRIC = "draft tokens/s (Markov refine+confidence+schedule) at R=256,V=129280; % roofline"
+COUNTERS = os.path.join(ROOT, "profiles", "markov_step_dsv4_counters.txt")
+STEP_SRC = os.path.join(ROOT, "draft_head_step_amd", "csrc", "markov_step.hip")
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def step_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one fused Markov step (one launch, all R requests):
+    W2 once, the base logits of this position, the uniforms (sampling), the
+    gathered W1 rows and the previous-token ids."""
+    R, g, V = wl["base"].shape
+    r = wl["W1"].shape[1]
+    b = V * r * 2 + R * V * 4 + R * r * 2 + R * 4
+    if wl["uniforms"] is not None:
+        b += R * V * 4
+    return b
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if the counters were taken on a different version of the kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != _sha(STEP_SRC):
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl):
+    """Time the CPU oracle (as it stands) on one whole call of the same workload."""
+    from oracle import dspark_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    R, g, _ = wl["base"].shape
+    t0 = time.perf_counter()
+    O.run_path(wl)
+    dt = time.perf_counter() - t0
+    return {"value": R * g / dt, "unit": "draft tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full call (all {R} requests x {g} positions: draft, confidence, survival, "
+                      f"schedule) in {dt:.1f} s, numpy fp64 oracle, BLAS threads={threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no "
+              "multi-GPU mode (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import draft_head_step_amd as D
+    from draft_head_step_amd.inputs import CONFIGS, make_workload
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # A plain copy of known size: reads and writes exactly 1 GiB per dispatch.
+        n = (1 << 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": n * 4, "dispatches": 3}), flush=True)
+        return
+    cfg = CONFIGS[args.config]
+    wl = make_workload(cfg)
+    R, g, V = wl["base"].shape
+    r = wl["W1"].shape[1]
+    d = wl["h"].shape[2]
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    W1, W2, h = bf16(wl["W1"]), bf16(wl["W2"]), bf16(wl["h"])
+    base = torch.from_numpy(wl["base"]).to(dev)
+    unif = torch.from_numpy(wl["uniforms"]).to(dev) if wl["uniforms"] is not None else None
+    anchors = torch.from_numpy(wl["anchors"]).to(dev)
+    w_conf = torch.from_numpy(wl["w_conf"]).to(dev)
+    sts = torch.from_numpy(wl["sts"]).to(dev) if wl["sts"] is not None else None
+    sps = torch.from_numpy(wl["sps"]).to(dev)
+    tokens = torch.empty((R, g), dtype=torch.int32, device=dev)
+    conf = torch.empty((R, g), dtype=torch.float32, device=dev)
+    surv = torch.empty((R, g), dtype=torch.float32, device=dev)
+    lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+    ws_d = torch.empty(D.dspark_markov_draft_workspace(R, g, V, r), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(D.dspark_schedule_workspace(R, g), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev=None):
+        D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
+                              tokens=tokens, workspace=ws_d, events=ev, stream=stream)
+        D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv, stream=stream)
+        D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # HIP events bracketing every fused Markov step launch inside the timed region.
+    def mk():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)   # materialise the underlying hipEvent_t
+        return e
+    begins = [[mk() for _ in range(g)] for _ in range(args.steps)]
+    ends = [[mk() for _ in range(g)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(([e.cuda_event for e in begins[i]], [e.cuda_event for e in ends[i]]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = R * g / (ms_per_step / 1e3)
+    durs = [begins[i][k].elapsed_time(ends[i][k]) for i in range(args.steps) for k in range(g)]
+    k_ms = float(np.mean(durs))
+    nbytes = step_bytes(wl)
+    achieved = nbytes / (k_ms / 1e3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: R={R}, gamma={g}, V={V}, r={r}, d={d}, "
+                               f"{'Gumbel-max sampling T=%g' % wl['temperature'] if wl['mode'] else 'greedy'}",
+                   "R": R, "gamma": g, "V": V, "r": r, "d": d},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(),
+                     "kernel": "markov_step_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_ms": round(k_ms, 5), "launches_per_step": g},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
