@@ -50,7 +50,7 @@ const char* dspark_last_error(void) { return dspark::g_last_error; }
 
 size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r) {
   if (R <= 0 || gamma <= 0 || V < 2 || r <= 0) return 0;
-  return dspark::plan_markov(R, gamma, V, r).ws_bytes;
+  return dspark::plan_markov(R, gamma, V, r, DSPARK_GREEDY, false).ws_bytes;
 }
 
 dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,

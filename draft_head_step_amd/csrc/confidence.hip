@@ -8,11 +8,10 @@
 //
 // The work is a dot product of length d + r per (request, position), bound by
 // the HBM read of h.  One workgroup handles all gamma positions of one
-// request, so the survival products are a short sequential tail in the same
-// workgroup.  Each thread streams 16-byte pieces of h (8 bf16) with the
-// matching two float4 pieces of w_h; partial sums are reduced across the
-// wavefront with shuffles and across waves through LDS in a fixed order, so
-// the result is deterministic.
+// request (one wavefront per position), so the survival products are a short
+// sequential tail in the same workgroup.  Each lane streams 16-byte pieces of h
+// (8 bf16) with the matching two float4 pieces of w_h, four pieces in flight;
+// the wavefront reduces with a fixed shuffle tree, so results are deterministic.
 #include <math.h>
 
 #include "dspark_internal.h"
@@ -22,7 +21,6 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 constexpr int kMaxGamma = 64;
 
 __device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
@@ -34,67 +32,88 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum of w[i] * x[i] (x bf16) over this thread's strided share of [0, n).
+// Sum of w[i] * x[i] (x bf16) over this lane's share of [0, n): 16-byte pieces
+// strided by the wavefront, four independent partial sums so that several
+// loads are in flight per lane.
 __device__ __forceinline__ float dot_part(const float* __restrict__ w,
-                                          const uint16_t* __restrict__ x, int n, bool vec) {
-  float acc = 0.f;
-  const int tid = threadIdx.x;
+                                          const uint16_t* __restrict__ x, int n, bool vec,
+                                          int lane) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int tail_from = 0;
   if (vec) {
     const int n8 = n >> 3;
-    for (int p = tid; p < n8; p += kThreads) {
+    int p = lane;
+    for (; p + 192 < n8; p += 256) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pp = p + 64 * u;
+        const u32x4 hv = *reinterpret_cast<const u32x4*>(x + 8 * pp);
+        const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * pp);
+        const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * pp + 4);
+        float a = acc[u];
+        a = fmaf(w0.x, bf16_lo(hv.x), a);
+        a = fmaf(w0.y, bf16_hi(hv.x), a);
+        a = fmaf(w0.z, bf16_lo(hv.y), a);
+        a = fmaf(w0.w, bf16_hi(hv.y), a);
+        a = fmaf(w1.x, bf16_lo(hv.z), a);
+        a = fmaf(w1.y, bf16_hi(hv.z), a);
+        a = fmaf(w1.z, bf16_lo(hv.w), a);
+        a = fmaf(w1.w, bf16_hi(hv.w), a);
+        acc[u] = a;
+      }
+    }
+    for (; p < n8; p += 64) {
       const u32x4 hv = *reinterpret_cast<const u32x4*>(x + 8 * p);
       const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * p);
       const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * p + 4);
-      acc = fmaf(w0.x, bf16_lo(hv.x), acc);
-      acc = fmaf(w0.y, bf16_hi(hv.x), acc);
-      acc = fmaf(w0.z, bf16_lo(hv.y), acc);
-      acc = fmaf(w0.w, bf16_hi(hv.y), acc);
-      acc = fmaf(w1.x, bf16_lo(hv.z), acc);
-      acc = fmaf(w1.y, bf16_hi(hv.z), acc);
-      acc = fmaf(w1.z, bf16_lo(hv.w), acc);
-      acc = fmaf(w1.w, bf16_hi(hv.w), acc);
+      float a = acc[0];
+      a = fmaf(w0.x, bf16_lo(hv.x), a);
+      a = fmaf(w0.y, bf16_hi(hv.x), a);
+      a = fmaf(w0.z, bf16_lo(hv.y), a);
+      a = fmaf(w0.w, bf16_hi(hv.y), a);
+      a = fmaf(w1.x, bf16_lo(hv.z), a);
+      a = fmaf(w1.y, bf16_hi(hv.z), a);
+      a = fmaf(w1.z, bf16_lo(hv.w), a);
+      a = fmaf(w1.w, bf16_hi(hv.w), a);
+      acc[0] = a;
     }
-    for (int i = 8 * n8 + tid; i < n; i += kThreads) acc = fmaf(w[i], __uint_as_float((unsigned)x[i] << 16), acc);
-  } else {
-    for (int i = tid; i < n; i += kThreads) acc = fmaf(w[i], __uint_as_float((unsigned)x[i] << 16), acc);
+    tail_from = 8 * n8;
   }
-  return acc;
+  for (int i = tail_from + lane; i < n; i += 64)
+    acc[1] = fmaf(w[i], __uint_as_float((unsigned)x[i] << 16), acc[1]);
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-__global__ __launch_bounds__(kThreads) void confidence_kernel(
+// One workgroup per request, one wavefront per draft position (looping when
+// gamma exceeds the wavefront count).
+__global__ __launch_bounds__(1024) void confidence_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W1,
     const int32_t* __restrict__ anchors, const int32_t* __restrict__ tokens,
     const float* __restrict__ w_conf, const float* __restrict__ sts_temp, int gamma, int d,
     int V, int r, int vec_h, int vec_e, float* __restrict__ conf, float* __restrict__ surv) {
-  __shared__ float red[kThreads / 64][kMaxGamma];
   __shared__ float cval[kMaxGamma];
   const int m = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
   const float* w_h = w_conf;
   const float* w_e = w_conf + d;
   float a = 1.0f;   // running survival product (thread 0)
   for (int k0 = 0; k0 < gamma; k0 += kMaxGamma) {
     const int kn = min(kMaxGamma, gamma - k0);
-    for (int kk = 0; kk < kn; ++kk) {
+    for (int kk = wave; kk < kn; kk += nwaves) {
       const int k = k0 + kk;
       int x = k == 0 ? anchors[m] : tokens[(size_t)m * gamma + k - 1];
       x = min(max(x, 0), V - 1);
-      float part = dot_part(w_h, h + ((size_t)m * gamma + k) * d, d, vec_h);
-      part += dot_part(w_e, W1 + (size_t)x * r, r, vec_e);
-      part = wave_sum(part);
-      if (lane == 0) red[wave][kk] = part;
-    }
-    __syncthreads();
-    if (threadIdx.x < kn) {
-      const int k = k0 + threadIdx.x;
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < kThreads / 64; ++w) s += red[w][threadIdx.x];
-      const float t = sts_temp ? sts_temp[k] : 1.0f;
-      const float c = 1.0f / (1.0f + expf(-(s / t)));
-      conf[(size_t)m * gamma + k] = c;
-      cval[threadIdx.x] = c;
+      float part = dot_part(w_h, h + ((size_t)m * gamma + k) * d, d, vec_h, lane);
+      part += dot_part(w_e, W1 + (size_t)x * r, r, vec_e, lane);
+      const float s = wave_sum(part);
+      if (lane == 0) {
+        const float t = sts_temp ? sts_temp[k] : 1.0f;
+        const float c = 1.0f / (1.0f + expf(-(s / t)));
+        conf[(size_t)m * gamma + k] = c;
+        cval[kk] = c;
+      }
     }
     __syncthreads();
     if (surv && threadIdx.x == 0) {
@@ -129,7 +148,8 @@ dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const int vec_h = (d % 8 == 0) && a16(h) && a16(w_conf);
   const int vec_e = (r % 8 == 0) && (d % 4 == 0) && a16(W1) && a16(w_conf);
-  hipLaunchKernelGGL(confidence_kernel, dim3(R), dim3(kThreads), 0, stream, h, W1, anchors,
+  const int waves = gamma < 16 ? gamma : 16;
+  hipLaunchKernelGGL(confidence_kernel, dim3(R), dim3(64 * waves), 0, stream, h, W1, anchors,
                      tokens, w_conf, sts_temp, gamma, d, V, r, vec_h, vec_e, conf, surv);
   return check_launch("confidence_kernel");
 }

@@ -27,7 +27,8 @@ struct MarkovPlan {
   size_t ws_bytes; // partial (max, argmax) pairs: R * n_vgroups * 8 bytes
 };
 
-MarkovPlan plan_markov(int R, int gamma, int V, int r);
+// for_launch = false: only the static parts (buckets, workspace); no device queries.
+MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch);
 
 dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
                                   const int32_t* anchors, int R, int gamma, int V, int r,

@@ -40,6 +40,16 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes the compiler wait for every outstanding global load
+// (vmcnt(0)) at each barrier and would drain the prefetch pipeline; the waves
+// here share nothing through global memory inside a launch.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Running argmax with smallest-index tie-break.
 __device__ __forceinline__ void merge_best(float& bv, int& bi, float ov, int oi) {
   if (ov > bv || (ov == bv && oi < bi)) {
@@ -48,12 +58,17 @@ __device__ __forceinline__ void merge_best(float& bv, int& bi, float ov, int oi)
   }
 }
 
-__device__ __forceinline__ float gumbel_noise(float u) {
-  // -ln(-ln u); logf is accurate to a few ulp relative to its result, so w stays
-  // accurate for u close to 1 where the noise is largest.
-  const float w = -logf(u);
-  return -logf(w);
-}
+// Prefetch depths, in 32-column chunks, of W2 (register staging ring) and of
+// the base / uniform epilogue inputs.  With rank 512 the gathered W1 rows alone
+// take 128 VGPRs per lane; the 4-wave variant runs one wave per SIMD and spends
+// the registers that frees on deeper prefetch instead.
+template <int RK, int NW>
+constexpr bool deep_variant() { return RK == 512 && NW == 4; }
+template <int RK, int NW>
+constexpr int w2_depth() { return deep_variant<RK, NW>() ? 2 : 1; }
+template <int RK, int NW>
+constexpr int epi_depth() { return deep_variant<RK, NW>() ? 3 : 1; }
+constexpr int lcm_small(int a, int b) { return (a % b == 0) ? a : (b % a == 0) ? b : a * b; }
 
 template <int RK, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
@@ -65,7 +80,15 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int KS = RK / 16;                          // MFMA K steps at the compiled bucket
   constexpr int NT = NW * 64;                          // threads per workgroup
-  constexpr int PMAX = (4 * RK + NT - 1) / NT;         // 16-byte W2 pieces per thread per chunk
+  constexpr int PPR = RK / 8;                          // 16-byte pieces per LDS row
+  constexpr int PIECES = kChunk * PPR;                 // pieces per chunk
+  constexpr int PMAX = (PIECES + NT - 1) / NT;         // pieces per thread per chunk
+  constexpr int PITCH = RK + 8;                        // bf16 per LDS row (16-byte pad)
+  constexpr int BUF = kChunk * PITCH;                  // bf16 per LDS buffer
+  constexpr int WD = w2_depth<RK, NW>();                // W2 staging slots (chunks in flight)
+  constexpr int PD = epi_depth<RK, NW>();
+  constexpr int NS = PD + 1;                           // epilogue register slots
+  constexpr int UNR = lcm_small(WD, NS);               // unroll keeping slot indices static
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -83,8 +106,7 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   const int c_end = min(c_begin + cpg, n_chunks);
 
   const int ksteps = r >> 4;
-  const int pitch = r + 8;                              // bf16 per LDS row (16-byte pad)
-  const int buf_elems = kChunk * pitch;
+  const int rpieces = r >> 3;                          // pieces at or beyond are stored as zeros
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
   // ---- gather: this lane's request row of W1 becomes the MFMA B operand ----
@@ -105,37 +127,28 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
     }
   }
 
-  // ---- W2 chunk staging: piece p of a chunk is 8 consecutive bf16 of one row ----
-  const int pieces = 4 * r;                            // 16-byte pieces per chunk (32 rows)
-  const int ppr = r >> 3;                              // pieces per row
-  int loff[PMAX];
-  int prow[PMAX];
-#pragma unroll
-  for (int j = 0; j < PMAX; ++j) {
-    const int p = tid + j * NT;
-    const int row = p / ppr;
-    prow[j] = p < pieces ? row : kChunk;                // kChunk marks "no piece"
-    loff[j] = row * pitch + (p - row * ppr) * 8;
-  }
-  u32x4 stage[PMAX];
-  auto load_chunk = [&](int c) {
+  // ---- W2 chunk staging: piece p = (row, 8-element column block) of a chunk ----
+  u32x4 stage[WD][PMAX];
+  auto load_chunk = [&](int c, u32x4 (&st)[PMAX]) {
     const int v0 = c * kChunk;
-    const uint16_t* src = W2 + (size_t)v0 * r;
 #pragma unroll
     for (int j = 0; j < PMAX; ++j) {
       const int p = tid + j * NT;
-      if (prow[j] < kChunk && v0 + prow[j] < V) {
-        stage[j] = *reinterpret_cast<const u32x4*>(src + (size_t)p * 8);
+      const int row = p / PPR;
+      const int cp = p % PPR;
+      if (p < PIECES && cp < rpieces && v0 + row < V) {
+        st[j] = *reinterpret_cast<const u32x4*>(W2 + (size_t)(v0 + row) * r + cp * 8);
       } else {
-        stage[j] = u32x4{0u, 0u, 0u, 0u};
+        st[j] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto store_chunk = [&](int b) {
-    uint16_t* dst = lds + b * buf_elems;
+  auto store_chunk = [&](int b, const u32x4 (&st)[PMAX]) {
+    uint16_t* dst = lds + b * BUF;
 #pragma unroll
     for (int j = 0; j < PMAX; ++j) {
-      if (prow[j] < kChunk) *reinterpret_cast<u32x4*>(dst + loff[j]) = stage[j];
+      const int p = tid + j * NT;
+      if (p < PIECES) *reinterpret_cast<u32x4*>(dst + (p / PPR) * PITCH + (p % PPR) * 8) = st[j];
     }
   };
 
@@ -144,76 +157,100 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   const float* urow = (MODE == DSPARK_SAMPLE) ? unif + row_off : nullptr;
   float* bout = bias_out ? bias_out + row_off : nullptr;
 
-  float best = -INFINITY;
-  int best_i = 0x7fffffff;
-
-  if (c_begin < c_end) load_chunk(c_begin);
-  for (int c = c_begin; c < c_end; ++c) {
-    const int b = (c - c_begin) & 1;
-    store_chunk(b);
-    __syncthreads();
-    if (c + 1 < c_end) load_chunk(c + 1);
-
-    // Epilogue inputs first, so their HBM latency overlaps the MFMAs.
+  // Epilogue inputs of chunk c in the accumulator layout: element 4*jq + i is
+  // vocabulary entry c*32 + 8*jq + 4*half + i of this lane's request.
+  float eb[NS][16];
+  float eu[NS][16];
+  auto load_epi = [&](int c, float (&bv)[16], float (&uv)[16]) {
+    if (!m_ok) return;
     const int v0 = c * kChunk;
-    float bv[16];
-    float uv[16];
-    if (m_ok) {
+    if (vec4 && v0 + kChunk <= V) {
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         const int v = v0 + 8 * jq + 4 * half;
-        if (vec4 && v + 3 < V) {
-          const float4 t = *reinterpret_cast<const float4*>(brow + v);
-          bv[4 * jq + 0] = t.x; bv[4 * jq + 1] = t.y; bv[4 * jq + 2] = t.z; bv[4 * jq + 3] = t.w;
-          if (MODE == DSPARK_SAMPLE) {
-            const float4 w = *reinterpret_cast<const float4*>(urow + v);
-            uv[4 * jq + 0] = w.x; uv[4 * jq + 1] = w.y; uv[4 * jq + 2] = w.z; uv[4 * jq + 3] = w.w;
-          }
-        } else {
+        const float4 t = *reinterpret_cast<const float4*>(brow + v);
+        bv[4 * jq + 0] = t.x; bv[4 * jq + 1] = t.y; bv[4 * jq + 2] = t.z; bv[4 * jq + 3] = t.w;
+        if (MODE == DSPARK_SAMPLE) {
+          const float4 w = *reinterpret_cast<const float4*>(urow + v);
+          uv[4 * jq + 0] = w.x; uv[4 * jq + 1] = w.y; uv[4 * jq + 2] = w.z; uv[4 * jq + 3] = w.w;
+        }
+      }
+    } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = v + i < V;
-            bv[4 * jq + i] = ok ? brow[v + i] : 0.f;
-            if (MODE == DSPARK_SAMPLE) uv[4 * jq + i] = ok ? urow[v + i] : 0.5f;
-          }
+      for (int jq = 0; jq < 4; ++jq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = v0 + 8 * jq + 4 * half + i;
+          const bool ok = v < V;
+          bv[4 * jq + i] = ok ? brow[v] : 0.f;
+          if (MODE == DSPARK_SAMPLE) uv[4 * jq + i] = ok ? urow[v] : 0.5f;
         }
       }
     }
+  };
 
-    // Bias tile: 32 vocabulary rows x 32 requests, K = r.
-    const uint16_t* abase = lds + b * buf_elems + col * pitch + half * 8;
+  float best = -INFINITY;
+  int best_i = 0x7fffffff;
+  // Selection score of one element.  Sampling: z/T - ln(-ln u) with the hardware
+  // base-2 logarithm (relative error ~1e-7 over the whole open unit interval).
+  auto score = [&](float b, float a, float u) {
+    const float z = b + a;
+    if (MODE == DSPARK_SAMPLE) {
+      constexpr float kLn2 = 0.693147180559945309f;
+      const float w = -kLn2 * __builtin_amdgcn_logf(u);      // -ln u  (> 0)
+      return fmaf(-kLn2, __builtin_amdgcn_logf(w), z * inv_t);
+    }
+    return z;
+  };
+
+  // One chunk: stage W2 into LDS, prefetch, bias tile on MFMA, fused select.
+  auto body = [&](int c, u32x4 (&st)[PMAX], float (&cb)[16], float (&cu)[16], float (&pb)[16],
+                  float (&pu)[16]) {
+    const int b = (c - c_begin) & 1;
+    store_chunk(b, st);
+    lds_barrier();
+    if (c + WD < c_end) load_chunk(c + WD, st);        // the slot just stored is free again
+    if (c + PD < c_end) load_epi(c + PD, pb, pu);
+
+    // Bias tile: 32 vocabulary rows x 32 requests over the compiled K = RK.  The
+    // steps beyond r multiply zero-filled LDS columns by zero E registers, so the
+    // loop has no branches and the LDS reads pipeline ahead of the MFMAs.
+    const uint16_t* abase = lds + b * BUF + col * PITCH + half * 8;
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s < ksteps) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + s * 16);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, e[s], acc, 0, 0, 0);
-      }
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + s * 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, e[s], acc, 0, 0, 0);
     }
 
     // Fused bias-add + select.  Lane holds rows v0 + 8*jq + 4*half + i of column m.
+    const int v0 = c * kChunk;
     if (m_ok) {
+      const int vl = v0 + 4 * half;
+      if (v0 + kChunk <= V) {
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int v = v0 + 8 * jq + 4 * half;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int vi = v + i;
-          if (vi < V) {
-            const float z = bv[4 * jq + i] + acc[4 * jq + i];
-            float s;
-            if (MODE == DSPARK_SAMPLE) {
-              s = z * inv_t + gumbel_noise(uv[4 * jq + i]);
-            } else {
-              s = z;
-            }
-            if (s > best) {
-              best = s;
-              best_i = vi;
-            }
+        for (int qq = 0; qq < 16; ++qq) {
+          const float sc = score(cb[qq], acc[qq], cu[qq]);
+          if (sc > best) {
+            best = sc;
+            best_i = vl + 8 * (qq >> 2) + (qq & 3);
           }
         }
-        if (bout) {
+      } else {
+#pragma unroll
+        for (int qq = 0; qq < 16; ++qq) {
+          const int vi = vl + 8 * (qq >> 2) + (qq & 3);
+          const float sc = score(cb[qq], acc[qq], cu[qq]);
+          if (vi < V && sc > best) {
+            best = sc;
+            best_i = vi;
+          }
+        }
+      }
+      if (bout) {
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const int v = v0 + 8 * jq + 4 * half;
           if (vec4 && v + 3 < V) {
             *reinterpret_cast<float4*>(bout + v) =
                 make_float4(acc[4 * jq], acc[4 * jq + 1], acc[4 * jq + 2], acc[4 * jq + 3]);
@@ -224,6 +261,21 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
         }
       }
     }
+  };
+
+#pragma unroll
+  for (int t = 0; t < WD; ++t)
+    if (c_begin + t < c_end) load_chunk(c_begin + t, stage[t]);
+#pragma unroll
+  for (int t = 0; t < PD; ++t)
+    if (c_begin + t < c_end) load_epi(c_begin + t, eb[t], eu[t]);
+  // Unrolled so that every register-slot index is static.
+  for (int c0 = c_begin; c0 < c_end; c0 += UNR) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      if (c0 + j < c_end)
+        body(c0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
+    }
   }
 
   // Lanes l and l^32 hold the same request: merge, then one lane writes the partial.
@@ -231,11 +283,12 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
   if (m_ok && half == 0) {
-    partials[(size_t)m * n_vgroups + vg] = make_float2(best, __int_as_float(best_i));
+    partials[(size_t)vg * R + m] = make_float2(best, __int_as_float(best_i));
   }
 }
 
-// One wave per request: reduce the per-group partials to x_k.
+// Reduce the per-group partials [group][request] to x_k: one wave per request,
+// lanes stride over the groups (independent loads), then a fixed shuffle tree.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __restrict__ partials,
                                                             int R, int n_vgroups, int V,
                                                             int gamma, int k,
@@ -245,8 +298,9 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __rest
   if (m >= R) return;
   float best = -INFINITY;
   int best_i = 0x7fffffff;
+#pragma unroll 4
   for (int g = lane; g < n_vgroups; g += 64) {
-    const float2 p = partials[(size_t)m * n_vgroups + g];
+    const float2 p = partials[(size_t)g * R + m];
     merge_best(best, best_i, p.x, __float_as_int(p.y));
   }
 #pragma unroll
@@ -268,7 +322,7 @@ dspark_status launch_step_t(const MarkovPlan& p, dim3 grid, size_t lds, hipStrea
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&markov_step_kernel<RK, NW, MODE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(2 * kChunk * (RK + 8) * 2)) != hipSuccess) {
+                            (int)lds) != hipSuccess) {
       return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the Markov step kernel");
     }
     attr_set = true;
@@ -316,6 +370,52 @@ dspark_status dispatch_nw(int mode, const MarkovPlan& p, dim3 grid, size_t lds,
   }
 }
 
+// Workgroups of the step kernel that fit on one CU (cached per instantiation).
+template <int RK, int NW, int MODE>
+int blocks_per_cu_t() {
+  static int cached = 0;
+  if (!cached) {
+    int nb = 0;
+    const size_t lds = 2 * kChunk * (size_t)(RK + 8) * 2;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&markov_step_kernel<RK, NW, MODE>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(&markov_step_kernel<RK, NW, MODE>), NW * 64,
+            lds) != hipSuccess || nb < 1)
+      nb = 1;
+    cached = nb;
+  }
+  return cached;
+}
+
+template <int RK>
+int blocks_per_cu_nw(int nw, int mode) {
+  const bool s = mode == DSPARK_SAMPLE;
+  switch (nw) {
+    case 1: return s ? blocks_per_cu_t<RK, 1, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 1, DSPARK_GREEDY>();
+    case 2: return s ? blocks_per_cu_t<RK, 2, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 2, DSPARK_GREEDY>();
+    case 4: return s ? blocks_per_cu_t<RK, 4, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 4, DSPARK_GREEDY>();
+    default: return s ? blocks_per_cu_t<RK, 8, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 8, DSPARK_GREEDY>();
+  }
+}
+
+int blocks_per_cu(int rk, int nw, int mode) {
+  switch (rk) {
+    case 64: return blocks_per_cu_nw<64>(nw, mode);
+    case 128: return blocks_per_cu_nw<128>(nw, mode);
+    case 256: return blocks_per_cu_nw<256>(nw, mode);
+    default: return blocks_per_cu_nw<512>(nw, mode);
+  }
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 int env_int(const char* name, int dflt) {
   const char* s = getenv(name);
   return (s && *s) ? atoi(s) : dflt;
@@ -323,20 +423,27 @@ int env_int(const char* name, int dflt) {
 
 }  // namespace
 
-MarkovPlan plan_markov(int R, int gamma, int V, int r) {
+MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch) {
   (void)gamma;
   MarkovPlan p{};
   p.rk = r <= 64 ? 64 : r <= 128 ? 128 : r <= 256 ? 256 : 512;
   const int waves_needed = (R + 31) / 32;
   int nw = waves_needed >= 8 ? 8 : waves_needed >= 4 ? 4 : waves_needed >= 2 ? 2 : 1;
+  // Rank-512 sampling: the 8-wave kernel would spill; the 4-wave, one-wave-per-SIMD
+  // variant with deeper prefetch is used instead.
+  if (p.rk == 512 && mode == DSPARK_SAMPLE && nw == 8) nw = 4;
   const int nw_env = env_int("DSPARK_MARKOV_NW", 0);
   if (nw_env == 1 || nw_env == 2 || nw_env == 4 || nw_env == 8) nw = nw_env;
   p.nw = nw;
   p.n_rblocks = (R + 32 * nw - 1) / (32 * nw);
   p.n_chunks = (V + kChunk - 1) / kChunk;
   const int max_groups = p.n_chunks < kMaxGroups ? p.n_chunks : kMaxGroups;
-  // Default: about 256 workgroups in flight (one per CU), split between the R blocks.
-  int target = env_int("DSPARK_MARKOV_WG", 256);
+  p.ws_bytes = (size_t)R * (size_t)max_groups * sizeof(float2);
+  if (!for_launch) return p;
+  // One wave of workgroups: as many as fit on the device at once, split between
+  // the R blocks (each V group is walked by n_rblocks workgroups).
+  int target = env_int("DSPARK_MARKOV_WG", 0);
+  if (target <= 0) target = device_cus() * blocks_per_cu(p.rk, nw, mode);
   if (target < 8) target = 8;
   int groups = (target + p.n_rblocks - 1) / p.n_rblocks;
   groups = (groups + 7) / 8 * 8;
@@ -344,7 +451,6 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r) {
   if (groups < 1) groups = 1;
   p.cpg = (p.n_chunks + groups - 1) / groups;
   p.n_vgroups = (p.n_chunks + p.cpg - 1) / p.cpg;
-  p.ws_bytes = (size_t)R * (size_t)max_groups * sizeof(float2);
   return p;
 }
 
@@ -353,11 +459,11 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
                                   int mode, float temperature, const float* uniforms,
                                   int32_t* tokens, float* bias_out, void* workspace,
                                   const dspark_step_events* events, hipStream_t stream) {
-  const MarkovPlan p = plan_markov(R, gamma, V, r);
+  const MarkovPlan p = plan_markov(R, gamma, V, r, mode, true);
   float2* partials = reinterpret_cast<float2*>(workspace);
   const int padded_groups = (p.n_vgroups + 7) / 8 * 8;
   const dim3 grid(padded_groups * p.n_rblocks);
-  const size_t lds = 2 * kChunk * (size_t)(r + 8) * 2;
+  const size_t lds = 2 * kChunk * (size_t)(p.rk + 8) * 2;   // two W2 chunk buffers
   const float inv_t = mode == DSPARK_SAMPLE ? 1.0f / temperature : 1.0f;
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const int vec4 = (V % 4 == 0) && a16(base) && (!uniforms || a16(uniforms)) &&
