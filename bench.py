@@ -7,6 +7,11 @@ dspark_confidence (confidence head, STS, survival), then dspark_schedule
 DeepSeek-V4-shaped drafter: R = 256 requests, gamma = 5, V = 129280,
 Markov rank r = 512, hidden d = 7168, Gumbel-max sampling at T = 1.
 
+The base logits and uniforms are handed over in the chunk-tiled layout
+([gamma][ceil(V/32)][R][32], what a producer that writes them tile by tile
+emits) by default; the row-major [R][gamma][V] layout is timed in the same run
+and reported beside it (``row_major``).
+
 Prints one JSON line with the throughput, the roofline position of the
 dominant kernel (the fused Markov step, timed live with HIP events on the
 stream it runs on), and the CPU oracle's throughput on the same workload.
@@ -27,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 METRIC = "draft tokens/s (Markov refine+confidence+schedule) at R=256,V=129280; % roofline"
-COUNTERS = os.path.join(ROOT, "profiles", "markov_step_dsv4_counters.txt")
+COUNTERS_FMT = os.path.join(ROOT, "profiles", "markov_step_{cfg}_{layout}_counters.txt")
 STEP_SRC = os.path.join(ROOT, "draft_head_step_amd", "csrc", "markov_step.hip")
 
 
@@ -48,13 +53,14 @@ def step_bytes(wl) -> int:
     return b
 
 
-def read_traffic():
+def read_traffic(cfg, layout):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     if the counters were taken on a different version of the kernel source."""
-    if not os.path.exists(COUNTERS):
+    path = COUNTERS_FMT.format(cfg=cfg, layout=layout)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(COUNTERS):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -89,6 +95,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="dsv4")
+    ap.add_argument("--layout", choices=["tiled", "rgv"], default="tiled",
+                    help="storage order of base / uniforms handed to the draft")
+    ap.add_argument("--no-row-major", action="store_true",
+                    help="skip the secondary timing in the row-major layout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
@@ -100,7 +110,7 @@ def main():
 
     import torch
     import draft_head_step_amd as D
-    from draft_head_step_amd.inputs import CONFIGS, make_workload
+    from draft_head_step_amd.inputs import CONFIGS, make_workload, to_tiled
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -124,8 +134,13 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     W1, W2, h = bf16(wl["W1"]), bf16(wl["W2"]), bf16(wl["h"])
-    base = torch.from_numpy(wl["base"]).to(dev)
-    unif = torch.from_numpy(wl["uniforms"]).to(dev) if wl["uniforms"] is not None else None
+    layouts = {"tiled": D.LAYOUT_TILED, "rgv": D.LAYOUT_RGV}
+
+    def inputs(layout):
+        conv = to_tiled if layout == "tiled" else (lambda a: a)
+        b = torch.from_numpy(conv(wl["base"])).to(dev)
+        u = torch.from_numpy(conv(wl["uniforms"])).to(dev) if wl["uniforms"] is not None else None
+        return b, u
     anchors = torch.from_numpy(wl["anchors"]).to(dev)
     w_conf = torch.from_numpy(wl["w_conf"]).to(dev)
     sts = torch.from_numpy(wl["sts"]).to(dev) if wl["sts"] is not None else None
@@ -138,38 +153,48 @@ def main():
     ws_s = torch.empty(D.dspark_schedule_workspace(R, g), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def one_step(ev=None):
-        D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
-                              tokens=tokens, workspace=ws_d, events=ev, stream=stream)
-        D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv, stream=stream)
-        D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
+    def run(layout, steps, warmup):
+        """Time `steps` whole steps; return (ms per step, mean fused-step launch ms)."""
+        base, unif = inputs(layout)
+        lay = layouts[layout]
 
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
+        def one_step(ev=None):
+            D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
+                                  tokens=tokens, workspace=ws_d, events=ev, stream=stream,
+                                  layout=lay)
+            D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv,
+                                stream=stream)
+            D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
 
-    # HIP events bracketing every fused Markov step launch inside the timed region.
-    def mk():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)   # materialise the underlying hipEvent_t
-        return e
-    begins = [[mk() for _ in range(g)] for _ in range(args.steps)]
-    ends = [[mk() for _ in range(g)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+        for _ in range(warmup):
+            one_step()
+        torch.cuda.synchronize()
 
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(([e.cuda_event for e in begins[i]], [e.cuda_event for e in ends[i]]))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+        # HIP events bracketing every fused Markov step launch inside the timed region.
+        def mk():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)   # materialise the underlying hipEvent_t
+            return e
+        begins = [[mk() for _ in range(g)] for _ in range(steps)]
+        ends = [[mk() for _ in range(g)] for _ in range(steps)]
+        torch.cuda.synchronize()
 
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one_step(([e.cuda_event for e in begins[i]], [e.cuda_event for e in ends[i]]))
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        durs = [begins[i][k].elapsed_time(ends[i][k]) for i in range(steps) for k in range(g)]
+        del base, unif
+        return (t1 - t0) * 1e3 / steps, float(np.mean(durs))
+
+    ms_per_step, k_ms = run(args.layout, args.steps, args.warmup)
     value = R * g / (ms_per_step / 1e3)
-    durs = [begins[i][k].elapsed_time(ends[i][k]) for i in range(args.steps) for k in range(g)]
-    k_ms = float(np.mean(durs))
     nbytes = step_bytes(wl)
     achieved = nbytes / (k_ms / 1e3) / 1e9
+    # The library runs rank-512 sampling on the K-split kernel, everything else
+    # on the plain one.
+    kernel = "markov_step_ksplit_kernel" if (r > 256 and wl["mode"]) else "markov_step_kernel"
 
     out = {
         "metric": METRIC,
@@ -186,14 +211,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: R={R}, gamma={g}, V={V}, r={r}, d={d}, "
                                f"{'Gumbel-max sampling T=%g' % wl['temperature'] if wl['mode'] else 'greedy'}",
-                   "R": R, "gamma": g, "V": V, "r": r, "d": d},
+                   "R": R, "gamma": g, "V": V, "r": r, "d": d, "layout": args.layout},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": read_traffic(),
-                     "kernel": "markov_step_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "traffic": read_traffic(cfg.name, args.layout),
+                     "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_ms": round(k_ms, 5), "launches_per_step": g},
         "cpu_baseline": None,
     }
+    if not args.no_row_major and args.layout != "rgv":
+        ms2, k2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1))
+        out["row_major"] = {"layout": "rgv", "ms_per_step": round(ms2, 4),
+                            "value": round(R * g / (ms2 / 1e3), 1),
+                            "avg_launch_ms": round(k2, 5),
+                            "frac": round(nbytes / (k2 / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

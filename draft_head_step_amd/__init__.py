@@ -18,13 +18,15 @@ import os
 from typing import Optional
 
 __all__ = [
-    "DsparkError", "GREEDY", "SAMPLE", "lib", "lib_path",
+    "DsparkError", "GREEDY", "SAMPLE", "LAYOUT_RGV", "LAYOUT_TILED", "lib", "lib_path",
     "dspark_markov_draft", "dspark_confidence", "dspark_survival", "dspark_schedule",
     "dspark_markov_draft_workspace", "dspark_schedule_workspace", "ScheduleInfo",
 ]
 
 GREEDY = 0
 SAMPLE = 1
+LAYOUT_RGV = 0     # base / uniforms / bias_out as [R, gamma, V]
+LAYOUT_TILED = 1   # [gamma, ceil(V/32), R, 32]
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -75,8 +77,8 @@ def lib() -> ctypes.CDLL:
     L.dspark_last_error.restype = ctypes.c_char_p
     L.dspark_markov_draft_workspace.argtypes = [i32, i32, i32, i32]
     L.dspark_markov_draft_workspace.restype = sz
-    L.dspark_markov_draft.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp,
-                                      vp, sz, ctypes.POINTER(StepEvents), vp]
+    L.dspark_markov_draft.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                      vp, vp, sz, ctypes.POINTER(StepEvents), vp]
     L.dspark_markov_draft.restype = i32
     L.dspark_confidence.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.dspark_confidence.restype = i32
@@ -136,28 +138,35 @@ def dspark_schedule_workspace(R: int, gamma: int) -> int:
 
 def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: float = 1.0,
                         uniforms=None, tokens=None, bias_out=None, workspace=None,
-                        events=None, stream=None):
-    """gamma-step Markov-head draft.  Shapes: W1, W2 [V, r] bf16; base [R, gamma, V] fp32;
-    anchors [R] int32; uniforms [R, gamma, V] fp32 (SAMPLE only).  Returns tokens [R, gamma] int32.
+                        events=None, stream=None, layout: int = LAYOUT_RGV):
+    """gamma-step Markov-head draft.  W1, W2 [V, r] bf16; anchors [R] int32; base (and
+    uniforms, SAMPLE only; bias_out, optional) fp32 as [R, gamma, V] (LAYOUT_RGV) or
+    [gamma, ceil(V/32), R, 32] (LAYOUT_TILED).  Returns tokens [R, gamma] int32.
 
     ``events`` is an optional pair (begin, end) of sequences of hipEvent_t handles (ints),
     recorded around each step's fused kernel."""
     torch = _torch()
     L = lib()
-    R, gamma, V = base.shape
-    r = W1.shape[1]
+    V, r = W1.shape
+    R = anchors.shape[0]
     dev = base.device
+    if layout == LAYOUT_TILED:
+        gamma = base.shape[0]
+        shape = (gamma, (V + 31) // 32, R, 32)
+    else:
+        gamma = base.shape[1]
+        shape = (R, gamma, V)
     _need(W1, "W1", _bf16_types(), (V, r), dev)
     _need(W2, "W2", _bf16_types(), (V, r), dev)
-    _need(base, "base", (torch.float32,), (R, gamma, V), dev)
+    _need(base, "base", (torch.float32,), shape, dev)
     _need(anchors, "anchors", (torch.int32,), (R,), dev)
     if uniforms is not None:
-        _need(uniforms, "uniforms", (torch.float32,), (R, gamma, V), dev)
+        _need(uniforms, "uniforms", (torch.float32,), shape, dev)
     if tokens is None:
         tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
     _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
     if bias_out is not None:
-        _need(bias_out, "bias_out", (torch.float32,), (R, gamma, V), dev)
+        _need(bias_out, "bias_out", (torch.float32,), shape, dev)
     need = int(L.dspark_markov_draft_workspace(R, gamma, V, r))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -167,8 +176,8 @@ def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: 
         ev = StepEvents((ctypes.c_void_p * len(b))(*b), (ctypes.c_void_p * len(e))(*e),
                         min(len(b), len(e)))
     st = L.dspark_markov_draft(_ptr(W1), _ptr(W2), _ptr(base), _ptr(anchors), R, gamma, V, r,
-                               int(mode), float(temperature), _ptr(uniforms), _ptr(tokens),
-                               _ptr(bias_out), _ptr(workspace), workspace.numel(),
+                               int(layout), int(mode), float(temperature), _ptr(uniforms),
+                               _ptr(tokens), _ptr(bias_out), _ptr(workspace), workspace.numel(),
                                ctypes.byref(ev) if ev is not None else None, _stream(stream))
     _check(st, "dspark_markov_draft")
     return tokens

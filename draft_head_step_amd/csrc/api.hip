@@ -55,7 +55,7 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r) {
 
 dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
                                   const int32_t* anchors, int R, int gamma, int V, int r,
-                                  int mode, float temperature, const float* uniforms,
+                                  int layout, int mode, float temperature, const float* uniforms,
                                   int32_t* tokens, float* bias_out, void* workspace,
                                   size_t ws_bytes, const dspark_step_events* events,
                                   void* stream) {
@@ -65,6 +65,8 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   if (R <= 0 || gamma <= 0 || r <= 0 || V < 2)
     return fail(DSPARK_EINVAL, "markov_draft: need R, gamma, r > 0 and V >= 2 (got %d %d %d %d)",
                 R, gamma, r, V);
+  if (layout != DSPARK_LAYOUT_RGV && layout != DSPARK_LAYOUT_TILED)
+    return fail(DSPARK_EINVAL, "markov_draft: unknown layout %d", layout);
   if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLE)
     return fail(DSPARK_EINVAL, "markov_draft: unknown mode %d", mode);
   if (mode == DSPARK_SAMPLE) {
@@ -79,14 +81,25 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   if (r > DSPARK_MAX_RANK || r % 16 != 0)
     return fail(DSPARK_EUNSUPPORTED, "markov_draft: r must be a multiple of 16 and <= %d (got %d)",
                 DSPARK_MAX_RANK, r);
+  {
+    // The kernels address each step's slice of one request block with 32-bit
+    // byte offsets (buffer loads).
+    const uint64_t C = ((uint64_t)V + 31) / 32;
+    if (C * 32 * (uint64_t)r > (1ull << 30))
+      return fail(DSPARK_EUNSUPPORTED, "markov_draft: ceil(V/32)*32*r above 2^30");
+    if (layout == DSPARK_LAYOUT_RGV && (uint64_t)gamma * (uint64_t)V >= (1ull << 22))
+      return fail(DSPARK_EUNSUPPORTED, "markov_draft: gamma*V must be below 2^22 in the RGV layout");
+    if (layout == DSPARK_LAYOUT_TILED && C * (uint64_t)R + 256 > (1ull << 25))
+      return fail(DSPARK_EUNSUPPORTED, "markov_draft: ceil(V/32)*R + 256 above 2^25 in the tiled layout");
+  }
   if (events && (events->count < gamma))
     return fail(DSPARK_EINVAL, "markov_draft: events->count < gamma");
   const size_t need = dspark_markov_draft_workspace(R, gamma, V, r);
   if (!workspace || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "markov_draft: workspace needs %zu bytes (got %zu)", need,
                 workspace ? ws_bytes : (size_t)0);
-  return dspark::launch_markov_draft(W1, W2, base, anchors, R, gamma, V, r, mode, temperature,
-                                     uniforms, tokens, bias_out, workspace, events,
+  return dspark::launch_markov_draft(W1, W2, base, anchors, R, gamma, V, r, layout, mode,
+                                     temperature, uniforms, tokens, bias_out, workspace, events,
                                      reinterpret_cast<hipStream_t>(stream));
 }
 

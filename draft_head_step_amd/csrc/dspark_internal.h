@@ -19,12 +19,13 @@ dspark_status check_launch(const char* what);
 
 struct MarkovPlan {
   int rk;          // compiled rank bucket (64, 128, 256, 512)
-  int nw;          // waves per workgroup; each wave owns 32 requests
+  int nw;          // waves per workgroup (32 requests per wave, or per wave pair if ksplit)
+  bool ksplit;     // rank-512 K-split pairs
   int n_rblocks;   // ceil(R / (32 * nw))
   int n_chunks;    // ceil(V / 32): 32-column chunks of V
   int n_vgroups;   // groups of consecutive chunks, one per workgroup (per R block)
   int cpg;         // chunks per group
-  size_t ws_bytes; // partial (max, argmax) pairs: R * n_vgroups * 8 bytes
+  size_t ws_bytes; // partial (max, argmax) pairs: R * 2 * max groups * 8 bytes
 };
 
 // for_launch = false: only the static parts (buckets, workspace); no device queries.
@@ -32,9 +33,10 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
 
 dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
                                   const int32_t* anchors, int R, int gamma, int V, int r,
-                                  int mode, float temperature, const float* uniforms,
-                                  int32_t* tokens, float* bias_out, void* workspace,
-                                  const dspark_step_events* events, hipStream_t stream);
+                                  int layout, int mode, float temperature,
+                                  const float* uniforms, int32_t* tokens, float* bias_out,
+                                  void* workspace, const dspark_step_events* events,
+                                  hipStream_t stream);
 
 // ---- confidence head + survival ----
 dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,

@@ -12,16 +12,30 @@
 //     and W2, and so that every lane's accumulators cover four consecutive
 //     vocabulary entries of one request: the base / uniform reads of the
 //     epilogue are 16-byte vector loads in exactly the accumulator layout.
-//   * Each wave owns 32 requests and keeps their gathered W1 rows (the MFMA B
-//     operand) in registers for the whole kernel.  A workgroup of NW waves
-//     shares 32-column chunks of W2 staged through LDS (double-buffered, rows
-//     padded by 16 bytes so the MFMA A-operand reads hit distinct banks).
-//   * Each workgroup walks a contiguous group of chunks and keeps a running
-//     (max, argmax) per request; a second tiny kernel reduces the per-group
-//     partials to the token.  No float atomics: the result is deterministic.
+//   * A wave owns 32 requests and keeps their gathered W1 rows (MFMA B operand)
+//     in registers for the whole launch.  The workgroup's waves share 32-column
+//     chunks of W2 staged through LDS (double-buffered, rows padded by 16 bytes
+//     so the A-operand reads hit distinct banks).
+//   * Each workgroup walks a contiguous group of chunks keeping a running
+//     (max, argmax) per request; a tiny second kernel reduces the per-group
+//     partials to the token.  No float atomics: results are deterministic.
 //   * Workgroup ids are decoded so that the R-blocks sharing a V group land on
 //     the same XCD (ids congruent mod 8) and are dispatched together, so the
 //     second and later reads of a W2 chunk hit that XCD's L2.
+//   * Loads run ahead of use through register rings (W2 staging, epilogue
+//     inputs).  The steady-state loop body is branch-free: every load is a raw
+//     buffer load issued unconditionally (the hardware range check turns the
+//     tail, padding and rank-padding reads into zeros) and validity is applied
+//     with selects, because a load on a conditional path makes the compiler's
+//     wait-count analysis assume the worst and drain the whole ring (vmcnt(0))
+//     at the next use.  Groups are padded to the unroll factor, prefetches stay
+//     inside the group, and scheduling barriers keep each chunk's arithmetic
+//     in its own iteration so the waits count the ring from the back.
+//   * Rank 512: the gathered rows take 128 VGPRs per lane.  Either one wave per
+//     SIMD with deeper rings ("plain", 4 waves), or K-split wave pairs (each
+//     wave holds one K half, 64 VGPRs, two waves per SIMD; partial tiles are
+//     exchanged through LDS and the epilogue of chunk c-1 runs beside the MFMAs
+//     of chunk c).
 #include <math.h>
 
 #include "dspark_internal.h"
@@ -41,9 +55,8 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
 }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global
-// memory, which makes the compiler wait for every outstanding global load
-// (vmcnt(0)) at each barrier and would drain the prefetch pipeline; the waves
-// here share nothing through global memory inside a launch.
+// memory, which makes the compiler wait for every outstanding global load at
+// each barrier; the waves here share nothing through global memory in a launch.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -58,37 +71,144 @@ __device__ __forceinline__ void merge_best(float& bv, int& bi, float ov, int oi)
   }
 }
 
-// Prefetch depths, in 32-column chunks, of W2 (register staging ring) and of
-// the base / uniform epilogue inputs.  With rank 512 the gathered W1 rows alone
-// take 128 VGPRs per lane; the 4-wave variant runs one wave per SIMD and spends
-// the registers that frees on deeper prefetch instead.
-template <int RK, int NW>
-constexpr bool deep_variant() { return RK == 512 && NW == 4; }
-template <int RK, int NW>
-constexpr int w2_depth() { return deep_variant<RK, NW>() ? 2 : 1; }
-template <int RK, int NW>
-constexpr int epi_depth() { return deep_variant<RK, NW>() ? 3 : 1; }
+// Selection score.  Sampling: z/T - ln(-ln u) with the hardware base-2
+// logarithm (relative error ~1e-7 over the whole open unit interval).
+template <int MODE>
+__device__ __forceinline__ float select_score(float b, float a, float u, float inv_t) {
+  const float z = b + a;
+  if (MODE == DSPARK_SAMPLE) {
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float w = -kLn2 * __builtin_amdgcn_logf(u);        // -ln u  (> 0)
+    return fmaf(-kLn2, __builtin_amdgcn_logf(w), z * inv_t);
+  }
+  return z;
+}
+
+// ---- raw buffer access ----
+// Buffer loads take one scalar resource (base, size) and a 32-bit per-lane
+// byte offset.  Offsets at or past the size read as zero instead of faulting,
+// which replaces every clamp and select of the tail, padding and rank-padding
+// cases; the per-lane offsets stay fixed over the loop (chunk steps are a
+// uniform add), so the ring needs no 64-bit address registers.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;     // untyped dword access (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Element (m, k, v) of base / uniforms / bias_out is at float offset
+// k_off + m * row_stride + (v / 32) * cstride + v % 32 in either layout; total
+// is the array's length in floats.  Byte offsets inside one R block of one
+// step fit in 32 bits (checked on the host).
+struct Addr {
+  size_t k_off, row_stride, cstride, total;
+};
+
+// Buffer resource over the rows of R block `rb` (first row rb * rows) at step k.
+__device__ __forceinline__ Rsrc block_rsrc(const float* arr, const Addr& ad, int rb, int rows) {
+  const size_t off = ad.k_off + (size_t)rb * rows * ad.row_stride;
+  const size_t rem = ad.total > off ? (ad.total - off) * 4 : 0;
+  return make_rsrc(arr + off, rem > 0xfffffff0u ? 0xfffffff0u : (uint32_t)rem);
+}
+
+// W2 chunk staging.  Piece p = tid + j * NT of the 32 x RK chunk is row p / PPR,
+// 8-element block p % PPR; since NT is a multiple of PPR the block is the same
+// for all j and the row advances by NT / PPR.  Blocks past r carry an offset
+// past the buffer, rows past V land past it, so both read as zeros.
+template <int RK, int NT>
+__device__ __forceinline__ uint32_t w2_lane_offset(int tid, int r) {
+  constexpr int PPR = RK / 8;
+  const int cp = tid % PPR;
+  return cp < (r >> 3) ? (uint32_t)((tid / PPR) * r + cp * 8) * 2u : kOutOfRange;
+}
+
+template <int RK, int NT, int PMAX>
+__device__ __forceinline__ void w2_load(u32x4 (&st)[PMAX], Rsrc rw2, uint32_t lane_off, int cc,
+                                        int r) {
+  constexpr int PPR = RK / 8;
+  const uint32_t off = lane_off + (uint32_t)cc * (uint32_t)(kChunk * r * 2);
+#pragma unroll
+  for (int j = 0; j < PMAX; ++j) st[j] = buf_load16(rw2, off + (uint32_t)(j * (NT / PPR) * r * 2));
+}
+
+template <int RK, int NT, int PMAX>
+__device__ __forceinline__ void w2_store(uint16_t* dst, const u32x4 (&st)[PMAX], int tid) {
+  constexpr int PPR = RK / 8;
+  constexpr int PIECES = kChunk * PPR;
+  constexpr int PITCH = RK + 8;
+#pragma unroll
+  for (int j = 0; j < PMAX; ++j) {
+    const int p = tid + j * NT;
+    if (PIECES % NT == 0 || p < PIECES)
+      *reinterpret_cast<u32x4*>(dst + (p / PPR) * PITCH + (p % PPR) * 8) = st[j];
+  }
+}
+
+// Epilogue inputs of NJ accumulator groups (jq = j0 .. j0+NJ-1) of one chunk for
+// one lane: element 4*j + i is vocabulary entry v0 + 8*(j0+j) + 4*half + i; `off`
+// is the lane's byte offset of entry v0 + 8*j0 + 4*half.
+template <int MODE, bool VEC4, int NJ>
+__device__ __forceinline__ void epi_load(float (&bv)[4 * NJ], float (&uv)[4 * NJ], Rsrc rbase,
+                                         Rsrc runif, uint32_t off) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (VEC4) {
+      const float4 t = __builtin_bit_cast(float4, buf_load16(rbase, off + 32u * j));
+      bv[4 * j + 0] = t.x; bv[4 * j + 1] = t.y; bv[4 * j + 2] = t.z; bv[4 * j + 3] = t.w;
+      if (MODE == DSPARK_SAMPLE) {
+        const float4 w = __builtin_bit_cast(float4, buf_load16(runif, off + 32u * j));
+        uv[4 * j + 0] = w.x; uv[4 * j + 1] = w.y; uv[4 * j + 2] = w.z; uv[4 * j + 3] = w.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bv[4 * j + i] = buf_load4(rbase, off + 32u * j + 4u * i);
+        if (MODE == DSPARK_SAMPLE) uv[4 * j + i] = buf_load4(runif, off + 32u * j + 4u * i);
+      }
+    }
+  }
+}
+
 constexpr int lcm_small(int a, int b) { return (a % b == 0) ? a : (b % a == 0) ? b : a * b; }
 
-template <int RK, int NW, int MODE>
+// ---------------------------------------------------------------------------
+// Plain kernel: a wave owns 32 requests over the full K.
+// ---------------------------------------------------------------------------
+template <int RK, int NW>
+constexpr bool plain_deep() { return RK == 512 && NW == 4; }
+template <int RK, int NW>
+constexpr int plain_wd() { return plain_deep<RK, NW>() ? 2 : 1; }   // W2 chunks staged ahead
+template <int RK, int NW>
+constexpr int plain_pd() { return plain_deep<RK, NW>() ? 3 : 1; }   // epilogue chunks ahead
+template <int RK, int NW>
+constexpr int plain_unroll() { return lcm_small(plain_wd<RK, NW>(), plain_pd<RK, NW>() + 1); }
+
+template <int RK, int NW, int MODE, bool VEC4, bool BIAS>
 __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
-    const int32_t* __restrict__ prev, int prev_stride, int R, int gamma, int V, int r, int k,
-    float inv_t, int n_rblocks, int n_vgroups, int cpg, int n_chunks, int vec4,
+    const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
+    int n_rblocks, int n_vgroups, int cpg, int n_chunks, Addr ad,
     float2* __restrict__ partials, float* __restrict__ bias_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int KS = RK / 16;                          // MFMA K steps at the compiled bucket
-  constexpr int NT = NW * 64;                          // threads per workgroup
-  constexpr int PPR = RK / 8;                          // 16-byte pieces per LDS row
-  constexpr int PIECES = kChunk * PPR;                 // pieces per chunk
-  constexpr int PMAX = (PIECES + NT - 1) / NT;         // pieces per thread per chunk
-  constexpr int PITCH = RK + 8;                        // bf16 per LDS row (16-byte pad)
-  constexpr int BUF = kChunk * PITCH;                  // bf16 per LDS buffer
-  constexpr int WD = w2_depth<RK, NW>();                // W2 staging slots (chunks in flight)
-  constexpr int PD = epi_depth<RK, NW>();
-  constexpr int NS = PD + 1;                           // epilogue register slots
-  constexpr int UNR = lcm_small(WD, NS);               // unroll keeping slot indices static
+  constexpr int KS = RK / 16;
+  constexpr int NT = NW * 64;
+  constexpr int ROWS = NW * 32;
+  constexpr int PMAX = (kChunk * (RK / 8) + NT - 1) / NT;
+  constexpr int PITCH = RK + 8;
+  constexpr int BUF = kChunk * PITCH;
+  constexpr int WD = plain_wd<RK, NW>();
+  constexpr int PD = plain_pd<RK, NW>();
+  constexpr int NS = PD + 1;
+  constexpr int UNR = plain_unroll<RK, NW>();
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,21 +216,18 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // XCD-aware decode of the workgroup id.
   const int id = blockIdx.x;
   const int q = id >> 3;
   const int rb = q % n_rblocks;
   const int vg = (q / n_rblocks) * 8 + (id & 7);
   if (vg >= n_vgroups) return;
   const int c_begin = vg * cpg;
-  const int c_end = min(c_begin + cpg, n_chunks);
-
-  const int ksteps = r >> 4;
-  const int rpieces = r >> 3;                          // pieces at or beyond are stored as zeros
+  const int c_end = min(c_begin + cpg, n_chunks);      // cpg is a multiple of UNR
+  const int c_last = c_end - 1;                        // prefetches stay in the group
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
-  // ---- gather: this lane's request row of W1 becomes the MFMA B operand ----
-  const int m = rb * (NW * 32) + wave * 32 + col;
+  const int m_loc = wave * 32 + col;
+  const int m = rb * ROWS + m_loc;
   const bool m_ok = m < R;
   bf16x8 e[KS];
   {
@@ -118,179 +235,278 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
     x = min(max(x, 0), V - 1);                          // out-of-range ids never fault
     const uint16_t* er = W1 + (size_t)x * r + half * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s < ksteps && m_ok) {
-        e[s] = ld_bf16x8(er + s * 16);
-      } else {
-        e[s] = bf16x8{};
-      }
-    }
+    for (int s = 0; s < KS; ++s) e[s] = (s * 16 < r && m_ok) ? ld_bf16x8(er + s * 16) : bf16x8{};
   }
 
-  // ---- W2 chunk staging: piece p = (row, 8-element column block) of a chunk ----
+  const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
+  const uint32_t w2_off = w2_lane_offset<RK, NT>(tid, r);
+  const Rsrc rbase = block_rsrc(base, ad, rb, ROWS);
+  const Rsrc runif = block_rsrc(MODE == DSPARK_SAMPLE ? unif : base, ad, rb, ROWS);
+  const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 4 * half) * 4u;
+  const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
+
   u32x4 stage[WD][PMAX];
-  auto load_chunk = [&](int c, u32x4 (&st)[PMAX]) {
-    const int v0 = c * kChunk;
-#pragma unroll
-    for (int j = 0; j < PMAX; ++j) {
-      const int p = tid + j * NT;
-      const int row = p / PPR;
-      const int cp = p % PPR;
-      if (p < PIECES && cp < rpieces && v0 + row < V) {
-        st[j] = *reinterpret_cast<const u32x4*>(W2 + (size_t)(v0 + row) * r + cp * 8);
-      } else {
-        st[j] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_chunk = [&](int b, const u32x4 (&st)[PMAX]) {
-    uint16_t* dst = lds + b * BUF;
-#pragma unroll
-    for (int j = 0; j < PMAX; ++j) {
-      const int p = tid + j * NT;
-      if (p < PIECES) *reinterpret_cast<u32x4*>(dst + (p / PPR) * PITCH + (p % PPR) * 8) = st[j];
-    }
-  };
-
-  const size_t row_off = ((size_t)(m_ok ? m : 0) * gamma + k) * (size_t)V;
-  const float* brow = base + row_off;
-  const float* urow = (MODE == DSPARK_SAMPLE) ? unif + row_off : nullptr;
-  float* bout = bias_out ? bias_out + row_off : nullptr;
-
-  // Epilogue inputs of chunk c in the accumulator layout: element 4*jq + i is
-  // vocabulary entry c*32 + 8*jq + 4*half + i of this lane's request.
   float eb[NS][16];
   float eu[NS][16];
-  auto load_epi = [&](int c, float (&bv)[16], float (&uv)[16]) {
-    if (!m_ok) return;
-    const int v0 = c * kChunk;
-    if (vec4 && v0 + kChunk <= V) {
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int v = v0 + 8 * jq + 4 * half;
-        const float4 t = *reinterpret_cast<const float4*>(brow + v);
-        bv[4 * jq + 0] = t.x; bv[4 * jq + 1] = t.y; bv[4 * jq + 2] = t.z; bv[4 * jq + 3] = t.w;
-        if (MODE == DSPARK_SAMPLE) {
-          const float4 w = *reinterpret_cast<const float4*>(urow + v);
-          uv[4 * jq + 0] = w.x; uv[4 * jq + 1] = w.y; uv[4 * jq + 2] = w.z; uv[4 * jq + 3] = w.w;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = v0 + 8 * jq + 4 * half + i;
-          const bool ok = v < V;
-          bv[4 * jq + i] = ok ? brow[v] : 0.f;
-          if (MODE == DSPARK_SAMPLE) uv[4 * jq + i] = ok ? urow[v] : 0.5f;
-        }
-      }
-    }
-  };
-
   float best = -INFINITY;
   int best_i = 0x7fffffff;
-  // Selection score of one element.  Sampling: z/T - ln(-ln u) with the hardware
-  // base-2 logarithm (relative error ~1e-7 over the whole open unit interval).
-  auto score = [&](float b, float a, float u) {
-    const float z = b + a;
-    if (MODE == DSPARK_SAMPLE) {
-      constexpr float kLn2 = 0.693147180559945309f;
-      const float w = -kLn2 * __builtin_amdgcn_logf(u);      // -ln u  (> 0)
-      return fmaf(-kLn2, __builtin_amdgcn_logf(w), z * inv_t);
-    }
-    return z;
-  };
 
-  // One chunk: stage W2 into LDS, prefetch, bias tile on MFMA, fused select.
   auto body = [&](int c, u32x4 (&st)[PMAX], float (&cb)[16], float (&cu)[16], float (&pb)[16],
                   float (&pu)[16]) {
     const int b = (c - c_begin) & 1;
-    store_chunk(b, st);
+    w2_store<RK, NT, PMAX>(lds + b * BUF, st, tid);
     lds_barrier();
-    if (c + WD < c_end) load_chunk(c + WD, st);        // the slot just stored is free again
-    if (c + PD < c_end) load_epi(c + PD, pb, pu);
+    w2_load<RK, NT, PMAX>(st, rw2, w2_off, min(c + WD, c_last), r);
+    epi_load<MODE, VEC4, 4>(pb, pu, rbase, runif, e_off + (uint32_t)min(c + PD, c_last) * e_cb);
+    __builtin_amdgcn_sched_barrier(0);   // issue the prefetches before the MFMAs
 
-    // Bias tile: 32 vocabulary rows x 32 requests over the compiled K = RK.  The
-    // steps beyond r multiply zero-filled LDS columns by zero E registers, so the
-    // loop has no branches and the LDS reads pipeline ahead of the MFMAs.
+    // Bias tile: 32 vocabulary rows x 32 requests over the compiled K = RK
+    // (steps past r multiply zero-filled LDS columns by zero registers).
     const uint16_t* abase = lds + b * BUF + col * PITCH + half * 8;
     f32x16 acc = {};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + s * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, e[s], acc, 0, 0, 0);
+    for (int s0 = 0; s0 < KS; s0 += 4) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(abase + (s0 + i) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], e[s0 + i], acc, 0, 0, 0);
     }
 
-    // Fused bias-add + select.  Lane holds rows v0 + 8*jq + 4*half + i of column m.
-    const int v0 = c * kChunk;
-    if (m_ok) {
-      const int vl = v0 + 4 * half;
-      if (v0 + kChunk <= V) {
+    // Fused bias-add + select; chunks are walked in increasing v, so a strict
+    // comparison keeps the smallest id among equal maxima within a lane.
+    const int vl = c * kChunk + 4 * half;
+    const int vlim = (c < c_end && m_ok) ? V : 0;
 #pragma unroll
-        for (int qq = 0; qq < 16; ++qq) {
-          const float sc = score(cb[qq], acc[qq], cu[qq]);
-          if (sc > best) {
-            best = sc;
-            best_i = vl + 8 * (qq >> 2) + (qq & 3);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int qq = 0; qq < 16; ++qq) {
-          const int vi = vl + 8 * (qq >> 2) + (qq & 3);
-          const float sc = score(cb[qq], acc[qq], cu[qq]);
-          if (vi < V && sc > best) {
-            best = sc;
-            best_i = vi;
-          }
-        }
-      }
-      if (bout) {
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const int v = v0 + 8 * jq + 4 * half;
-          if (vec4 && v + 3 < V) {
-            *reinterpret_cast<float4*>(bout + v) =
-                make_float4(acc[4 * jq], acc[4 * jq + 1], acc[4 * jq + 2], acc[4 * jq + 3]);
-          } else {
-            for (int i = 0; i < 4; ++i)
-              if (v + i < V) bout[v + i] = acc[4 * jq + i];
-          }
-        }
+    for (int qq = 0; qq < 16; ++qq) {
+      const int vi = vl + 8 * (qq >> 2) + (qq & 3);
+      const float sc = select_score<MODE>(cb[qq], acc[qq], cu[qq], inv_t);
+      if (vi < vlim && sc > best) {
+        best = sc;
+        best_i = vi;
       }
     }
+    if (BIAS) {
+      float* oc = bias_out + ad.k_off + (size_t)min(m, R - 1) * ad.row_stride +
+                  (size_t)min(c, n_chunks - 1) * ad.cstride;
+#pragma unroll
+      for (int qq = 0; qq < 16; ++qq) {
+        const int o = 8 * (qq >> 2) + 4 * half + (qq & 3);
+        if (c * kChunk + o < vlim) oc[o] = acc[qq];
+      }
+    }
+    // Keep each chunk's arithmetic in its own iteration: hoisting the noise of
+    // a prefetched chunk next to its load would wait for that load.
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Prologue loads in the order they are consumed (oldest first), so that the
+  // waits at the top of the loop can count them from the back.
 #pragma unroll
-  for (int t = 0; t < WD; ++t)
-    if (c_begin + t < c_end) load_chunk(c_begin + t, stage[t]);
+  for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
+    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, min(c_begin + t, c_last), r);
+    if (t < PD)
+      epi_load<MODE, VEC4, 4>(eb[t], eu[t], rbase, runif,
+                              e_off + (uint32_t)min(c_begin + t, c_last) * e_cb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int c0 = c_begin; c0 < c_begin + cpg; c0 += UNR) {
 #pragma unroll
-  for (int t = 0; t < PD; ++t)
-    if (c_begin + t < c_end) load_epi(c_begin + t, eb[t], eu[t]);
-  // Unrolled so that every register-slot index is static.
-  for (int c0 = c_begin; c0 < c_end; c0 += UNR) {
-#pragma unroll
-    for (int j = 0; j < UNR; ++j) {
-      if (c0 + j < c_end)
-        body(c0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
-    }
+    for (int j = 0; j < UNR; ++j)
+      body(c0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
   }
 
   // Lanes l and l^32 hold the same request: merge, then one lane writes the partial.
   const float ov = __shfl_xor(best, 32);
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
-  if (m_ok && half == 0) {
-    partials[(size_t)vg * R + m] = make_float2(best, __int_as_float(best_i));
+  if (m_ok && half == 0) partials[(size_t)vg * R + m] = make_float2(best, __int_as_float(best_i));
+}
+
+// ---------------------------------------------------------------------------
+// K-split kernel (rank 512): wave pairs share 32 requests, one K half each.
+// After its MFMAs each wave hands the half-tile it does not finish (groups
+// jq outside {2kh, 2kh+1}) to its partner through a double-buffered LDS slot;
+// the epilogue of chunk c-1 runs in iteration c beside the MFMAs of chunk c,
+// so one barrier per chunk orders everything.  Each wave writes its own
+// partial per request and V group (two partials per group).
+// ---------------------------------------------------------------------------
+constexpr int kSplitWD = 2;
+constexpr int kSplitPD = 2;
+constexpr int kSplitUnroll = lcm_small(kSplitWD, kSplitPD + 1);
+
+template <int NP>
+constexpr size_t ksplit_lds_bytes() {
+  return (size_t)2 * kChunk * (512 + 8) * 2 + (size_t)2 * (2 * NP) * 64 * 8 * 4;
+}
+
+template <int NP, int MODE, bool VEC4, bool BIAS>
+__global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
+    const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
+    const float* __restrict__ base, const float* __restrict__ unif,
+    const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
+    int n_rblocks, int n_vgroups, int cpg, int n_chunks, Addr ad,
+    float2* __restrict__ partials, float* __restrict__ bias_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int RK = 512;
+  constexpr int NW = 2 * NP;
+  constexpr int NT = NW * 64;
+  constexpr int ROWS = NP * 32;
+  constexpr int KH = RK / 32;                          // MFMA K steps per half
+  constexpr int PMAX = (kChunk * (RK / 8) + NT - 1) / NT;
+  constexpr int PITCH = RK + 8;
+  constexpr int BUF = kChunk * PITCH;
+  constexpr int WD = kSplitWD;
+  constexpr int PD = kSplitPD;
+  constexpr int NS = PD + 1;
+  constexpr int UNR = kSplitUnroll;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int pair = wave >> 1;
+  const int kh = wave & 1;
+
+  const int id = blockIdx.x;
+  const int q = id >> 3;
+  const int rb = q % n_rblocks;
+  const int vg = (q / n_rblocks) * 8 + (id & 7);
+  if (vg >= n_vgroups) return;
+  const int c_begin = vg * cpg;
+  const int c_end = min(c_begin + cpg, n_chunks);
+  const int c_last = c_end - 1;
+  uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
+  float* xbuf = reinterpret_cast<float*>(smem + (size_t)2 * BUF * 2);   // [2][NW][64][8]
+
+  const int m_loc = pair * 32 + col;
+  const int m = rb * ROWS + m_loc;
+  const bool m_ok = m < R;
+  bf16x8 e[KH];
+  {
+    int x = m_ok ? prev[(size_t)m * prev_stride] : 0;
+    x = min(max(x, 0), V - 1);
+    const uint16_t* er = W1 + (size_t)x * r + half * 8;
+#pragma unroll
+    for (int s = 0; s < KH; ++s) {
+      const int ks = kh * KH + s;
+      e[s] = (ks * 16 < r && m_ok) ? ld_bf16x8(er + ks * 16) : bf16x8{};
+    }
   }
+
+  const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
+  const uint32_t w2_off = w2_lane_offset<RK, NT>(tid, r);
+  const Rsrc rbase = block_rsrc(base, ad, rb, ROWS);
+  const Rsrc runif = block_rsrc(MODE == DSPARK_SAMPLE ? unif : base, ad, rb, ROWS);
+  const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 16 * kh + 4 * half) * 4u;
+  const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
+
+  u32x4 stage[WD][PMAX];
+  float eb[NS][8];
+  float eu[NS][8];
+  float own[8];
+  float best = -INFINITY;
+  int best_i = 0x7fffffff;
+
+  // Epilogue of chunk c: own half-tile + partner's from xbuf slot xs.
+  auto epilogue = [&](int c, int xs, const float (&cb)[8], const float (&cu)[8]) {
+    const float* px = xbuf + (((size_t)xs * NW + (wave ^ 1)) * 64 + lane) * 8;
+    const float4 p0 = *reinterpret_cast<const float4*>(px);
+    const float4 p1 = *reinterpret_cast<const float4*>(px + 4);
+    const float part[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const int vl = c * kChunk + 16 * kh + 4 * half;
+    const int vlim = (c < c_end && m_ok) ? V : 0;
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) {
+      const int vi = vl + 8 * (qq >> 2) + (qq & 3);
+      const float sc = select_score<MODE>(cb[qq], part[qq] + own[qq], cu[qq], inv_t);
+      if (vi < vlim && sc > best) {
+        best = sc;
+        best_i = vi;
+      }
+    }
+    if (BIAS) {
+      float* oc = bias_out + ad.k_off + (size_t)min(m, R - 1) * ad.row_stride +
+                  (size_t)min(c, n_chunks - 1) * ad.cstride;
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        const int o = 16 * kh + 8 * (qq >> 2) + 4 * half + (qq & 3);
+        if (c * kChunk + o < vlim) oc[o] = part[qq] + own[qq];
+      }
+    }
+  };
+
+  auto body = [&](int c, u32x4 (&st)[PMAX], float (&pb)[8], float (&pu)[8], float (&nb)[8],
+                  float (&nu)[8]) {
+    const int t = c - c_begin;
+    w2_store<RK, NT, PMAX>(lds + (t & 1) * BUF, st, tid);
+    lds_barrier();
+    w2_load<RK, NT, PMAX>(st, rw2, w2_off, min(c + WD, c_last), r);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const uint16_t* abase = lds + (t & 1) * BUF + col * PITCH + half * 8 + kh * KH * 16;
+    f32x16 acc = {};
+#pragma unroll
+    for (int s0 = 0; s0 < KH; s0 += 4) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(abase + (s0 + i) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], e[s0 + i], acc, 0, 0, 0);
+    }
+    // Epilogue of the previous chunk (its partner half was written before this
+    // iteration's barrier).  At t = 0 there is none (a uniform branch with no
+    // memory loads).
+    if (t >= 1) epilogue(c - 1, (t - 1) & 1, pb, pu);
+    // Hand the other half-tile to the partner; keep ours for the next iteration.
+    const int oj = 2 * (kh ^ 1);
+    float* px = xbuf + (((size_t)(t & 1) * NW + wave) * 64 + lane) * 8;
+    *reinterpret_cast<float4*>(px) =
+        make_float4(acc[4 * oj], acc[4 * oj + 1], acc[4 * oj + 2], acc[4 * oj + 3]);
+    *reinterpret_cast<float4*>(px + 4) =
+        make_float4(acc[4 * oj + 4], acc[4 * oj + 5], acc[4 * oj + 6], acc[4 * oj + 7]);
+    const int mj = 2 * kh;
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) own[qq] = acc[4 * mj + qq];
+    // The slot of chunk c-1 is free now: refill it with chunk c + PD.
+    epi_load<MODE, VEC4, 2>(nb, nu, rbase, runif, e_off + (uint32_t)min(c + PD, c_last) * e_cb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+#pragma unroll
+  for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
+    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, min(c_begin + t, c_last), r);
+    if (t < PD)
+      epi_load<MODE, VEC4, 2>(eb[t], eu[t], rbase, runif,
+                              e_off + (uint32_t)min(c_begin + t, c_last) * e_cb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Chunk c's epilogue inputs live in slot (c - c_begin) % NS; iteration c
+  // finishes chunk c-1 and refills that slot with chunk c + PD.
+  for (int c0 = c_begin; c0 < c_begin + cpg; c0 += UNR) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j)
+      body(c0 + j, stage[j % WD], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS],
+           eb[(j + PD) % NS], eu[(j + PD) % NS]);
+  }
+  lds_barrier();   // the partner's last half-tile
+  // cpg is a multiple of UNR (hence of NS): the last chunk's slot is NS - 1.
+  epilogue(c_begin + cpg - 1, (cpg - 1) & 1, eb[NS - 1], eu[NS - 1]);
+
+  const float ov = __shfl_xor(best, 32);
+  const int oi = __shfl_xor(best_i, 32);
+  merge_best(best, best_i, ov, oi);
+  if (m_ok && half == 0)
+    partials[((size_t)vg * 2 + kh) * R + m] = make_float2(best, __int_as_float(best_i));
 }
 
 // Reduce the per-group partials [group][request] to x_k: one wave per request,
 // lanes stride over the groups (independent loads), then a fixed shuffle tree.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __restrict__ partials,
-                                                            int R, int n_vgroups, int V,
+                                                            int R, int n_groups, int V,
                                                             int gamma, int k,
                                                             int32_t* __restrict__ tokens) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -299,7 +515,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __rest
   float best = -INFINITY;
   int best_i = 0x7fffffff;
 #pragma unroll 4
-  for (int g = lane; g < n_vgroups; g += 64) {
+  for (int g = lane; g < n_groups; g += 64) {
     const float2 p = partials[(size_t)g * R + m];
     merge_best(best, best_i, p.x, __float_as_int(p.y));
   }
@@ -312,100 +528,86 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __rest
   if (lane == 0) tokens[(size_t)m * gamma + k] = best_i < V ? best_i : 0;
 }
 
-template <int RK, int NW, int MODE>
-dspark_status launch_step_t(const MarkovPlan& p, dim3 grid, size_t lds, hipStream_t stream,
-                            const uint16_t* W1, const uint16_t* W2, const float* base,
-                            const float* unif, const int32_t* prev, int prev_stride, int R,
-                            int gamma, int V, int r, int k, float inv_t, int vec4,
-                            float2* partials, float* bias_out) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&markov_step_kernel<RK, NW, MODE>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess) {
-      return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the Markov step kernel");
-    }
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((markov_step_kernel<RK, NW, MODE>), grid, dim3(NW * 64), lds, stream, W1,
-                     W2, base, unif, prev, prev_stride, R, gamma, V, r, k, inv_t, p.n_rblocks,
-                     p.n_vgroups, p.cpg, p.n_chunks, vec4, partials, bias_out);
-  return check_launch("markov_step_kernel");
+// ---- host side: kernel variants ----
+
+using StepKernel = void (*)(const uint16_t*, const uint16_t*, const float*, const float*,
+                            const int32_t*, int, int, int, int, float, int, int, int, int, Addr,
+                            float2*, float*);
+
+struct StepVariant {
+  StepKernel fn;
+  int threads;
+  size_t lds;
+  int rows;     // requests per workgroup
+  int split;    // partials per (request, V group)
+  int unroll;   // chunks per group must be a multiple of this
+};
+
+template <int RK, int NW, int MODE, bool VEC4, bool BIAS>
+StepVariant plain_variant() {
+  return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS>, NW * 64,
+          (size_t)2 * kChunk * (RK + 8) * 2, NW * 32, 1, plain_unroll<RK, NW>()};
+}
+template <int NP, int MODE, bool VEC4, bool BIAS>
+StepVariant ksplit_variant() {
+  return {&markov_step_ksplit_kernel<NP, MODE, VEC4, BIAS>, NP * 128, ksplit_lds_bytes<NP>(),
+          NP * 32, 2, kSplitUnroll};
 }
 
-template <int RK, int NW>
-dspark_status dispatch_mode(int mode, const MarkovPlan& p, dim3 grid, size_t lds,
-                            hipStream_t stream, const uint16_t* W1, const uint16_t* W2,
-                            const float* base, const float* unif, const int32_t* prev,
-                            int prev_stride, int R, int gamma, int V, int r, int k, float inv_t,
-                            int vec4, float2* partials, float* bias_out) {
-  if (mode == DSPARK_SAMPLE)
-    return launch_step_t<RK, NW, DSPARK_SAMPLE>(p, grid, lds, stream, W1, W2, base, unif, prev,
-                                                prev_stride, R, gamma, V, r, k, inv_t, vec4,
-                                                partials, bias_out);
-  return launch_step_t<RK, NW, DSPARK_GREEDY>(p, grid, lds, stream, W1, W2, base, unif, prev,
-                                              prev_stride, R, gamma, V, r, k, inv_t, vec4,
-                                              partials, bias_out);
-}
-
-template <int RK>
-dspark_status dispatch_nw(int mode, const MarkovPlan& p, dim3 grid, size_t lds,
-                          hipStream_t stream, const uint16_t* W1, const uint16_t* W2,
-                          const float* base, const float* unif, const int32_t* prev,
-                          int prev_stride, int R, int gamma, int V, int r, int k, float inv_t,
-                          int vec4, float2* partials, float* bias_out) {
-  switch (p.nw) {
-    case 1:
-      return dispatch_mode<RK, 1>(mode, p, grid, lds, stream, W1, W2, base, unif, prev,
-                                  prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-    case 2:
-      return dispatch_mode<RK, 2>(mode, p, grid, lds, stream, W1, W2, base, unif, prev,
-                                  prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-    case 4:
-      return dispatch_mode<RK, 4>(mode, p, grid, lds, stream, W1, W2, base, unif, prev,
-                                  prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-    default:
-      return dispatch_mode<RK, 8>(mode, p, grid, lds, stream, W1, W2, base, unif, prev,
-                                  prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-  }
-}
-
-// Workgroups of the step kernel that fit on one CU (cached per instantiation).
-template <int RK, int NW, int MODE>
-int blocks_per_cu_t() {
-  static int cached = 0;
-  if (!cached) {
-    int nb = 0;
-    const size_t lds = 2 * kChunk * (size_t)(RK + 8) * 2;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&markov_step_kernel<RK, NW, MODE>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&markov_step_kernel<RK, NW, MODE>), NW * 64,
-            lds) != hipSuccess || nb < 1)
-      nb = 1;
-    cached = nb;
-  }
-  return cached;
-}
-
-template <int RK>
-int blocks_per_cu_nw(int nw, int mode) {
-  const bool s = mode == DSPARK_SAMPLE;
+template <int RK, int MODE, bool VEC4, bool BIAS>
+StepVariant plain_by_nw(int nw) {
   switch (nw) {
-    case 1: return s ? blocks_per_cu_t<RK, 1, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 1, DSPARK_GREEDY>();
-    case 2: return s ? blocks_per_cu_t<RK, 2, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 2, DSPARK_GREEDY>();
-    case 4: return s ? blocks_per_cu_t<RK, 4, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 4, DSPARK_GREEDY>();
-    default: return s ? blocks_per_cu_t<RK, 8, DSPARK_SAMPLE>() : blocks_per_cu_t<RK, 8, DSPARK_GREEDY>();
+    case 1: return plain_variant<RK, 1, MODE, VEC4, BIAS>();
+    case 2: return plain_variant<RK, 2, MODE, VEC4, BIAS>();
+    case 4: return plain_variant<RK, 4, MODE, VEC4, BIAS>();
+    default: return plain_variant<RK, 8, MODE, VEC4, BIAS>();
   }
 }
-
-int blocks_per_cu(int rk, int nw, int mode) {
-  switch (rk) {
-    case 64: return blocks_per_cu_nw<64>(nw, mode);
-    case 128: return blocks_per_cu_nw<128>(nw, mode);
-    case 256: return blocks_per_cu_nw<256>(nw, mode);
-    default: return blocks_per_cu_nw<512>(nw, mode);
+template <int MODE, bool VEC4, bool BIAS>
+StepVariant pick3(const MarkovPlan& p) {
+  if (p.ksplit) {
+    switch (p.nw / 2) {
+      case 1: return ksplit_variant<1, MODE, VEC4, BIAS>();
+      case 2: return ksplit_variant<2, MODE, VEC4, BIAS>();
+      default: return ksplit_variant<4, MODE, VEC4, BIAS>();
+    }
   }
+  switch (p.rk) {
+    case 64: return plain_by_nw<64, MODE, VEC4, BIAS>(p.nw);
+    case 128: return plain_by_nw<128, MODE, VEC4, BIAS>(p.nw);
+    case 256: return plain_by_nw<256, MODE, VEC4, BIAS>(p.nw);
+    default: return plain_by_nw<512, MODE, VEC4, BIAS>(p.nw);
+  }
+}
+template <int MODE>
+StepVariant pick2(const MarkovPlan& p, bool vec4, bool bias) {
+  if (vec4) return bias ? pick3<MODE, true, true>(p) : pick3<MODE, true, false>(p);
+  return bias ? pick3<MODE, false, true>(p) : pick3<MODE, false, false>(p);
+}
+StepVariant pick_variant(const MarkovPlan& p, int mode, bool vec4, bool bias) {
+  return mode == DSPARK_SAMPLE ? pick2<DSPARK_SAMPLE>(p, vec4, bias)
+                               : pick2<DSPARK_GREEDY>(p, vec4, bias);
+}
+
+// Per-kernel launch attributes and occupancy, resolved once per variant.
+struct VariantState {
+  StepKernel fn;
+  int blocks_per_cu;
+};
+VariantState g_states[256];
+int g_nstates = 0;
+
+int prepare_variant(const StepVariant& v) {
+  for (int i = 0; i < g_nstates; ++i)
+    if (g_states[i].fn == v.fn) return g_states[i].blocks_per_cu;
+  const void* f = reinterpret_cast<const void*>(v.fn);
+  if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)v.lds) != hipSuccess)
+    return -1;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, v.threads, v.lds) != hipSuccess || nb < 1)
+    nb = 1;
+  if (g_nstates < 256) g_states[g_nstates++] = {v.fn, nb};
+  return nb;
 }
 
 int device_cus() {
@@ -425,82 +627,89 @@ int env_int(const char* name, int dflt) {
 
 MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch) {
   (void)gamma;
+  (void)for_launch;
   MarkovPlan p{};
   p.rk = r <= 64 ? 64 : r <= 128 ? 128 : r <= 256 ? 256 : 512;
   const int waves_needed = (R + 31) / 32;
   int nw = waves_needed >= 8 ? 8 : waves_needed >= 4 ? 4 : waves_needed >= 2 ? 2 : 1;
-  // Rank-512 sampling: the 8-wave kernel would spill; the 4-wave, one-wave-per-SIMD
-  // variant with deeper prefetch is used instead.
+  // Choices measured on MI355X.  Rank 512 sampling: K-split wave pairs (a
+  // plain wave would need the whole SIMD); rank 512 greedy: eight plain waves;
+  // up to 64 requests: one-wave workgroups (twice the workgroups, and the
+  // second R block's W2 reads hit L2).  DSPARK_MARKOV_KSPLIT / _NW / _WG
+  // override the choice for tuning.
+  if (waves_needed <= 2) nw = 1;
   if (p.rk == 512 && mode == DSPARK_SAMPLE && nw == 8) nw = 4;
+  const int ks_env = env_int("DSPARK_MARKOV_KSPLIT", -1);
+  p.ksplit = p.rk == 512 && (ks_env < 0 ? mode == DSPARK_SAMPLE : ks_env != 0);
+  if (p.ksplit) nw = 2 * (waves_needed >= 4 ? 4 : waves_needed >= 2 ? 2 : 1);
   const int nw_env = env_int("DSPARK_MARKOV_NW", 0);
-  if (nw_env == 1 || nw_env == 2 || nw_env == 4 || nw_env == 8) nw = nw_env;
+  if (!p.ksplit && (nw_env == 1 || nw_env == 2 || nw_env == 4 || nw_env == 8)) nw = nw_env;
   p.nw = nw;
-  p.n_rblocks = (R + 32 * nw - 1) / (32 * nw);
+  const int rows = p.ksplit ? nw / 2 * 32 : nw * 32;
+  p.n_rblocks = (R + rows - 1) / rows;
   p.n_chunks = (V + kChunk - 1) / kChunk;
   const int max_groups = p.n_chunks < kMaxGroups ? p.n_chunks : kMaxGroups;
-  p.ws_bytes = (size_t)R * (size_t)max_groups * sizeof(float2);
-  if (!for_launch) return p;
+  p.ws_bytes = (size_t)R * (size_t)max_groups * 2 * sizeof(float2);
+  return p;
+}
+
+dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                  const int32_t* anchors, int R, int gamma, int V, int r,
+                                  int layout, int mode, float temperature,
+                                  const float* uniforms, int32_t* tokens, float* bias_out,
+                                  void* workspace, const dspark_step_events* events,
+                                  hipStream_t stream) {
+  MarkovPlan p = plan_markov(R, gamma, V, r, mode, true);
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const bool tiled = layout == DSPARK_LAYOUT_TILED;
+  const bool vec4 = (tiled || V % 4 == 0) && V >= 4 && a16(base) &&
+                    (!uniforms || a16(uniforms)) && (!bias_out || a16(bias_out));
+  const StepVariant var = pick_variant(p, mode, vec4, bias_out != nullptr);
+  const int bpc = prepare_variant(var);
+  if (bpc < 0) return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the Markov step kernel");
+
   // One wave of workgroups: as many as fit on the device at once, split between
-  // the R blocks (each V group is walked by n_rblocks workgroups).
+  // the R blocks (each V group is walked by n_rblocks workgroups).  Groups hold
+  // a multiple of the kernel's unroll factor of chunks.
+  const int max_groups = p.n_chunks < kMaxGroups ? p.n_chunks : kMaxGroups;
   int target = env_int("DSPARK_MARKOV_WG", 0);
-  if (target <= 0) target = device_cus() * blocks_per_cu(p.rk, nw, mode);
+  if (target <= 0) target = device_cus() * bpc;
   if (target < 8) target = 8;
   int groups = (target + p.n_rblocks - 1) / p.n_rblocks;
   groups = (groups + 7) / 8 * 8;
   if (groups > max_groups) groups = max_groups;
   if (groups < 1) groups = 1;
   p.cpg = (p.n_chunks + groups - 1) / groups;
+  p.cpg = (p.cpg + var.unroll - 1) / var.unroll * var.unroll;
   p.n_vgroups = (p.n_chunks + p.cpg - 1) / p.cpg;
-  return p;
-}
 
-dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
-                                  const int32_t* anchors, int R, int gamma, int V, int r,
-                                  int mode, float temperature, const float* uniforms,
-                                  int32_t* tokens, float* bias_out, void* workspace,
-                                  const dspark_step_events* events, hipStream_t stream) {
-  const MarkovPlan p = plan_markov(R, gamma, V, r, mode, true);
   float2* partials = reinterpret_cast<float2*>(workspace);
   const int padded_groups = (p.n_vgroups + 7) / 8 * 8;
   const dim3 grid(padded_groups * p.n_rblocks);
-  const size_t lds = 2 * kChunk * (size_t)(p.rk + 8) * 2;   // two W2 chunk buffers
   const float inv_t = mode == DSPARK_SAMPLE ? 1.0f / temperature : 1.0f;
-  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
-  const int vec4 = (V % 4 == 0) && a16(base) && (!uniforms || a16(uniforms)) &&
-                   (!bias_out || a16(bias_out));
+  Addr ad;
+  ad.row_stride = tiled ? (size_t)kChunk : (size_t)gamma * V;
+  ad.cstride = tiled ? (size_t)R * kChunk : (size_t)kChunk;
+  ad.total = tiled ? (size_t)gamma * p.n_chunks * R * kChunk : (size_t)R * gamma * V;
   for (int k = 0; k < gamma; ++k) {
     const int32_t* prev = k == 0 ? anchors : tokens + (k - 1);
     const int prev_stride = k == 0 ? 1 : gamma;
+    ad.k_off = tiled ? (size_t)k * p.n_chunks * R * kChunk : (size_t)k * V;
     if (events && k < events->count && events->begin && events->begin[k]) {
       if (hipEventRecord(reinterpret_cast<hipEvent_t>(events->begin[k]), stream) != hipSuccess)
         return fail(DSPARK_EDEVICE, "hipEventRecord failed");
     }
-    dspark_status st;
-    switch (p.rk) {
-      case 64:
-        st = dispatch_nw<64>(mode, p, grid, lds, stream, W1, W2, base, uniforms, prev,
-                             prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-        break;
-      case 128:
-        st = dispatch_nw<128>(mode, p, grid, lds, stream, W1, W2, base, uniforms, prev,
-                              prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-        break;
-      case 256:
-        st = dispatch_nw<256>(mode, p, grid, lds, stream, W1, W2, base, uniforms, prev,
-                              prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-        break;
-      default:
-        st = dispatch_nw<512>(mode, p, grid, lds, stream, W1, W2, base, uniforms, prev,
-                              prev_stride, R, gamma, V, r, k, inv_t, vec4, partials, bias_out);
-        break;
-    }
+    hipLaunchKernelGGL(var.fn, grid, dim3(var.threads), var.lds, stream, W1, W2, base, uniforms,
+                       prev, prev_stride, R, V, r, inv_t, p.n_rblocks, p.n_vgroups, p.cpg,
+                       p.n_chunks, ad, partials, bias_out);
+    dspark_status st = check_launch("markov_step_kernel");
     if (st != DSPARK_OK) return st;
     if (events && k < events->count && events->end && events->end[k]) {
       if (hipEventRecord(reinterpret_cast<hipEvent_t>(events->end[k]), stream) != hipSuccess)
         return fail(DSPARK_EDEVICE, "hipEventRecord failed");
     }
     hipLaunchKernelGGL(argmax_reduce_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, partials,
-                       R, p.n_vgroups, V, gamma, k, tokens);
+                       R, p.n_vgroups * var.split, V, gamma, k, tokens);
     st = check_launch("argmax_reduce_kernel");
     if (st != DSPARK_OK) return st;
   }

@@ -60,6 +60,21 @@ typedef enum {
   DSPARK_SAMPLE = 1  /* x_k = argmax_v (z_v / T - ln(-ln u_v))  (Gumbel-max) */
 } dspark_mode;
 
+/* Storage order of the [R, gamma, V] fp32 arrays of dspark_markov_draft (base,
+ * uniforms, bias_out).  Element (m, k, v) -- request m, position k (0-based),
+ * vocabulary entry v -- sits at
+ *   DSPARK_LAYOUT_RGV:   (m * gamma + k) * V + v                     (row-major [R][gamma][V])
+ *   DSPARK_LAYOUT_TILED: ((k * C + v / 32) * R + m) * 32 + v % 32,  C = ceil(V / 32)
+ * The tiled order ([gamma][C][R][32], tail columns of the last chunk padding)
+ * puts the 32-column slice of every request that one step reads together in
+ * one contiguous block, which the HBM streams at full burst length; a backbone
+ * LM-head epilogue or a random-number fill can write it at no extra cost.
+ * Row-major arrays are read in 128-byte pieces per request row instead. */
+typedef enum {
+  DSPARK_LAYOUT_RGV = 0,
+  DSPARK_LAYOUT_TILED = 1
+} dspark_layout;
+
 /* Limits of this build. */
 #define DSPARK_MAX_RANK 512          /* r <= 512 and r % 16 == 0 */
 #define DSPARK_MAX_CANDIDATES (1 << 23) /* R * gamma, keeps the fixed-point tau sum exact */
@@ -100,24 +115,31 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *   W1        [V, r] bf16   Markov embedding table (row t = W1[t]).
  *   W2        [V, r] bf16   the r x V projection stored column by column:
  *                           element (i, v) at W2[v * r + i].
- *   base      [R, gamma, V] fp32 backbone base logits.
+ *   layout    DSPARK_LAYOUT_RGV or DSPARK_LAYOUT_TILED: storage order of base,
+ *             uniforms and bias_out (see dspark_layout).
+ *   base      [R, gamma, V] fp32 backbone base logits (in `layout` order; the
+ *             tiled order holds gamma * C * R * 32 floats).
  *   anchors   [R] int32     anchor token of each request (x_0), in [0, V).
  *   mode      DSPARK_GREEDY or DSPARK_SAMPLE.
  *   temperature  > 0 and finite when mode == DSPARK_SAMPLE; ignored for GREEDY.
- *   uniforms  [R, gamma, V] fp32 in (0, 1), required iff SAMPLE (NULL for GREEDY).
+ *   uniforms  [R, gamma, V] fp32 in (0, 1) in `layout` order, required iff SAMPLE
+ *             (NULL for GREEDY).
  *   tokens    [R, gamma] int32 output, tokens[m * gamma + k - 1] = x_k.
- *   bias_out  optional [R, gamma, V] fp32 output of the Markov bias of every
- *             step (a debugging aid; pass NULL on the hot path).
+ *   bias_out  optional [R, gamma, V] fp32 output (in `layout` order) of the
+ *             Markov bias of every step (a debugging aid; NULL on the hot path).
  *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...).
  *   events    optional timing hooks (NULL on the hot path).
  * Errors: EINVAL for NULL required pointers, R/gamma/V/r <= 0, V < 2, a bad
- * mode, a non-positive or non-finite temperature in SAMPLE mode, or uniforms
- * given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or r % 16 != 0;
- * EWORKSPACE if the workspace is too small; EDEVICE on a launch failure.
+ * layout or mode, a non-positive or non-finite temperature in SAMPLE mode, or uniforms
+ * given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or r % 16 != 0, and
+ * where one step of one block of requests would not fit 32-bit byte offsets:
+ * ceil(V/32)*32*r > 2^30, gamma*V >= 2^22 (DSPARK_LAYOUT_RGV) or
+ * ceil(V/32)*R + 256 > 2^25 (DSPARK_LAYOUT_TILED); EWORKSPACE if the workspace
+ * is too small; EDEVICE on a launch failure.
  */
 dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
                                   const int32_t* anchors, int R, int gamma, int V, int r,
-                                  int mode, float temperature, const float* uniforms,
+                                  int layout, int mode, float temperature, const float* uniforms,
                                   int32_t* tokens, float* bias_out, void* workspace,
                                   size_t ws_bytes, const dspark_step_events* events,
                                   void* stream);

@@ -40,13 +40,27 @@ def to_device(wl: dict, device="cuda:0") -> dict:
     return g
 
 
-def run_draft(wl, g, bias=False):
+def run_draft(wl, g, bias=False, layout=D.LAYOUT_RGV):
+    """Run the draft on the device copies in g; `layout` picks the storage order of
+    base / uniforms / bias_out (tiled copies are made here from the logical arrays)."""
+    from draft_head_step_amd.inputs import from_tiled, to_tiled
     R, gm, V = wl["base"].shape
-    bias_out = torch.empty((R, gm, V), dtype=torch.float32, device=g["base"].device) if bias else None
-    tok = D.dspark_markov_draft(g["W1"], g["W2"], g["base"], g["anchors"], wl["mode"],
-                                wl["temperature"], g.get("uniforms"), bias_out=bias_out)
+    dev = g["W1"].device
+    if layout == D.LAYOUT_TILED:
+        base = torch.from_numpy(to_tiled(wl["base"])).to(dev)
+        unif = None if wl["uniforms"] is None else torch.from_numpy(to_tiled(wl["uniforms"])).to(dev)
+    else:
+        base, unif = g["base"], g.get("uniforms")
+    bias_out = torch.full(base.shape, float("nan"), dtype=torch.float32, device=dev) if bias else None
+    tok = D.dspark_markov_draft(g["W1"], g["W2"], base, g["anchors"], wl["mode"],
+                                wl["temperature"], unif, bias_out=bias_out, layout=layout)
     torch.cuda.synchronize()
-    return tok.cpu().numpy(), (bias_out.cpu().numpy() if bias else None)
+    b = None
+    if bias:
+        b = bias_out.cpu().numpy()
+        if layout == D.LAYOUT_TILED:
+            b = from_tiled(b, V)
+    return tok.cpu().numpy(), b
 
 
 def check_draft(wl, gpu_tokens, rows=None, gpu_bias=None):

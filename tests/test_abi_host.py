@@ -58,11 +58,11 @@ def test_workspace_queries():
     assert big >= 5 * 8192 * 7 * 4
 
 
-def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, mode=GREEDY, T=1.0, u=None,
-           tokens=P, ws=P, ws_bytes=1 << 30, events=None):
+def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, layout=0, mode=GREEDY, T=1.0,
+           u=None, tokens=P, ws=P, ws_bytes=1 << 30, events=None):
     L = D.lib()
-    return L.dspark_markov_draft(W1, W2, base, anchors, R, g, V, r, mode, T, u, tokens, None, ws,
-                                 ws_bytes, events, None)
+    return L.dspark_markov_draft(W1, W2, base, anchors, R, g, V, r, layout, mode, T, u, tokens,
+                                 None, ws, ws_bytes, events, None)
 
 
 @no_gpu
@@ -70,7 +70,7 @@ def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, mode=GREEDY, T
     (dict(W1=None), EINVAL), (dict(W2=None), EINVAL), (dict(base=None), EINVAL),
     (dict(anchors=None), EINVAL), (dict(tokens=None), EINVAL),
     (dict(R=0), EINVAL), (dict(g=-1), EINVAL), (dict(V=1), EINVAL), (dict(r=0), EINVAL),
-    (dict(mode=2), EINVAL),
+    (dict(mode=2), EINVAL), (dict(layout=2), EINVAL), (dict(layout=-1), EINVAL),
     (dict(mode=SAMPLE, u=None), EINVAL),
     (dict(mode=SAMPLE, u=P, T=0.0), EINVAL),
     (dict(mode=SAMPLE, u=P, T=-1.0), EINVAL),
@@ -79,6 +79,10 @@ def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, mode=GREEDY, T
     (dict(mode=GREEDY, u=P), EINVAL),
     (dict(W1=P + 4), EINVAL),
     (dict(r=40), EUNSUPPORTED), (dict(r=1024), EUNSUPPORTED),
+    # 32-bit byte offsets of one step of one request block
+    (dict(g=1, V=1 << 22), EUNSUPPORTED),                       # gamma*V = 2^22, RGV
+    (dict(V=(1 << 21) + 32, r=512, layout=1), EUNSUPPORTED),   # ceil(V/32)*32*r > 2^30
+    (dict(R=1 << 20, V=4096, layout=1), EUNSUPPORTED),         # ceil(V/32)*R > 2^25
     (dict(ws=None), EWORKSPACE), (dict(ws_bytes=8), EWORKSPACE),
 ])
 def test_markov_draft_rejects(kw, want):
@@ -139,3 +143,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(D, "_LIB", None)
     with pytest.raises(ImportError):
         D.lib()
+
+
+def test_tiled_layout_roundtrip():
+    import numpy as np
+    from draft_head_step_amd.inputs import from_tiled, to_tiled
+    x = np.random.default_rng(0).standard_normal((5, 3, 70)).astype(np.float32)
+    t = to_tiled(x)
+    assert t.shape == (3, 3, 5, 32)
+    # element (m, k, v) at ((k * C + v // 32) * R + m) * 32 + v % 32
+    flat = t.reshape(-1)
+    for (m, k, v) in [(0, 0, 0), (4, 2, 69), (2, 1, 33), (3, 0, 31)]:
+        assert flat[((k * 3 + v // 32) * 5 + m) * 32 + v % 32] == x[m, k, v]
+    assert np.array_equal(from_tiled(t, 70), x)
+    assert np.all(t[:, 2, :, 6:] == 0)

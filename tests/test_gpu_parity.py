@@ -29,9 +29,9 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _full_path_check(wl, rows=None, bias_rows=True):
+def _full_path_check(wl, rows=None, bias_rows=True, layout=D.LAYOUT_RGV):
     g = H.to_device(wl, DEV)
-    toks, bias = H.run_draft(wl, g, bias=bias_rows)
+    toks, bias = H.run_draft(wl, g, bias=bias_rows, layout=layout)
     n_clear, n_amb = H.check_draft(wl, toks, rows, bias)
     tok_dev = torch.from_numpy(toks).to(DEV)
     conf, surv = H.run_confidence(wl, g, tok_dev)
@@ -43,10 +43,11 @@ def _full_path_check(wl, rows=None, bias_rows=True):
 
 # --------------------------------------------------------------------------- tiny
 
-def test_tiny_greedy_end_to_end():
-    _say("case tiny greedy")
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
+def test_tiny_greedy_end_to_end(layout):
+    _say(f"case tiny greedy layout={layout}")
     wl = make_workload(CONFIGS["tiny"])
-    _, n_clear, _ = _full_path_check(wl)
+    _, n_clear, _ = _full_path_check(wl, layout=layout)
     assert n_clear > 0
 
 
@@ -57,12 +58,12 @@ def test_tiny_bias_dominant_moves_tokens():
     assert (toks != np.argmax(wl["base"], axis=2)).any()
 
 
-@pytest.mark.parametrize("T", [1.0, 0.7])
-def test_tiny_sampling(T):
-    _say(f"case tiny sample T={T}")
+@pytest.mark.parametrize("T,layout", [(1.0, D.LAYOUT_RGV), (0.7, D.LAYOUT_RGV), (0.7, D.LAYOUT_TILED)])
+def test_tiny_sampling(T, layout):
+    _say(f"case tiny sample T={T} layout={layout}")
     cfg = dataclasses.replace(CONFIGS["tiny"], mode=SAMPLE, temperature=T)
     wl = make_workload(cfg, w_std=0.2)
-    _full_path_check(wl)
+    _full_path_check(wl, layout=layout)
 
 
 def test_deterministic_repeat():
@@ -87,13 +88,14 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
 @pytest.mark.parametrize("R,g,V,r,d,mode", EDGE)
-def test_edge_shapes(R, g, V, r, d, mode):
-    _say(f"case edge R={R} g={g} V={V} r={r} d={d} mode={mode}")
+def test_edge_shapes(R, g, V, r, d, mode, layout):
+    _say(f"case edge R={R} g={g} V={V} r={r} d={d} mode={mode} layout={layout}")
     cfg = Config("edge", R=R, gamma=g, V=V, r=r, d=d, mode=mode, temperature=0.9, w_std=0.2,
                  base_std=1.0, wconf_std=0.1, seed=100 + R)
     wl = make_workload(cfg)
-    _full_path_check(wl)
+    _full_path_check(wl, layout=layout)
 
 
 def test_unaligned_base_uses_scalar_path():
@@ -185,16 +187,18 @@ def _sample_rows(R, n, seed):
     return np.unique(np.concatenate([[0, R - 1], rng.choice(R, size=min(n, R), replace=False)]))
 
 
-def test_qwen3_8b_full():
-    _say("case qwen3_8b (R=64, V=151936, r=256)")
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
+def test_qwen3_8b_full(layout):
+    _say(f"case qwen3_8b (R=64, V=151936, r=256) layout={layout}")
     wl = make_workload(CONFIGS["qwen3_8b"])
-    _full_path_check(wl)
+    _full_path_check(wl, layout=layout)
 
 
-def test_dsv4_full():
-    _say("case dsv4 (R=256, V=129280, r=512, sampling)")
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
+def test_dsv4_full(layout):
+    _say(f"case dsv4 (R=256, V=129280, r=512, sampling) layout={layout}")
     wl = make_workload(CONFIGS["dsv4"])
-    _full_path_check(wl, rows=_sample_rows(256, 24, 1))
+    _full_path_check(wl, rows=_sample_rows(256, 24, 1), layout=layout)
 
 
 def test_long_block_full():
