@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
     const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
-    int n_rblocks, int n_vgroups, int cpg, int n_chunks, Addr ad,
+    int n_rblocks, int n_vgroups, int cpg, int cstep, int n_chunks, Addr ad,
     float2* __restrict__ partials, float* __restrict__ bias_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int KS = RK / 16;
@@ -221,9 +221,13 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   const int rb = q % n_rblocks;
   const int vg = (q / n_rblocks) * 8 + (id & 7);
   if (vg >= n_vgroups) return;
-  const int c_begin = vg * cpg;
-  const int c_end = min(c_begin + cpg, n_chunks);      // cpg is a multiple of UNR
-  const int c_last = c_end - 1;                        // prefetches stay in the group
+  // Iteration i (0 <= i < cpg, a multiple of UNR) handles chunk c0 + i * cstep:
+  // contiguous groups (cstep 1) or groups strided across V (cstep = number of
+  // groups).  Iterations past the group's n_valid chunks are masked, and
+  // prefetches are clamped to the group's last chunk.
+  const int c0 = cstep == 1 ? vg * cpg : vg;
+  const int n_valid = cstep == 1 ? min(cpg, n_chunks - c0) : (n_chunks - 1 - vg) / cstep + 1;
+  auto chunk = [&](int i) { return c0 + min(i, n_valid - 1) * cstep; };
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
   const int m_loc = wave * 32 + col;
@@ -251,13 +255,13 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   float best = -INFINITY;
   int best_i = 0x7fffffff;
 
-  auto body = [&](int c, u32x4 (&st)[PMAX], float (&cb)[16], float (&cu)[16], float (&pb)[16],
+  auto body = [&](int i, u32x4 (&st)[PMAX], float (&cb)[16], float (&cu)[16], float (&pb)[16],
                   float (&pu)[16]) {
-    const int b = (c - c_begin) & 1;
+    const int b = i & 1;
     w2_store<RK, NT, PMAX>(lds + b * BUF, st, tid);
     lds_barrier();
-    w2_load<RK, NT, PMAX>(st, rw2, w2_off, min(c + WD, c_last), r);
-    epi_load<MODE, VEC4, 4>(pb, pu, rbase, runif, e_off + (uint32_t)min(c + PD, c_last) * e_cb);
+    w2_load<RK, NT, PMAX>(st, rw2, w2_off, chunk(i + WD), r);
+    epi_load<MODE, VEC4, 4>(pb, pu, rbase, runif, e_off + (uint32_t)chunk(i + PD) * e_cb);
     __builtin_amdgcn_sched_barrier(0);   // issue the prefetches before the MFMAs
 
     // Bias tile: 32 vocabulary rows x 32 requests over the compiled K = RK
@@ -276,8 +280,8 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
 
     // Fused bias-add + select; chunks are walked in increasing v, so a strict
     // comparison keeps the smallest id among equal maxima within a lane.
-    const int vl = c * kChunk + 4 * half;
-    const int vlim = (c < c_end && m_ok) ? V : 0;
+    const int vl = (c0 + i * cstep) * kChunk + 4 * half;
+    const int vlim = (i < n_valid && m_ok) ? V : 0;
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) {
       const int vi = vl + 8 * (qq >> 2) + (qq & 3);
@@ -289,11 +293,11 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
     }
     if (BIAS) {
       float* oc = bias_out + ad.k_off + (size_t)min(m, R - 1) * ad.row_stride +
-                  (size_t)min(c, n_chunks - 1) * ad.cstride;
+                  (size_t)chunk(i) * ad.cstride;
 #pragma unroll
       for (int qq = 0; qq < 16; ++qq) {
         const int o = 8 * (qq >> 2) + 4 * half + (qq & 3);
-        if (c * kChunk + o < vlim) oc[o] = acc[qq];
+        if (vl - 4 * half + o < vlim) oc[o] = acc[qq];
       }
     }
     // Keep each chunk's arithmetic in its own iteration: hoisting the noise of
@@ -305,23 +309,22 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   // waits at the top of the loop can count them from the back.
 #pragma unroll
   for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
-    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, min(c_begin + t, c_last), r);
-    if (t < PD)
-      epi_load<MODE, VEC4, 4>(eb[t], eu[t], rbase, runif,
-                              e_off + (uint32_t)min(c_begin + t, c_last) * e_cb);
+    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, chunk(t), r);
+    if (t < PD) epi_load<MODE, VEC4, 4>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int c0 = c_begin; c0 < c_begin + cpg; c0 += UNR) {
+  for (int i0 = 0; i0 < cpg; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(c0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
+      body(i0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
   }
 
   // Lanes l and l^32 hold the same request: merge, then one lane writes the partial.
   const float ov = __shfl_xor(best, 32);
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
-  if (m_ok && half == 0) partials[(size_t)vg * R + m] = make_float2(best, __int_as_float(best_i));
+  if (m_ok && half == 0)
+    partials[(size_t)m * n_vgroups + vg] = make_float2(best, __int_as_float(best_i));
 }
 
 // ---------------------------------------------------------------------------
@@ -329,11 +332,11 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
 // After its MFMAs each wave hands the half-tile it does not finish (groups
 // jq outside {2kh, 2kh+1}) to its partner through a double-buffered LDS slot;
 // the epilogue of chunk c-1 runs in iteration c beside the MFMAs of chunk c,
-// so one barrier per chunk orders everything.  Each wave writes its own
-// partial per request and V group (two partials per group).
+// so one barrier per chunk orders everything.  At the end the pair merges its
+// halves through LDS and writes one partial per request and V group.
 // ---------------------------------------------------------------------------
 constexpr int kSplitWD = 2;
-constexpr int kSplitPD = 2;
+constexpr int kSplitPD = 1;
 constexpr int kSplitUnroll = lcm_small(kSplitWD, kSplitPD + 1);
 
 template <int NP>
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
     const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
-    int n_rblocks, int n_vgroups, int cpg, int n_chunks, Addr ad,
+    int n_rblocks, int n_vgroups, int cpg, int cstep, int n_chunks, Addr ad,
     float2* __restrict__ partials, float* __restrict__ bias_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int RK = 512;
@@ -375,9 +378,9 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   const int rb = q % n_rblocks;
   const int vg = (q / n_rblocks) * 8 + (id & 7);
   if (vg >= n_vgroups) return;
-  const int c_begin = vg * cpg;
-  const int c_end = min(c_begin + cpg, n_chunks);
-  const int c_last = c_end - 1;
+  const int c0 = cstep == 1 ? vg * cpg : vg;
+  const int n_valid = cstep == 1 ? min(cpg, n_chunks - c0) : (n_chunks - 1 - vg) / cstep + 1;
+  auto chunk = [&](int i) { return c0 + min(i, n_valid - 1) * cstep; };
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
   float* xbuf = reinterpret_cast<float*>(smem + (size_t)2 * BUF * 2);   // [2][NW][64][8]
 
@@ -410,14 +413,14 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   float best = -INFINITY;
   int best_i = 0x7fffffff;
 
-  // Epilogue of chunk c: own half-tile + partner's from xbuf slot xs.
-  auto epilogue = [&](int c, int xs, const float (&cb)[8], const float (&cu)[8]) {
+  // Epilogue of iteration i: own half-tile + partner's from xbuf slot xs.
+  auto epilogue = [&](int i, int xs, const float (&cb)[8], const float (&cu)[8]) {
     const float* px = xbuf + (((size_t)xs * NW + (wave ^ 1)) * 64 + lane) * 8;
     const float4 p0 = *reinterpret_cast<const float4*>(px);
     const float4 p1 = *reinterpret_cast<const float4*>(px + 4);
     const float part[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    const int vl = c * kChunk + 16 * kh + 4 * half;
-    const int vlim = (c < c_end && m_ok) ? V : 0;
+    const int vl = (c0 + i * cstep) * kChunk + 16 * kh + 4 * half;
+    const int vlim = (i < n_valid && m_ok) ? V : 0;
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) {
       const int vi = vl + 8 * (qq >> 2) + (qq & 3);
@@ -429,21 +432,20 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     }
     if (BIAS) {
       float* oc = bias_out + ad.k_off + (size_t)min(m, R - 1) * ad.row_stride +
-                  (size_t)min(c, n_chunks - 1) * ad.cstride;
+                  (size_t)chunk(i) * ad.cstride;
 #pragma unroll
       for (int qq = 0; qq < 8; ++qq) {
         const int o = 16 * kh + 8 * (qq >> 2) + 4 * half + (qq & 3);
-        if (c * kChunk + o < vlim) oc[o] = part[qq] + own[qq];
+        if (vl - 16 * kh - 4 * half + o < vlim) oc[o] = part[qq] + own[qq];
       }
     }
   };
 
-  auto body = [&](int c, u32x4 (&st)[PMAX], float (&pb)[8], float (&pu)[8], float (&nb)[8],
+  auto body = [&](int t, u32x4 (&st)[PMAX], float (&pb)[8], float (&pu)[8], float (&nb)[8],
                   float (&nu)[8]) {
-    const int t = c - c_begin;
     w2_store<RK, NT, PMAX>(lds + (t & 1) * BUF, st, tid);
     lds_barrier();
-    w2_load<RK, NT, PMAX>(st, rw2, w2_off, min(c + WD, c_last), r);
+    w2_load<RK, NT, PMAX>(st, rw2, w2_off, chunk(t + WD), r);
     __builtin_amdgcn_sched_barrier(0);
 
     const uint16_t* abase = lds + (t & 1) * BUF + col * PITCH + half * 8 + kh * KH * 16;
@@ -460,7 +462,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     // Epilogue of the previous chunk (its partner half was written before this
     // iteration's barrier).  At t = 0 there is none (a uniform branch with no
     // memory loads).
-    if (t >= 1) epilogue(c - 1, (t - 1) & 1, pb, pu);
+    if (t >= 1) epilogue(t - 1, (t - 1) & 1, pb, pu);
     // Hand the other half-tile to the partner; keep ours for the next iteration.
     const int oj = 2 * (kh ^ 1);
     float* px = xbuf + (((size_t)(t & 1) * NW + wave) * 64 + lane) * 8;
@@ -471,40 +473,46 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     const int mj = 2 * kh;
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) own[qq] = acc[4 * mj + qq];
-    // The slot of chunk c-1 is free now: refill it with chunk c + PD.
-    epi_load<MODE, VEC4, 2>(nb, nu, rbase, runif, e_off + (uint32_t)min(c + PD, c_last) * e_cb);
+    // The slot of iteration t-1 is free now: refill it with iteration t + PD.
+    epi_load<MODE, VEC4, 2>(nb, nu, rbase, runif, e_off + (uint32_t)chunk(t + PD) * e_cb);
     __builtin_amdgcn_sched_barrier(0);
   };
 
 #pragma unroll
   for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
-    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, min(c_begin + t, c_last), r);
-    if (t < PD)
-      epi_load<MODE, VEC4, 2>(eb[t], eu[t], rbase, runif,
-                              e_off + (uint32_t)min(c_begin + t, c_last) * e_cb);
+    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, chunk(t), r);
+    if (t < PD) epi_load<MODE, VEC4, 2>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Chunk c's epilogue inputs live in slot (c - c_begin) % NS; iteration c
-  // finishes chunk c-1 and refills that slot with chunk c + PD.
-  for (int c0 = c_begin; c0 < c_begin + cpg; c0 += UNR) {
+  // Iteration t's epilogue inputs live in slot t % NS; iteration t finishes
+  // iteration t-1 and refills that slot with iteration t + PD.
+  for (int i0 = 0; i0 < cpg; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(c0 + j, stage[j % WD], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS],
+      body(i0 + j, stage[j % WD], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS],
            eb[(j + PD) % NS], eu[(j + PD) % NS]);
   }
   lds_barrier();   // the partner's last half-tile
-  // cpg is a multiple of UNR (hence of NS): the last chunk's slot is NS - 1.
-  epilogue(c_begin + cpg - 1, (cpg - 1) & 1, eb[NS - 1], eu[NS - 1]);
+  // cpg is a multiple of UNR (hence of NS): the last iteration's slot is NS - 1.
+  epilogue(cpg - 1, (cpg - 1) & 1, eb[NS - 1], eu[NS - 1]);
 
   const float ov = __shfl_xor(best, 32);
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
-  if (m_ok && half == 0)
-    partials[((size_t)vg * 2 + kh) * R + m] = make_float2(best, __int_as_float(best_i));
+  // Merge the pair's two halves through LDS (the W2 staging area is free: every
+  // wave finished its MFMAs before the barrier above), one partial per group.
+  float2* xch = reinterpret_cast<float2*>(smem);
+  if (kh == 1 && half == 0) xch[pair * 32 + col] = make_float2(best, __int_as_float(best_i));
+  lds_barrier();
+  if (kh == 0 && half == 0 && m_ok) {
+    const float2 o = xch[pair * 32 + col];
+    merge_best(best, best_i, o.x, __float_as_int(o.y));
+    partials[(size_t)m * n_vgroups + vg] = make_float2(best, __int_as_float(best_i));
+  }
 }
 
-// Reduce the per-group partials [group][request] to x_k: one wave per request,
-// lanes stride over the groups (independent loads), then a fixed shuffle tree.
+// Reduce the per-group partials [request][group] to x_k: one wave per request,
+// lanes read consecutive groups (coalesced), then a fixed shuffle tree.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __restrict__ partials,
                                                             int R, int n_groups, int V,
                                                             int gamma, int k,
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __rest
   int best_i = 0x7fffffff;
 #pragma unroll 4
   for (int g = lane; g < n_groups; g += 64) {
-    const float2 p = partials[(size_t)g * R + m];
+    const float2 p = partials[(size_t)m * n_groups + g];
     merge_best(best, best_i, p.x, __float_as_int(p.y));
   }
 #pragma unroll
@@ -531,27 +539,26 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __rest
 // ---- host side: kernel variants ----
 
 using StepKernel = void (*)(const uint16_t*, const uint16_t*, const float*, const float*,
-                            const int32_t*, int, int, int, int, float, int, int, int, int, Addr,
-                            float2*, float*);
+                            const int32_t*, int, int, int, int, float, int, int, int, int, int,
+                            Addr, float2*, float*);
 
 struct StepVariant {
   StepKernel fn;
   int threads;
   size_t lds;
   int rows;     // requests per workgroup
-  int split;    // partials per (request, V group)
   int unroll;   // chunks per group must be a multiple of this
 };
 
 template <int RK, int NW, int MODE, bool VEC4, bool BIAS>
 StepVariant plain_variant() {
   return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS>, NW * 64,
-          (size_t)2 * kChunk * (RK + 8) * 2, NW * 32, 1, plain_unroll<RK, NW>()};
+          (size_t)2 * kChunk * (RK + 8) * 2, NW * 32, plain_unroll<RK, NW>()};
 }
 template <int NP, int MODE, bool VEC4, bool BIAS>
 StepVariant ksplit_variant() {
   return {&markov_step_ksplit_kernel<NP, MODE, VEC4, BIAS>, NP * 128, ksplit_lds_bytes<NP>(),
-          NP * 32, 2, kSplitUnroll};
+          NP * 32, kSplitUnroll};
 }
 
 template <int RK, int MODE, bool VEC4, bool BIAS>
@@ -634,10 +641,9 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
   int nw = waves_needed >= 8 ? 8 : waves_needed >= 4 ? 4 : waves_needed >= 2 ? 2 : 1;
   // Choices measured on MI355X.  Rank 512 sampling: K-split wave pairs (a
   // plain wave would need the whole SIMD); rank 512 greedy: eight plain waves;
-  // up to 64 requests: one-wave workgroups (twice the workgroups, and the
-  // second R block's W2 reads hit L2).  DSPARK_MARKOV_KSPLIT / _NW / _WG
-  // override the choice for tuning.
-  if (waves_needed <= 2) nw = 1;
+  // up to 64 requests: two-wave workgroups, at most two per CU (fewer,
+  // longer groups).  DSPARK_MARKOV_KSPLIT / _NW / _WG / _STRIDED override the
+  // choice for tuning.
   if (p.rk == 512 && mode == DSPARK_SAMPLE && nw == 8) nw = 4;
   const int ks_env = env_int("DSPARK_MARKOV_KSPLIT", -1);
   p.ksplit = p.rk == 512 && (ks_env < 0 ? mode == DSPARK_SAMPLE : ks_env != 0);
@@ -649,7 +655,7 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
   p.n_rblocks = (R + rows - 1) / rows;
   p.n_chunks = (V + kChunk - 1) / kChunk;
   const int max_groups = p.n_chunks < kMaxGroups ? p.n_chunks : kMaxGroups;
-  p.ws_bytes = (size_t)R * (size_t)max_groups * 2 * sizeof(float2);
+  p.ws_bytes = (size_t)R * (size_t)max_groups * sizeof(float2);   // partials [R][groups]
   return p;
 }
 
@@ -673,7 +679,7 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   // a multiple of the kernel's unroll factor of chunks.
   const int max_groups = p.n_chunks < kMaxGroups ? p.n_chunks : kMaxGroups;
   int target = env_int("DSPARK_MARKOV_WG", 0);
-  if (target <= 0) target = device_cus() * bpc;
+  if (target <= 0) target = device_cus() * (p.n_rblocks == 1 && R <= 64 && bpc > 2 ? 2 : bpc);
   if (target < 8) target = 8;
   int groups = (target + p.n_rblocks - 1) / p.n_rblocks;
   groups = (groups + 7) / 8 * 8;
@@ -681,7 +687,15 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   if (groups < 1) groups = 1;
   p.cpg = (p.n_chunks + groups - 1) / groups;
   p.cpg = (p.cpg + var.unroll - 1) / var.unroll * var.unroll;
-  p.n_vgroups = (p.n_chunks + p.cpg - 1) / p.cpg;
+  // Contiguous groups: group g owns chunks [g*cpg, (g+1)*cpg).  Strided groups:
+  // group g owns chunks g, g + G, g + 2G, ... (all G groups in flight read one
+  // contiguous window of W2 and of the logits at a time).
+  // Strided groups measured faster for the tiled layout at R >= 128 (sampling
+  // and long blocks); row-major rows are far apart whichever way V is split.
+  const int st_env = env_int("DSPARK_MARKOV_STRIDED", -1);
+  const bool strided = st_env < 0 ? (tiled && R >= 128) : st_env != 0;
+  p.n_vgroups = strided ? groups : (p.n_chunks + p.cpg - 1) / p.cpg;
+  const int cstep = strided ? groups : 1;
 
   float2* partials = reinterpret_cast<float2*>(workspace);
   const int padded_groups = (p.n_vgroups + 7) / 8 * 8;
@@ -700,7 +714,7 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
         return fail(DSPARK_EDEVICE, "hipEventRecord failed");
     }
     hipLaunchKernelGGL(var.fn, grid, dim3(var.threads), var.lds, stream, W1, W2, base, uniforms,
-                       prev, prev_stride, R, V, r, inv_t, p.n_rblocks, p.n_vgroups, p.cpg,
+                       prev, prev_stride, R, V, r, inv_t, p.n_rblocks, p.n_vgroups, p.cpg, cstep,
                        p.n_chunks, ad, partials, bias_out);
     dspark_status st = check_launch("markov_step_kernel");
     if (st != DSPARK_OK) return st;
@@ -709,7 +723,7 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
         return fail(DSPARK_EDEVICE, "hipEventRecord failed");
     }
     hipLaunchKernelGGL(argmax_reduce_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, partials,
-                       R, p.n_vgroups * var.split, V, gamma, k, tokens);
+                       R, p.n_vgroups, V, gamma, k, tokens);
     st = check_launch("argmax_reduce_kernel");
     if (st != DSPARK_OK) return st;
   }
