@@ -38,6 +38,8 @@
 //     of chunk c).
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "dspark_internal.h"
 
 namespace dspark {
@@ -71,17 +73,48 @@ __device__ __forceinline__ void merge_best(float& bv, int& bi, float ov, int oi)
   }
 }
 
-// Selection score.  Sampling: z/T - ln(-ln u) with the hardware base-2
-// logarithm (relative error ~1e-7 over the whole open unit interval).
+// Selection score of z = b + a.  Sampling compares the Gumbel-max score in
+// base 2: (z/T - ln(-ln u)) / ln 2 = z * log2(e)/T - log2(-log2 u) + const, the
+// same argmax, with two hardware base-2 logarithms (relative error ~1e-7 over
+// the open unit interval) and one fma.  `kscale` is log2(e)/T.
 template <int MODE>
-__device__ __forceinline__ float select_score(float b, float a, float u, float inv_t) {
-  const float z = b + a;
+__device__ __forceinline__ float select_score(float b, float a, float u, float kscale) {
   if (MODE == DSPARK_SAMPLE) {
-    constexpr float kLn2 = 0.693147180559945309f;
-    const float w = -kLn2 * __builtin_amdgcn_logf(u);        // -ln u  (> 0)
-    return fmaf(-kLn2, __builtin_amdgcn_logf(w), z * inv_t);
+    const float g = __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+    return fmaf(b + a, kscale, -g);
   }
-  return z;
+  return b + a;
+}
+
+// Running argmax over one lane's N accumulator elements of a chunk; element q
+// is vocabulary entry vl + 8 * (q / 4) + (q % 4).  Chunks arrive in increasing
+// v, so a strict comparison keeps the smallest id among equal maxima.  Only a
+// chunk that crosses V (or a padding iteration, vlim = 0) needs the mask; the
+// test is uniform and the branch holds no loads.
+template <int MODE, int N>
+__device__ __forceinline__ void select_chunk(float& best, int& best_i, const float* cb,
+                                             const float* acc, const float* cu, float kscale,
+                                             int vl, bool whole, int vlim) {
+  if (whole) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const float sc = select_score<MODE>(cb[q], acc[q], cu[q], kscale);
+      if (sc > best) {
+        best = sc;
+        best_i = vl + 8 * (q >> 2) + (q & 3);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const int vi = vl + 8 * (q >> 2) + (q & 3);
+      const float sc = select_score<MODE>(cb[q], acc[q], cu[q], kscale);
+      if (vi < vlim && sc > best) {
+        best = sc;
+        best_i = vi;
+      }
+    }
+  }
 }
 
 // ---- raw buffer access ----
@@ -215,6 +248,7 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
+  const float kscale = inv_t * 1.44269504088896341f;   // log2(e) / T
 
   const int id = blockIdx.x;
   const int q = id >> 3;
@@ -278,26 +312,21 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], e[s0 + i], acc, 0, 0, 0);
     }
 
-    // Fused bias-add + select; chunks are walked in increasing v, so a strict
-    // comparison keeps the smallest id among equal maxima within a lane.
-    const int vl = (c0 + i * cstep) * kChunk + 4 * half;
-    const int vlim = (i < n_valid && m_ok) ? V : 0;
+    // Fused bias-add + select.  Rows past R are never written, so they need
+    // no mask.
+    const int cv = (c0 + i * cstep) * kChunk;
+    const int vlim = i < n_valid ? V : 0;
+    float av[16];
 #pragma unroll
-    for (int qq = 0; qq < 16; ++qq) {
-      const int vi = vl + 8 * (qq >> 2) + (qq & 3);
-      const float sc = select_score<MODE>(cb[qq], acc[qq], cu[qq], inv_t);
-      if (vi < vlim && sc > best) {
-        best = sc;
-        best_i = vi;
-      }
-    }
-    if (BIAS) {
-      float* oc = bias_out + ad.k_off + (size_t)min(m, R - 1) * ad.row_stride +
-                  (size_t)chunk(i) * ad.cstride;
+    for (int qq = 0; qq < 16; ++qq) av[qq] = acc[qq];
+    select_chunk<MODE, 16>(best, best_i, cb, av, cu, kscale, cv + 4 * half,
+                           i < n_valid && cv + kChunk <= V, vlim);
+    if (BIAS && m_ok) {
+      float* oc = bias_out + ad.k_off + (size_t)m * ad.row_stride + (size_t)chunk(i) * ad.cstride;
 #pragma unroll
       for (int qq = 0; qq < 16; ++qq) {
         const int o = 8 * (qq >> 2) + 4 * half + (qq & 3);
-        if (vl - 4 * half + o < vlim) oc[o] = acc[qq];
+        if (cv + o < vlim) oc[o] = acc[qq];
       }
     }
     // Keep each chunk's arithmetic in its own iteration: hoisting the noise of
@@ -370,6 +399,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
+  const float kscale = inv_t * 1.44269504088896341f;   // log2(e) / T
   const int pair = wave >> 1;
   const int kh = wave & 1;
 
@@ -419,24 +449,19 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     const float4 p0 = *reinterpret_cast<const float4*>(px);
     const float4 p1 = *reinterpret_cast<const float4*>(px + 4);
     const float part[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    const int vl = (c0 + i * cstep) * kChunk + 16 * kh + 4 * half;
-    const int vlim = (i < n_valid && m_ok) ? V : 0;
+    const int cv = (c0 + i * cstep) * kChunk;
+    const int vlim = i < n_valid ? V : 0;
+    float z[8];
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) {
-      const int vi = vl + 8 * (qq >> 2) + (qq & 3);
-      const float sc = select_score<MODE>(cb[qq], part[qq] + own[qq], cu[qq], inv_t);
-      if (vi < vlim && sc > best) {
-        best = sc;
-        best_i = vi;
-      }
-    }
-    if (BIAS) {
-      float* oc = bias_out + ad.k_off + (size_t)min(m, R - 1) * ad.row_stride +
-                  (size_t)chunk(i) * ad.cstride;
+    for (int qq = 0; qq < 8; ++qq) z[qq] = part[qq] + own[qq];
+    select_chunk<MODE, 8>(best, best_i, cb, z, cu, kscale, cv + 16 * kh + 4 * half,
+                          i < n_valid && cv + kChunk <= V, vlim);
+    if (BIAS && m_ok) {
+      float* oc = bias_out + ad.k_off + (size_t)m * ad.row_stride + (size_t)chunk(i) * ad.cstride;
 #pragma unroll
       for (int qq = 0; qq < 8; ++qq) {
         const int o = 16 * kh + 8 * (qq >> 2) + 4 * half + (qq & 3);
-        if (vl - 16 * kh - 4 * half + o < vlim) oc[o] = part[qq] + own[qq];
+        if (cv + o < vlim) oc[o] = z[qq];
       }
     }
   };
@@ -448,7 +473,10 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     w2_load<RK, NT, PMAX>(st, rw2, w2_off, chunk(t + WD), r);
     __builtin_amdgcn_sched_barrier(0);
 
-    const uint16_t* abase = lds + (t & 1) * BUF + col * PITCH + half * 8 + kh * KH * 16;
+    // Wave kh reads the chunk's rows as col ^ 16*kh, so its own 16 rows always
+    // land in acc[0..7] and the partner's in acc[8..15] (constant indices).
+    const uint16_t* abase =
+        lds + (t & 1) * BUF + (col ^ (16 * kh)) * PITCH + half * 8 + kh * KH * 16;
     f32x16 acc = {};
 #pragma unroll
     for (int s0 = 0; s0 < KH; s0 += 4) {
@@ -464,15 +492,11 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     // memory loads).
     if (t >= 1) epilogue(t - 1, (t - 1) & 1, pb, pu);
     // Hand the other half-tile to the partner; keep ours for the next iteration.
-    const int oj = 2 * (kh ^ 1);
     float* px = xbuf + (((size_t)(t & 1) * NW + wave) * 64 + lane) * 8;
-    *reinterpret_cast<float4*>(px) =
-        make_float4(acc[4 * oj], acc[4 * oj + 1], acc[4 * oj + 2], acc[4 * oj + 3]);
-    *reinterpret_cast<float4*>(px + 4) =
-        make_float4(acc[4 * oj + 4], acc[4 * oj + 5], acc[4 * oj + 6], acc[4 * oj + 7]);
-    const int mj = 2 * kh;
+    *reinterpret_cast<float4*>(px) = make_float4(acc[8], acc[9], acc[10], acc[11]);
+    *reinterpret_cast<float4*>(px + 4) = make_float4(acc[12], acc[13], acc[14], acc[15]);
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) own[qq] = acc[4 * mj + qq];
+    for (int qq = 0; qq < 8; ++qq) own[qq] = acc[qq];
     // The slot of iteration t-1 is free now: refill it with iteration t + PD.
     epi_load<MODE, VEC4, 2>(nb, nu, rbase, runif, e_off + (uint32_t)chunk(t + PD) * e_cb);
     __builtin_amdgcn_sched_barrier(0);
@@ -709,19 +733,19 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
     const int32_t* prev = k == 0 ? anchors : tokens + (k - 1);
     const int prev_stride = k == 0 ? 1 : gamma;
     ad.k_off = tiled ? (size_t)k * p.n_chunks * R * kChunk : (size_t)k * V;
-    if (events && k < events->count && events->begin && events->begin[k]) {
-      if (hipEventRecord(reinterpret_cast<hipEvent_t>(events->begin[k]), stream) != hipSuccess)
-        return fail(DSPARK_EDEVICE, "hipEventRecord failed");
+    // Timing hooks ride on the dispatch itself (start / stop timestamps of the
+    // kernel's packet), so they add no marker packets between kernels.
+    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
+    if (events && k < events->count) {
+      if (events->begin) ev_begin = reinterpret_cast<hipEvent_t>(events->begin[k]);
+      if (events->end) ev_end = reinterpret_cast<hipEvent_t>(events->end[k]);
     }
-    hipLaunchKernelGGL(var.fn, grid, dim3(var.threads), var.lds, stream, W1, W2, base, uniforms,
-                       prev, prev_stride, R, V, r, inv_t, p.n_rblocks, p.n_vgroups, p.cpg, cstep,
-                       p.n_chunks, ad, partials, bias_out);
+    hipExtLaunchKernelGGL(var.fn, grid, dim3(var.threads), (uint32_t)var.lds, stream, ev_begin,
+                          ev_end, 0u, W1, W2, base, uniforms, prev, prev_stride, R, V, r, inv_t,
+                          p.n_rblocks, p.n_vgroups, p.cpg, cstep, p.n_chunks, ad, partials,
+                          bias_out);
     dspark_status st = check_launch("markov_step_kernel");
     if (st != DSPARK_OK) return st;
-    if (events && k < events->count && events->end && events->end[k]) {
-      if (hipEventRecord(reinterpret_cast<hipEvent_t>(events->end[k]), stream) != hipSuccess)
-        return fail(DSPARK_EDEVICE, "hipEventRecord failed");
-    }
     hipLaunchKernelGGL(argmax_reduce_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, partials,
                        R, p.n_vgroups, V, gamma, k, tokens);
     st = check_launch("argmax_reduce_kernel");

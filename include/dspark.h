@@ -79,10 +79,12 @@ typedef enum {
 #define DSPARK_MAX_RANK 512          /* r <= 512 and r % 16 == 0 */
 #define DSPARK_MAX_CANDIDATES (1 << 23) /* R * gamma, keeps the fixed-point tau sum exact */
 
-/* Optional per-step timing hooks for dspark_markov_draft.  When non-NULL, the
- * library records begin[k] on `stream` immediately before the fused step
- * kernel of position k+1 and end[k] immediately after it (k = 0..gamma-1).
- * Each entry is a hipEvent_t created by the caller; count must be >= gamma. */
+/* Optional per-step timing hooks for dspark_markov_draft.  When non-NULL,
+ * begin[k] and end[k] (k = 0..gamma-1) receive the start and stop time of the
+ * fused step kernel of position k+1: they are attached to that kernel's
+ * dispatch (hipExtLaunchKernel), so hipEventElapsedTime(begin[k], end[k]) is
+ * the kernel's own duration.  Each entry is a hipEvent_t created by the caller
+ * (NULL entries are skipped); count must be >= gamma. */
 typedef struct {
   void* const* begin;
   void* const* end;

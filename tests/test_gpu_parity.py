@@ -213,3 +213,24 @@ def test_long_block_full():
     H.check_confidence(wl, toks, conf, surv)
     lengths, order, info = H.run_schedule(torch.from_numpy(surv).to(DEV), g["sps"])
     H.check_schedule(surv, wl["sps"], lengths, order, info)
+
+
+def test_step_events_time_each_fused_launch():
+    _say("case step events")
+    wl = make_workload(CONFIGS["tiny"], w_std=0.3)
+    g = H.to_device(wl, DEV)
+    ref, _ = H.run_draft(wl, g)
+    gm = wl["base"].shape[1]
+    begins = [torch.cuda.Event(enable_timing=True) for _ in range(gm)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(gm)]
+    for e in begins + ends:
+        e.record()   # materialise the hipEvent_t handles
+    torch.cuda.synchronize()
+    tok = D.dspark_markov_draft(g["W1"], g["W2"], g["base"], g["anchors"], wl["mode"],
+                                wl["temperature"], None,
+                                events=([e.cuda_event for e in begins], [e.cuda_event for e in ends]))
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), ref)
+    for b, e in zip(begins, ends):
+        ms = b.elapsed_time(e)
+        assert 0.0 < ms < 100.0
