@@ -38,6 +38,8 @@
 //     of chunk c).
 #include <math.h>
 
+#include <type_traits>
+
 #include <hip/hip_ext.h>
 
 #include "dspark_internal.h"
@@ -86,35 +88,40 @@ __device__ __forceinline__ float select_score(float b, float a, float u, float k
   return b + a;
 }
 
-// Running argmax over one lane's N accumulator elements of a chunk; element q
-// is vocabulary entry vl + 8 * (q / 4) + (q % 4).  Chunks arrive in increasing
-// v, so a strict comparison keeps the smallest id among equal maxima.  Only a
-// chunk that crosses V (or a padding iteration, vlim = 0) needs the mask; the
-// test is uniform and the branch holds no loads.
-template <int MODE, int N>
-__device__ __forceinline__ void select_chunk(float& best, int& best_i, const float* cb,
-                                             const float* acc, const float* cu, float kscale,
-                                             int vl, bool whole, int vlim) {
-  if (whole) {
+// Running argmax of one lane.  Element q of a chunk is vocabulary entry
+// (chunk)*32 + lane offset + 8*(q/4) + (q%4).  Per element only the score and
+// q are kept (q is an inline constant); the iteration whose chunk raised the
+// maximum is recorded once per chunk and the id is rebuilt at the end.  Chunks
+// arrive in increasing v and q runs in increasing v within a chunk, so a
+// strict comparison keeps the smallest id among equal maxima.
+struct Argmax {
+  float best = -INFINITY;
+  int q = 0;
+  int iter = -1;
+};
+
+template <int MODE, int N, bool MASKED>
+__device__ __forceinline__ void select_chunk(Argmax& am, const float* cb, const float* z,
+                                             const float* cu, float kscale, int iter, int lim) {
+  const float before = am.best;
 #pragma unroll
-    for (int q = 0; q < N; ++q) {
-      const float sc = select_score<MODE>(cb[q], acc[q], cu[q], kscale);
-      if (sc > best) {
-        best = sc;
-        best_i = vl + 8 * (q >> 2) + (q & 3);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < N; ++q) {
-      const int vi = vl + 8 * (q >> 2) + (q & 3);
-      const float sc = select_score<MODE>(cb[q], acc[q], cu[q], kscale);
-      if (vi < vlim && sc > best) {
-        best = sc;
-        best_i = vi;
-      }
+  for (int q = 0; q < N; ++q) {
+    const float sc = select_score<MODE>(cb[q], z[q], cu[q], kscale);
+    // MASKED: only elements with in-chunk offset below lim are valid (the chunk
+    // that crosses V, padding iterations with lim <= 0).
+    const bool take = MASKED ? (sc > am.best && 8 * (q >> 2) + (q & 3) < lim) : sc > am.best;
+    if (take) {
+      am.best = sc;
+      am.q = q;
     }
   }
+  if (am.best != before) am.iter = iter;
+}
+
+// Vocabulary id of an Argmax (0x7fffffff if nothing was taken).
+__device__ __forceinline__ int argmax_id(const Argmax& am, int c0, int cstep, int lane_off) {
+  return am.iter < 0 ? 0x7fffffff
+                     : (c0 + am.iter * cstep) * kChunk + lane_off + 8 * (am.q >> 2) + (am.q & 3);
 }
 
 // ---- raw buffer access ----
@@ -212,6 +219,13 @@ __device__ __forceinline__ void epi_load(float (&bv)[4 * NJ], float (&uv)[4 * NJ
 
 constexpr int lcm_small(int a, int b) { return (a % b == 0) ? a : (b % a == 0) ? b : a * b; }
 
+// Number of leading iterations of a group whose chunks lie wholly inside V: all
+// n_valid, unless the group's last chunk is the one that crosses V.
+__device__ __forceinline__ int n_whole(int c0, int cstep, int n_valid, int V) {
+  const int last = c0 + (n_valid - 1) * cstep;
+  return (last + 1) * kChunk <= V ? n_valid : n_valid - 1;
+}
+
 // ---------------------------------------------------------------------------
 // Plain kernel: a wave owns 32 requests over the full K.
 // ---------------------------------------------------------------------------
@@ -286,11 +300,11 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   u32x4 stage[WD][PMAX];
   float eb[NS][16];
   float eu[NS][16];
-  float best = -INFINITY;
-  int best_i = 0x7fffffff;
+  Argmax am;
 
-  auto body = [&](int i, u32x4 (&st)[PMAX], float (&cb)[16], float (&cu)[16], float (&pb)[16],
-                  float (&pu)[16]) {
+  auto body = [&](auto masked, int i, u32x4 (&st)[PMAX], float (&cb)[16], float (&cu)[16],
+                  float (&pb)[16], float (&pu)[16]) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int b = i & 1;
     w2_store<RK, NT, PMAX>(lds + b * BUF, st, tid);
     lds_barrier();
@@ -319,8 +333,7 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
     float av[16];
 #pragma unroll
     for (int qq = 0; qq < 16; ++qq) av[qq] = acc[qq];
-    select_chunk<MODE, 16>(best, best_i, cb, av, cu, kscale, cv + 4 * half,
-                           i < n_valid && cv + kChunk <= V, vlim);
+    select_chunk<MODE, 16, MASKED>(am, cb, av, cu, kscale, i, vlim - cv - 4 * half);
     if (BIAS && m_ok) {
       float* oc = bias_out + ad.k_off + (size_t)m * ad.row_stride + (size_t)chunk(i) * ad.cstride;
 #pragma unroll
@@ -342,13 +355,26 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
     if (t < PD) epi_load<MODE, VEC4, 4>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int i0 = 0; i0 < cpg; i0 += UNR) {
+  // Iterations [0, n_main) hold chunks wholly inside V and run unmasked; the
+  // rest (the chunk that crosses V, padding) take the masked select.
+  const int n_main = n_whole(c0, cstep, n_valid, V) / UNR * UNR;
+  int i0 = 0;
+  for (; i0 < n_main; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(i0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
+      body(std::false_type{}, i0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS],
+           eu[(j + PD) % NS]);
+  }
+  for (; i0 < cpg; i0 += UNR) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j)
+      body(std::true_type{}, i0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS],
+           eu[(j + PD) % NS]);
   }
 
   // Lanes l and l^32 hold the same request: merge, then one lane writes the partial.
+  float best = am.best;
+  int best_i = argmax_id(am, c0, cstep, 4 * half);
   const float ov = __shfl_xor(best, 32);
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
@@ -440,11 +466,11 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   float eb[NS][8];
   float eu[NS][8];
   float own[8];
-  float best = -INFINITY;
-  int best_i = 0x7fffffff;
+  Argmax am;
 
   // Epilogue of iteration i: own half-tile + partner's from xbuf slot xs.
-  auto epilogue = [&](int i, int xs, const float (&cb)[8], const float (&cu)[8]) {
+  auto epilogue = [&](auto masked, int i, int xs, const float (&cb)[8], const float (&cu)[8]) {
+    constexpr bool MASKED = decltype(masked)::value;
     const float* px = xbuf + (((size_t)xs * NW + (wave ^ 1)) * 64 + lane) * 8;
     const float4 p0 = *reinterpret_cast<const float4*>(px);
     const float4 p1 = *reinterpret_cast<const float4*>(px + 4);
@@ -454,8 +480,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     float z[8];
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) z[qq] = part[qq] + own[qq];
-    select_chunk<MODE, 8>(best, best_i, cb, z, cu, kscale, cv + 16 * kh + 4 * half,
-                          i < n_valid && cv + kChunk <= V, vlim);
+    select_chunk<MODE, 8, MASKED>(am, cb, z, cu, kscale, i, vlim - cv - 16 * kh - 4 * half);
     if (BIAS && m_ok) {
       float* oc = bias_out + ad.k_off + (size_t)m * ad.row_stride + (size_t)chunk(i) * ad.cstride;
 #pragma unroll
@@ -466,8 +491,8 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     }
   };
 
-  auto body = [&](int t, u32x4 (&st)[PMAX], float (&pb)[8], float (&pu)[8], float (&nb)[8],
-                  float (&nu)[8]) {
+  auto body = [&](auto masked, auto first, int t, u32x4 (&st)[PMAX], float (&pb)[8],
+                  float (&pu)[8], float (&nb)[8], float (&nu)[8]) {
     w2_store<RK, NT, PMAX>(lds + (t & 1) * BUF, st, tid);
     lds_barrier();
     w2_load<RK, NT, PMAX>(st, rw2, w2_off, chunk(t + WD), r);
@@ -490,7 +515,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     // Epilogue of the previous chunk (its partner half was written before this
     // iteration's barrier).  At t = 0 there is none (a uniform branch with no
     // memory loads).
-    if (t >= 1) epilogue(t - 1, (t - 1) & 1, pb, pu);
+    if (!decltype(first)::value || t >= 1) epilogue(masked, t - 1, (t - 1) & 1, pb, pu);
     // Hand the other half-tile to the partner; keep ours for the next iteration.
     float* px = xbuf + (((size_t)(t & 1) * NW + wave) * 64 + lane) * 8;
     *reinterpret_cast<float4*>(px) = make_float4(acc[8], acc[9], acc[10], acc[11]);
@@ -510,16 +535,33 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   }
   // Iteration t's epilogue inputs live in slot t % NS; iteration t finishes
   // iteration t-1 and refills that slot with iteration t + PD.
-  for (int i0 = 0; i0 < cpg; i0 += UNR) {
+  // The first UNR iterations (the first has no previous chunk) and those from
+  // n_main on run the masked select; in between every epilogue's chunk lies
+  // wholly inside V.
+  const int n_main = n_whole(c0, cstep, n_valid, V) / UNR * UNR;
+#pragma unroll
+  for (int j = 0; j < UNR; ++j)
+    body(std::true_type{}, std::true_type{}, j, stage[j % WD], eb[(j + NS - 1) % NS],
+         eu[(j + NS - 1) % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
+  int i0 = UNR;
+  for (; i0 < n_main; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(i0 + j, stage[j % WD], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS],
-           eb[(j + PD) % NS], eu[(j + PD) % NS]);
+      body(std::false_type{}, std::false_type{}, i0 + j, stage[j % WD], eb[(j + NS - 1) % NS],
+           eu[(j + NS - 1) % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
+  }
+  for (; i0 < cpg; i0 += UNR) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j)
+      body(std::true_type{}, std::false_type{}, i0 + j, stage[j % WD], eb[(j + NS - 1) % NS],
+           eu[(j + NS - 1) % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
   }
   lds_barrier();   // the partner's last half-tile
   // cpg is a multiple of UNR (hence of NS): the last iteration's slot is NS - 1.
-  epilogue(cpg - 1, (cpg - 1) & 1, eb[NS - 1], eu[NS - 1]);
+  epilogue(std::true_type{}, cpg - 1, (cpg - 1) & 1, eb[NS - 1], eu[NS - 1]);
 
+  float best = am.best;
+  int best_i = argmax_id(am, c0, cstep, 16 * kh + 4 * half);
   const float ov = __shfl_xor(best, 32);
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
