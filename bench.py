@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 METRIC = "draft tokens/s (Markov refine+confidence+schedule) at R=256,V=129280; % roofline"
 COUNTERS_FMT = os.path.join(ROOT, "profiles", "markov_step_{cfg}_{layout}_counters.txt")
 STEP_SRC = os.path.join(ROOT, "draft_head_step_amd", "csrc", "markov_step.hip")
@@ -99,6 +100,8 @@ def main():
                     help="storage order of base / uniforms handed to the draft")
     ap.add_argument("--no-row-major", action="store_true",
                     help="skip the secondary timing in the row-major layout")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the cold-cache, GEMM-only and row-major side measurements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
@@ -110,7 +113,7 @@ def main():
 
     import torch
     import draft_head_step_amd as D
-    from draft_head_step_amd.inputs import CONFIGS, make_workload, to_tiled
+    from draft_head_step_amd.inputs import CONFIGS, make_head, make_workload, to_tiled
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -154,7 +157,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def run(layout, steps, warmup):
-        """Time `steps` whole steps; return (ms per step, mean fused-step launch ms)."""
+        """Time `steps` whole steps; return (ms per step, fused-step launch durations in ms)."""
         base, unif = inputs(layout)
         lay = layouts[layout]
 
@@ -186,9 +189,67 @@ def main():
         t1 = time.perf_counter()
         durs = [begins[i][k].elapsed_time(ends[i][k]) for i in range(steps) for k in range(g)]
         del base, unif
-        return (t1 - t0) * 1e3 / steps, float(np.mean(durs))
+        return (t1 - t0) * 1e3 / steps, durs
 
-    ms_per_step, k_ms = run(args.layout, args.steps, args.warmup)
+    def cold_steps(layout, n):
+        """Per-step time with the caches flushed first (a 512 MB fill outside the
+        bracketed step): median over n steps, in ms."""
+        base, unif = inputs(layout)
+        lay = layouts[layout]
+        scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        times = []
+        for i in range(n + 1):
+            scratch.fill_(float(i))
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
+                                  tokens=tokens, workspace=ws_d, stream=stream, layout=lay)
+            D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv,
+                                stream=stream)
+            D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
+            e.record(stream)
+            torch.cuda.synchronize()
+            if i:
+                times.append(b.elapsed_time(e))
+        del base, unif, scratch
+        return float(np.median(times))
+
+    def gemm_only(name, steps=10):
+        """Greedy on the Markov bias alone (no logits stream): the gather + bias GEMM +
+        argmax, per fused launch, against the bf16 MFMA peak."""
+        c = CONFIGS[name]
+        hd = make_head(c)
+        gW1, gW2 = bf16(hd["W1"]), bf16(hd["W2"])
+        ganc = torch.from_numpy(hd["anchors"]).to(dev)
+        gR, gg, gV, gr = hd["R"], hd["gamma"], hd["V"], hd["r"]
+        gtok = torch.empty((gR, gg), dtype=torch.int32, device=dev)
+        gws = torch.empty(D.dspark_markov_draft_workspace(gR, gg, gV, gr), dtype=torch.uint8,
+                          device=dev)
+        for _ in range(2):
+            D.dspark_markov_draft(gW1, gW2, None, ganc, 0, gamma=gg, tokens=gtok, workspace=gws,
+                                  stream=stream)
+        torch.cuda.synchronize()
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(gg)] for _ in range(steps)]
+        eve = [[torch.cuda.Event(enable_timing=True) for _ in range(gg)] for _ in range(steps)]
+        for lst in evb + eve:
+            for e in lst:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            D.dspark_markov_draft(gW1, gW2, None, ganc, 0, gamma=gg, tokens=gtok, workspace=gws,
+                                  stream=stream,
+                                  events=([e.cuda_event for e in evb[i]], [e.cuda_event for e in eve[i]]))
+        torch.cuda.synchronize()
+        ms = float(np.mean([evb[i][k].elapsed_time(eve[i][k])
+                            for i in range(steps) for k in range(gg)]))
+        flops = 2.0 * gR * gr * gV
+        tf = flops / (ms / 1e3) / 1e12
+        del gW1, gW2, gws
+        return {"shape": f"{name}: R={gR}, r={gr}, V={gV}", "avg_launch_ms": round(ms, 5),
+                "tflops": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+    ms_per_step, durs = run(args.layout, args.steps, args.warmup)
+    k_ms = float(np.mean(durs))
     value = R * g / (ms_per_step / 1e3)
     nbytes = step_bytes(wl)
     achieved = nbytes / (k_ms / 1e3) / 1e9
@@ -216,11 +277,20 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(cfg.name, args.layout),
                      "kernel": kernel, "algorithmic_bytes_per_launch": nbytes,
-                     "avg_launch_ms": round(k_ms, 5), "launches_per_step": g},
+                     "avg_launch_ms": round(k_ms, 5), "launches_per_step": g,
+                     "launch_ms_p10_p50_p90": [round(float(x), 5)
+                                               for x in np.percentile(durs, [10, 50, 90])],
+                     "mfma_frac": round(2.0 * R * r * V / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
     }
-    if not args.no_row_major and args.layout != "rgv":
-        ms2, k2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1))
+    if not args.no_extras:
+        cold = cold_steps(args.layout, 10)
+        out["cold"] = {"ms_per_step_median": round(cold, 4), "value": round(R * g / (cold / 1e3), 1),
+                       "note": "512 MB cache flush before each step, outside its events"}
+        out["gemm_only"] = [gemm_only(args.config), gemm_only("long_block")]
+    if not args.no_row_major and not args.no_extras and args.layout != "rgv":
+        ms2, d2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1))
+        k2 = float(np.mean(d2))
         out["row_major"] = {"layout": "rgv", "ms_per_step": round(ms2, 4),
                             "value": round(R * g / (ms2 / 1e3), 1),
                             "avg_launch_ms": round(k2, 5),

@@ -138,27 +138,31 @@ def dspark_schedule_workspace(R: int, gamma: int) -> int:
 
 def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: float = 1.0,
                         uniforms=None, tokens=None, bias_out=None, workspace=None,
-                        events=None, stream=None, layout: int = LAYOUT_RGV):
+                        events=None, stream=None, layout: int = LAYOUT_RGV, gamma=None):
     """gamma-step Markov-head draft.  W1, W2 [V, r] bf16; anchors [R] int32; base (and
     uniforms, SAMPLE only; bias_out, optional) fp32 as [R, gamma, V] (LAYOUT_RGV) or
     [gamma, ceil(V/32), R, 32] (LAYOUT_TILED).  Returns tokens [R, gamma] int32.
+    ``base=None`` (GREEDY only, ``gamma`` given) drafts from the Markov bias alone.
 
-    ``events`` is an optional pair (begin, end) of sequences of hipEvent_t handles (ints),
-    recorded around each step's fused kernel."""
+    ``events`` is an optional pair (begin, end) of sequences of hipEvent_t handles (ints)
+    that receive the start and stop of each step's fused kernel."""
     torch = _torch()
     L = lib()
     V, r = W1.shape
     R = anchors.shape[0]
-    dev = base.device
+    dev = W1.device
+    if gamma is None:
+        if base is None:
+            raise ValueError("gamma must be given when base is None")
+        gamma = base.shape[0] if layout == LAYOUT_TILED else base.shape[1]
     if layout == LAYOUT_TILED:
-        gamma = base.shape[0]
         shape = (gamma, (V + 31) // 32, R, 32)
     else:
-        gamma = base.shape[1]
         shape = (R, gamma, V)
     _need(W1, "W1", _bf16_types(), (V, r), dev)
     _need(W2, "W2", _bf16_types(), (V, r), dev)
-    _need(base, "base", (torch.float32,), shape, dev)
+    if base is not None:
+        _need(base, "base", (torch.float32,), shape, dev)
     _need(anchors, "anchors", (torch.int32,), (R,), dev)
     if uniforms is not None:
         _need(uniforms, "uniforms", (torch.float32,), shape, dev)

@@ -60,8 +60,10 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
                                   size_t ws_bytes, const dspark_step_events* events,
                                   void* stream) {
   dspark::g_last_error[0] = 0;
-  if (!W1 || !W2 || !base || !anchors || !tokens)
+  if (!W1 || !W2 || !anchors || !tokens)
     return fail(DSPARK_EINVAL, "markov_draft: NULL required pointer");
+  if (!base && mode != DSPARK_GREEDY)
+    return fail(DSPARK_EINVAL, "markov_draft: base may be NULL only in GREEDY mode");
   if (R <= 0 || gamma <= 0 || r <= 0 || V < 2)
     return fail(DSPARK_EINVAL, "markov_draft: need R, gamma, r > 0 and V >= 2 (got %d %d %d %d)",
                 R, gamma, r, V);

@@ -53,6 +53,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 32;         // vocabulary rows of W2 per MFMA tile
 constexpr int kMaxGroups = 1024;   // upper bound on V groups (sizes the workspace)
+// Internal mode: greedy on the Markov bias alone (no base logits are read).
+constexpr int kBiasOnly = 2;
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -198,6 +200,11 @@ __device__ __forceinline__ void w2_store(uint16_t* dst, const u32x4 (&st)[PMAX],
 template <int MODE, bool VEC4, int NJ>
 __device__ __forceinline__ void epi_load(float (&bv)[4 * NJ], float (&uv)[4 * NJ], Rsrc rbase,
                                          Rsrc runif, uint32_t off) {
+  if (MODE == kBiasOnly) {
+#pragma unroll
+    for (int j = 0; j < 4 * NJ; ++j) bv[j] = 0.0f;
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     if (VEC4) {
@@ -292,8 +299,8 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
 
   const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
   const uint32_t w2_off = w2_lane_offset<RK, NT>(tid, r);
-  const Rsrc rbase = block_rsrc(base, ad, rb, ROWS);
-  const Rsrc runif = block_rsrc(MODE == DSPARK_SAMPLE ? unif : base, ad, rb, ROWS);
+  const Rsrc rbase = MODE == kBiasOnly ? make_rsrc(W2, 0u) : block_rsrc(base, ad, rb, ROWS);
+  const Rsrc runif = MODE == DSPARK_SAMPLE ? block_rsrc(unif, ad, rb, ROWS) : rbase;
   const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 4 * half) * 4u;
   const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
 
@@ -457,8 +464,8 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
 
   const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
   const uint32_t w2_off = w2_lane_offset<RK, NT>(tid, r);
-  const Rsrc rbase = block_rsrc(base, ad, rb, ROWS);
-  const Rsrc runif = block_rsrc(MODE == DSPARK_SAMPLE ? unif : base, ad, rb, ROWS);
+  const Rsrc rbase = MODE == kBiasOnly ? make_rsrc(W2, 0u) : block_rsrc(base, ad, rb, ROWS);
+  const Rsrc runif = MODE == DSPARK_SAMPLE ? block_rsrc(unif, ad, rb, ROWS) : rbase;
   const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 16 * kh + 4 * half) * 4u;
   const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
 
@@ -658,6 +665,8 @@ StepVariant pick2(const MarkovPlan& p, bool vec4, bool bias) {
   return bias ? pick3<MODE, false, true>(p) : pick3<MODE, false, false>(p);
 }
 StepVariant pick_variant(const MarkovPlan& p, int mode, bool vec4, bool bias) {
+  if (mode == kBiasOnly)   // no logits stream: the vector-width choice does not arise
+    return bias ? pick3<kBiasOnly, true, true>(p) : pick3<kBiasOnly, true, false>(p);
   return mode == DSPARK_SAMPLE ? pick2<DSPARK_SAMPLE>(p, vec4, bias)
                                : pick2<DSPARK_GREEDY>(p, vec4, bias);
 }
@@ -736,7 +745,9 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   const bool tiled = layout == DSPARK_LAYOUT_TILED;
   const bool vec4 = (tiled || V % 4 == 0) && V >= 4 && a16(base) &&
                     (!uniforms || a16(uniforms)) && (!bias_out || a16(bias_out));
-  const StepVariant var = pick_variant(p, mode, vec4, bias_out != nullptr);
+  // No base logits: greedy on the Markov bias alone.
+  const int kmode = base ? mode : kBiasOnly;
+  const StepVariant var = pick_variant(p, kmode, vec4, bias_out != nullptr);
   const int bpc = prepare_variant(var);
   if (bpc < 0) return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the Markov step kernel");
 

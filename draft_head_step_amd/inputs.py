@@ -241,3 +241,14 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, R: Optional[int] =
     out["sps"] = sps_table(cfg.sps_kind, b_max)
     out["B_max"] = b_max
     return out
+
+
+def make_head(cfg: Config, seed: Optional[int] = None, *, w_std: Optional[float] = None) -> dict:
+    """W1, W2 and anchors of ``cfg`` only: the same streams as make_workload, so the
+    arrays equal that workload's, without drawing the logits."""
+    seed = cfg.seed if seed is None else seed
+    ws = cfg.w_std if w_std is None else w_std
+    V, r = cfg.V, cfg.r
+    return {"W1": _normal_bf16(seed, "W1", (V, r), ws), "W2": _normal_bf16(seed, "W2", (V, r), ws),
+            "anchors": _gen(seed, "anchors").integers(0, V, size=(cfg.R,), dtype=np.int32),
+            "R": cfg.R, "gamma": cfg.gamma, "V": V, "r": r}

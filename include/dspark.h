@@ -120,7 +120,9 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *   layout    DSPARK_LAYOUT_RGV or DSPARK_LAYOUT_TILED: storage order of base,
  *             uniforms and bias_out (see dspark_layout).
  *   base      [R, gamma, V] fp32 backbone base logits (in `layout` order; the
- *             tiled order holds gamma * C * R * 32 floats).
+ *             tiled order holds gamma * C * R * 32 floats).  NULL in GREEDY mode
+ *             drafts from the Markov bias alone (base taken as zero; no logits
+ *             are read, so a call costs the gather + bias GEMM + argmax only).
  *   anchors   [R] int32     anchor token of each request (x_0), in [0, V).
  *   mode      DSPARK_GREEDY or DSPARK_SAMPLE.
  *   temperature  > 0 and finite when mode == DSPARK_SAMPLE; ignored for GREEDY.
@@ -131,9 +133,9 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *             Markov bias of every step (a debugging aid; NULL on the hot path).
  *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...).
  *   events    optional timing hooks (NULL on the hot path).
- * Errors: EINVAL for NULL required pointers, R/gamma/V/r <= 0, V < 2, a bad
- * layout or mode, a non-positive or non-finite temperature in SAMPLE mode, or uniforms
- * given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or r % 16 != 0, and
+ * Errors: EINVAL for NULL required pointers (base is optional only in GREEDY
+ * mode), R/gamma/V/r <= 0, V < 2, a bad layout or mode, a non-positive or
+ * non-finite temperature in SAMPLE mode, or uniforms given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or r % 16 != 0, and
  * where one step of one block of requests would not fit 32-bit byte offsets:
  * ceil(V/32)*32*r > 2^30, gamma*V >= 2^22 (DSPARK_LAYOUT_RGV) or
  * ceil(V/32)*R + 256 > 2^25 (DSPARK_LAYOUT_TILED); EWORKSPACE if the workspace

@@ -67,7 +67,7 @@ def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, layout=0, mode
 
 @no_gpu
 @pytest.mark.parametrize("kw,want", [
-    (dict(W1=None), EINVAL), (dict(W2=None), EINVAL), (dict(base=None), EINVAL),
+    (dict(W1=None), EINVAL), (dict(W2=None), EINVAL), (dict(base=None, mode=SAMPLE, u=P), EINVAL),
     (dict(anchors=None), EINVAL), (dict(tokens=None), EINVAL),
     (dict(R=0), EINVAL), (dict(g=-1), EINVAL), (dict(V=1), EINVAL), (dict(r=0), EINVAL),
     (dict(mode=2), EINVAL), (dict(layout=2), EINVAL), (dict(layout=-1), EINVAL),

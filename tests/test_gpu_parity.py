@@ -234,3 +234,32 @@ def test_step_events_time_each_fused_launch():
     for b, e in zip(begins, ends):
         ms = b.elapsed_time(e)
         assert 0.0 < ms < 100.0
+
+
+# --------------------------------------------------------------------------- bias only
+
+def _bias_only_case(wl, rows=None, bias=True):
+    """base = NULL (greedy on the Markov bias alone) against the oracle with base = 0."""
+    g = H.to_device(wl, DEV)
+    R, gm, V = wl["base"].shape
+    bias_out = torch.full((R, gm, V), float("nan"), dtype=torch.float32, device=DEV) if bias else None
+    tok = D.dspark_markov_draft(g["W1"], g["W2"], None, g["anchors"], GREEDY, gamma=gm,
+                                bias_out=bias_out)
+    torch.cuda.synchronize()
+    ref = dict(wl, base=np.zeros_like(wl["base"]), mode=GREEDY, uniforms=None)
+    H.check_draft(ref, tok.cpu().numpy(), rows, None if bias_out is None else bias_out.cpu().numpy())
+
+
+@pytest.mark.parametrize("R,g,V,r", [(4, 5, 4096, 64), (70, 4, 3000, 256), (3, 6, 64, 512),
+                                     (300, 2, 777, 64)])
+def test_bias_only_small(R, g, V, r):
+    _say(f"case bias-only R={R} g={g} V={V} r={r}")
+    cfg = Config("edge", R=R, gamma=g, V=V, r=r, d=16, mode=GREEDY, temperature=1.0, w_std=0.3,
+                 base_std=1.0, wconf_std=0.1, seed=500 + R)
+    _bias_only_case(make_workload(cfg))
+
+
+def test_bias_only_dsv4_shape():
+    _say("case bias-only at R=256, V=129280, r=512")
+    cfg = dataclasses.replace(CONFIGS["dsv4"], mode=GREEDY, w_std=0.05)
+    _bias_only_case(make_workload(cfg), rows=_sample_rows(256, 16, 4), bias=False)
