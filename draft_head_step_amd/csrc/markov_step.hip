@@ -194,6 +194,63 @@ __device__ __forceinline__ void w2_store(uint16_t* dst, const u32x4 (&st)[PMAX],
   }
 }
 
+// Rank 512: a W2 row is 1 KB, one wave-wide 16-byte load, so the chunk is staged
+// by direct loads into LDS (buffer_load ... lds): lane l's 16 bytes land at
+// M0 + 16 l, the row pitch keeps its 16-byte pad, and out-of-range lanes (blocks
+// past r, rows past V) write zeros.  No registers hold the data and no LDS
+// stores are issued; wave w stages rows w, w + NW, ...
+//
+// The load is issued from inline assembly on purpose.  The compiler does not
+// know it writes LDS, so it adds no drain before the LDS reads that follow.
+// The kernels instead wait for it explicitly (vmcnt, then a barrier) before
+// reading a stage buffer.  The compiler's own vmcnt waits for ordinary loads
+// stay correct: loads retire in issue order, so VMEM ops it does not see only
+// make a wait stricter.
+constexpr int kPitch512 = 512 + 8;
+
+__device__ __forceinline__ uint32_t w2_dma_lane_offset(int lane, int r) {
+  return lane * 8 < r ? (uint32_t)lane * 16u : kOutOfRange;
+}
+
+// Raw buffer descriptor words (base, stride 0, size in bytes, untyped dwords).
+__device__ __forceinline__ u32x4 raw_desc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kRsrcWord3};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int NW>
+__device__ __forceinline__ void w2_dma(uint16_t* buf, u32x4 dw2, uint32_t lane_off, int cc, int r,
+                                       int wave) {
+#pragma unroll
+  for (int j = 0; j < kChunk / NW; ++j) {
+    const int row = wave + j * NW;
+    const uint32_t voff = lane_off + (uint32_t)((cc * kChunk + row) * r) * 2u;
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(dw2), "{m0}"(lds_addr(buf + row * kPitch512))
+                 : "memory");
+  }
+}
+
+// s_waitcnt vmcnt(min(N, 63)), other counters untouched (gfx9 encoding).  A
+// smaller count only waits longer, so clamping keeps it correct.
+template <int N0>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int N = N0 < 63 ? N0 : 63;
+  static_assert(N >= 0, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// VMEM instructions one epi_load issues (they count in vmcnt with the DMA).
+template <int MODE, bool VEC4, int NJ>
+constexpr int epi_load_count() {
+  return MODE == kBiasOnly ? 0 : (VEC4 ? NJ : 4 * NJ) * (MODE == DSPARK_SAMPLE ? 2 : 1);
+}
+
 // Epilogue inputs of NJ accumulator groups (jq = j0 .. j0+NJ-1) of one chunk for
 // one lane: element 4*j + i is vocabulary entry v0 + 8*(j0+j) + 4*half + i; `off`
 // is the lane's byte offset of entry v0 + 8*j0 + 4*half.
@@ -226,6 +283,27 @@ __device__ __forceinline__ void epi_load(float (&bv)[4 * NJ], float (&uv)[4 * NJ
 
 constexpr int lcm_small(int a, int b) { return (a % b == 0) ? a : (b % a == 0) ? b : a * b; }
 
+// Scheduling template for one chunk's MFMA chain (masks: 0x100 LDS read,
+// 0x008 MFMA, 0x002 VALU): kLdsAhead A-operand reads first, then per K-step
+// one MFMA, the next read and two VALU instructions, then the last MFMAs.
+constexpr int kLdsAhead = 4;
+
+template <int KS>
+__device__ __forceinline__ void mfma_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kLdsAhead, 0);
+#pragma unroll
+  for (int s = 0; s < KS - kLdsAhead; ++s) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+#pragma unroll
+  for (int s = 0; s < kLdsAhead; ++s) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+}
+
 // Number of leading iterations of a group whose chunks lie wholly inside V: all
 // n_valid, unless the group's last chunk is the one that crosses V.
 __device__ __forceinline__ int n_whole(int c0, int cstep, int n_valid, int V) {
@@ -245,8 +323,16 @@ constexpr int plain_pd() { return plain_deep<RK, NW>() ? 3 : 1; }   // epilogue 
 template <int RK, int NW>
 constexpr int plain_unroll() { return lcm_small(plain_wd<RK, NW>(), plain_pd<RK, NW>() + 1); }
 
+// Rank 512 keeps 128 VGPRs of W1 rows per lane and its LDS stages hold one
+// workgroup per CU, so two waves per SIMD is the occupancy that can ever run.
+// Saying so lets the compiler spend registers on a deeper LDS-read pipeline
+// instead of packing for an occupancy the launch never reaches.
+template <int RK>
+constexpr int plain_max_waves() { return RK == 512 ? 2 : 8; }
+
 template <int RK, int NW, int MODE, bool VEC4, bool BIAS>
-__global__ __launch_bounds__(NW * 64) void markov_step_kernel(
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
     const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
@@ -263,6 +349,12 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   constexpr int PD = plain_pd<RK, NW>();
   constexpr int NS = PD + 1;
   constexpr int UNR = plain_unroll<RK, NW>();
+  constexpr bool DMA = RK == 512;                  // W2 staged by direct loads into LDS
+  constexpr int NBUF = DMA ? WD + 1 : 2;           // LDS stage buffers
+  // vmcnt at the top of an iteration that leaves only the loads issued after
+  // the DMA of its own chunk outstanding (0 with bias stores in flight).
+  constexpr int EL = epi_load_count<MODE, VEC4, 4>();
+  constexpr int DMA_WAIT = BIAS ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -298,43 +390,25 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   }
 
   const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
-  const uint32_t w2_off = w2_lane_offset<RK, NT>(tid, r);
+  const u32x4 dw2 = raw_desc(W2, (uint32_t)V * (uint32_t)r * 2u);
+  const uint32_t w2_off = DMA ? w2_dma_lane_offset(lane, r) : w2_lane_offset<RK, NT>(tid, r);
   const Rsrc rbase = MODE == kBiasOnly ? make_rsrc(W2, 0u) : block_rsrc(base, ad, rb, ROWS);
   const Rsrc runif = MODE == DSPARK_SAMPLE ? block_rsrc(unif, ad, rb, ROWS) : rbase;
   const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 4 * half) * 4u;
   const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
 
-  u32x4 stage[WD][PMAX];
+  u32x4 stage[DMA ? 1 : WD][DMA ? 1 : PMAX];
   float eb[NS][16];
   float eu[NS][16];
+  f32x16 accs[2];
   Argmax am;
+  static_assert(UNR % 2 == 0 && UNR % NS == 0, "the unroll must cycle the rings");
 
-  auto body = [&](auto masked, int i, u32x4 (&st)[PMAX], float (&cb)[16], float (&cu)[16],
-                  float (&pb)[16], float (&pu)[16]) {
+  // Fused bias-add + select of iteration i.  Rows past R are never written, so
+  // they need no mask.
+  auto finish = [&](auto masked, int i, const f32x16& acc, const float (&cb)[16],
+                    const float (&cu)[16]) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int b = i & 1;
-    w2_store<RK, NT, PMAX>(lds + b * BUF, st, tid);
-    lds_barrier();
-    w2_load<RK, NT, PMAX>(st, rw2, w2_off, chunk(i + WD), r);
-    epi_load<MODE, VEC4, 4>(pb, pu, rbase, runif, e_off + (uint32_t)chunk(i + PD) * e_cb);
-    __builtin_amdgcn_sched_barrier(0);   // issue the prefetches before the MFMAs
-
-    // Bias tile: 32 vocabulary rows x 32 requests over the compiled K = RK
-    // (steps past r multiply zero-filled LDS columns by zero registers).
-    const uint16_t* abase = lds + b * BUF + col * PITCH + half * 8;
-    f32x16 acc = {};
-#pragma unroll
-    for (int s0 = 0; s0 < KS; s0 += 4) {
-      bf16x8 a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(abase + (s0 + i) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], e[s0 + i], acc, 0, 0, 0);
-    }
-
-    // Fused bias-add + select.  Rows past R are never written, so they need
-    // no mask.
     const int cv = (c0 + i * cstep) * kChunk;
     const int vlim = i < n_valid ? V : 0;
     float av[16];
@@ -349,6 +423,47 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
         if (cv + o < vlim) oc[o] = acc[qq];
       }
     }
+  };
+
+  // Iteration i: stage chunk i, run its MFMAs into one accumulator, finish
+  // iteration i-1 from the other beside them (the select does not wait for this
+  // chunk's MFMAs), then refill the epilogue slot it freed with iteration i + PD.
+  // Iteration i's epilogue inputs live in slot i % NS.
+  auto body = [&](auto masked, auto first, int i, auto& st, f32x16& acc, const f32x16& pacc,
+                  float (&pb)[16], float (&pu)[16]) {
+    const int b = NBUF == 2 ? (i & 1) : i % NBUF;
+    if constexpr (DMA) {
+      // This wave's rows of chunk i have landed; the barrier publishes all rows.
+      if constexpr (decltype(first)::value) wait_vmcnt<0>();
+      else wait_vmcnt<DMA_WAIT>();
+      lds_barrier();
+      w2_dma<NW>(lds + ((i + WD) % NBUF) * BUF, dw2, w2_off, chunk(i + WD), r, wave);
+    } else {
+      w2_store<RK, NT, PMAX>(lds + b * BUF, st, tid);
+      lds_barrier();
+      w2_load<RK, NT, PMAX>(st, rw2, w2_off, chunk(i + WD), r);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before the MFMAs
+
+    // Bias tile: 32 vocabulary rows x 32 requests over the compiled K = RK
+    // (steps past r multiply zero-filled LDS columns by zero registers).
+    const uint16_t* abase = lds + b * BUF + col * PITCH + half * 8;
+    acc = f32x16{};
+#pragma unroll
+    for (int s0 = 0; s0 < KS; s0 += 4) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(abase + (s0 + i) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], e[s0 + i], acc, 0, 0, 0);
+    }
+    if (!decltype(first)::value || i >= 1) finish(masked, i - 1, pacc, pb, pu);
+    // Rank 512: LDS reads run kLdsAhead K-steps ahead of the MFMAs, and the
+    // previous chunk's select fills the issue slots between them (measured
+    // slower at rank 256, where the compiler's own order wins).
+    if constexpr (RK == 512) mfma_pipeline<KS>();
+    epi_load<MODE, VEC4, 4>(pb, pu, rbase, runif, e_off + (uint32_t)chunk(i + PD) * e_cb);
     // Keep each chunk's arithmetic in its own iteration: hoisting the noise of
     // a prefetched chunk next to its load would wait for that load.
     __builtin_amdgcn_sched_barrier(0);
@@ -358,26 +473,37 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
   // waits at the top of the loop can count them from the back.
 #pragma unroll
   for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
-    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, chunk(t), r);
+    if (t < WD) {
+      if constexpr (DMA) w2_dma<NW>(lds + t * BUF, dw2, w2_off, chunk(t), r, wave);
+      else w2_load<RK, NT, PMAX>(stage[t % (DMA ? 1 : WD)], rw2, w2_off, chunk(t), r);
+    }
     if (t < PD) epi_load<MODE, VEC4, 4>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Iterations [0, n_main) hold chunks wholly inside V and run unmasked; the
-  // rest (the chunk that crosses V, padding) take the masked select.
+  // The first UNR iterations (the first has nothing to finish) and those from
+  // n_main on use the masked select; in between every finished chunk lies
+  // wholly inside V.
   const int n_main = n_whole(c0, cstep, n_valid, V) / UNR * UNR;
-  int i0 = 0;
+#pragma unroll
+  for (int j = 0; j < UNR; ++j)
+    body(std::true_type{}, std::true_type{}, j, stage[DMA ? 0 : j % WD], accs[j & 1],
+         accs[(j + 1) & 1], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS]);
+  int i0 = UNR;
   for (; i0 < n_main; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(std::false_type{}, i0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS],
-           eu[(j + PD) % NS]);
+      body(std::false_type{}, std::false_type{}, i0 + j, stage[DMA ? 0 : j % WD], accs[j & 1],
+           accs[(j + 1) & 1], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS]);
   }
   for (; i0 < cpg; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(std::true_type{}, i0 + j, stage[j % WD], eb[j % NS], eu[j % NS], eb[(j + PD) % NS],
-           eu[(j + PD) % NS]);
+      body(std::true_type{}, std::false_type{}, i0 + j, stage[DMA ? 0 : j % WD], accs[j & 1],
+           accs[(j + 1) & 1], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS]);
   }
+  // cpg is a multiple of UNR: the last iteration used accs[1] and slot NS - 1.
+  finish(std::true_type{}, cpg - 1, accs[1], eb[NS - 1], eu[NS - 1]);
+  if constexpr (DMA) wait_vmcnt<0>();   // no direct load lands in LDS after exit
 
   // Lanes l and l^32 hold the same request: merge, then one lane writes the partial.
   float best = am.best;
@@ -397,17 +523,22 @@ __global__ __launch_bounds__(NW * 64) void markov_step_kernel(
 // so one barrier per chunk orders everything.  At the end the pair merges its
 // halves through LDS and writes one partial per request and V group.
 // ---------------------------------------------------------------------------
-constexpr int kSplitWD = 2;
+constexpr int kSplitWD = 1;
 constexpr int kSplitPD = 1;
 constexpr int kSplitUnroll = lcm_small(kSplitWD, kSplitPD + 1);
 
+constexpr int kSplitBufs = kSplitWD + 1;   // LDS stage buffers (direct loads run WD ahead)
+
 template <int NP>
 constexpr size_t ksplit_lds_bytes() {
-  return (size_t)2 * kChunk * (512 + 8) * 2 + (size_t)2 * (2 * NP) * 64 * 8 * 4;
+  return (size_t)kSplitBufs * kChunk * kPitch512 * 2 + (size_t)2 * (2 * NP) * 64 * 8 * 4;
 }
 
+// One K-split workgroup (its LDS stages and exchange buffer) fills a CU's LDS:
+// at most two waves per SIMD.
 template <int NP, int MODE, bool VEC4, bool BIAS>
-__global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
+__global__ __launch_bounds__(NP * 128)
+__attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
     const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
@@ -426,6 +557,14 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   constexpr int PD = kSplitPD;
   constexpr int NS = PD + 1;
   constexpr int UNR = kSplitUnroll;
+  constexpr int NBUF = kSplitBufs;
+  constexpr int EL = epi_load_count<MODE, VEC4, 2>();
+  // vmcnt at the top of an iteration that leaves only the loads issued after
+  // the DMA of its own chunk outstanding (0 with bias stores in flight).  With
+  // WD = 1 those are the previous iteration's epilogue loads, which also
+  // retires the epilogue inputs this iteration uses.
+  constexpr int DMA_WAIT = BIAS ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
+  static_assert(PITCH == kPitch512, "rank-512 pitch");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -445,7 +584,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   const int n_valid = cstep == 1 ? min(cpg, n_chunks - c0) : (n_chunks - 1 - vg) / cstep + 1;
   auto chunk = [&](int i) { return c0 + min(i, n_valid - 1) * cstep; };
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
-  float* xbuf = reinterpret_cast<float*>(smem + (size_t)2 * BUF * 2);   // [2][NW][64][8]
+  float* xbuf = reinterpret_cast<float*>(smem + (size_t)NBUF * BUF * 2);   // [2][NW][64][8]
 
   const int m_loc = pair * 32 + col;
   const int m = rb * ROWS + m_loc;
@@ -462,14 +601,13 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     }
   }
 
-  const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
-  const uint32_t w2_off = w2_lane_offset<RK, NT>(tid, r);
+  const u32x4 dw2 = raw_desc(W2, (uint32_t)V * (uint32_t)r * 2u);
+  const uint32_t w2_off = w2_dma_lane_offset(lane, r);
   const Rsrc rbase = MODE == kBiasOnly ? make_rsrc(W2, 0u) : block_rsrc(base, ad, rb, ROWS);
   const Rsrc runif = MODE == DSPARK_SAMPLE ? block_rsrc(unif, ad, rb, ROWS) : rbase;
   const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 16 * kh + 4 * half) * 4u;
   const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
 
-  u32x4 stage[WD][PMAX];
   float eb[NS][8];
   float eu[NS][8];
   float own[8];
@@ -498,17 +636,19 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     }
   };
 
-  auto body = [&](auto masked, auto first, int t, u32x4 (&st)[PMAX], float (&pb)[8],
-                  float (&pu)[8], float (&nb)[8], float (&nu)[8]) {
-    w2_store<RK, NT, PMAX>(lds + (t & 1) * BUF, st, tid);
+  auto body = [&](auto masked, auto first, int t, float (&pb)[8], float (&pu)[8], float (&nb)[8],
+                  float (&nu)[8]) {
+    // This wave's rows of chunk t have landed; the barrier publishes all rows.
+    if constexpr (decltype(first)::value) wait_vmcnt<0>();
+    else wait_vmcnt<DMA_WAIT>();
     lds_barrier();
-    w2_load<RK, NT, PMAX>(st, rw2, w2_off, chunk(t + WD), r);
+    w2_dma<NW>(lds + ((t + WD) % NBUF) * BUF, dw2, w2_off, chunk(t + WD), r, wave);
     __builtin_amdgcn_sched_barrier(0);
 
     // Wave kh reads the chunk's rows as col ^ 16*kh, so its own 16 rows always
     // land in acc[0..7] and the partner's in acc[8..15] (constant indices).
     const uint16_t* abase =
-        lds + (t & 1) * BUF + (col ^ (16 * kh)) * PITCH + half * 8 + kh * KH * 16;
+        lds + (t % NBUF) * BUF + (col ^ (16 * kh)) * PITCH + half * 8 + kh * KH * 16;
     f32x16 acc = {};
 #pragma unroll
     for (int s0 = 0; s0 < KH; s0 += 4) {
@@ -523,6 +663,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
     // iteration's barrier).  At t = 0 there is none (a uniform branch with no
     // memory loads).
     if (!decltype(first)::value || t >= 1) epilogue(masked, t - 1, (t - 1) & 1, pb, pu);
+    mfma_pipeline<KH>();
     // Hand the other half-tile to the partner; keep ours for the next iteration.
     float* px = xbuf + (((size_t)(t & 1) * NW + wave) * 64 + lane) * 8;
     *reinterpret_cast<float4*>(px) = make_float4(acc[8], acc[9], acc[10], acc[11]);
@@ -536,7 +677,7 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
 
 #pragma unroll
   for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
-    if (t < WD) w2_load<RK, NT, PMAX>(stage[t], rw2, w2_off, chunk(t), r);
+    if (t < WD) w2_dma<NW>(lds + t * BUF, dw2, w2_off, chunk(t), r, wave);
     if (t < PD) epi_load<MODE, VEC4, 2>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -548,21 +689,24 @@ __global__ __launch_bounds__(NP * 128) void markov_step_ksplit_kernel(
   const int n_main = n_whole(c0, cstep, n_valid, V) / UNR * UNR;
 #pragma unroll
   for (int j = 0; j < UNR; ++j)
-    body(std::true_type{}, std::true_type{}, j, stage[j % WD], eb[(j + NS - 1) % NS],
+    body(std::true_type{}, std::true_type{}, j, eb[(j + NS - 1) % NS],
          eu[(j + NS - 1) % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
   int i0 = UNR;
   for (; i0 < n_main; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(std::false_type{}, std::false_type{}, i0 + j, stage[j % WD], eb[(j + NS - 1) % NS],
+      body(std::false_type{}, std::false_type{}, i0 + j, eb[(j + NS - 1) % NS],
            eu[(j + NS - 1) % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
   }
   for (; i0 < cpg; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
-      body(std::true_type{}, std::false_type{}, i0 + j, stage[j % WD], eb[(j + NS - 1) % NS],
+      body(std::true_type{}, std::false_type{}, i0 + j, eb[(j + NS - 1) % NS],
            eu[(j + NS - 1) % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
   }
+  // No direct load may land in LDS after this point (the merge below reuses
+  // stage memory, and the workgroup's LDS is released at exit).
+  wait_vmcnt<0>();
   lds_barrier();   // the partner's last half-tile
   // cpg is a multiple of UNR (hence of NS): the last iteration's slot is NS - 1.
   epilogue(std::true_type{}, cpg - 1, (cpg - 1) & 1, eb[NS - 1], eu[NS - 1]);
@@ -626,7 +770,8 @@ struct StepVariant {
 template <int RK, int NW, int MODE, bool VEC4, bool BIAS>
 StepVariant plain_variant() {
   return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS>, NW * 64,
-          (size_t)2 * kChunk * (RK + 8) * 2, NW * 32, plain_unroll<RK, NW>()};
+          (size_t)(RK == 512 ? plain_wd<RK, NW>() + 1 : 2) * kChunk * (RK + 8) * 2, NW * 32,
+          plain_unroll<RK, NW>()};
 }
 template <int NP, int MODE, bool VEC4, bool BIAS>
 StepVariant ksplit_variant() {
