@@ -4,8 +4,7 @@
 // tau = sum (1 + sum_{j<=l_r} a_{r,j}); candidates sorted globally by survival)
 // and section 三 challenge 2 (no early stop: every budget is evaluated).
 //
-// One workgroup of 1024 threads (16 wavefronts) does the whole schedule in a
-// single launch, so the call costs one dispatch whatever the batch:
+// Steps (both paths):
 //   1. keys: the fp32 bit pattern of a (non-negative, so monotone in a),
 //      complemented so that an ascending sort gives descending survival;
 //   2. stable LSD radix sort, 4 passes of 8 bits.  Within a tile each wavefront
@@ -14,10 +13,11 @@
 //      over (digit, wave), which keeps equal keys in id order;
 //   3. exact fixed-point prefix sums q = rint(a * 2^40) (uint64) in sorted
 //      order, Theta for every budget in fp64, first argmax;
-//   4. inverse permutation, then l_r = #{j : rank(r, j) < m*}.
-// Up to 16384 candidates the tile lives in LDS (one tile, no global traffic);
-// beyond that the sort ping-pongs between two workspace buffers, tile by tile,
-// with a per-pass digit histogram giving the global digit offsets.
+//   4. l_r = #{j : rank(r, j) < m*}.
+// Up to 8192 candidates one workgroup of 1024 threads (16 wavefronts) does it
+// all in LDS in a single launch.  Beyond that the sort and the scan are spread
+// over tiles of 1024 candidates on the whole device through workspace buffers
+// (a dozen short launches, no host sync).
 #include "dspark_internal.h"
 
 namespace dspark {
@@ -26,10 +26,9 @@ namespace {
 constexpr int kT = 1024;          // threads
 constexpr int kW = kT / 64;       // wavefronts
 constexpr int kDig = 256;         // radix digits per pass
-constexpr int kTileItems = 16;    // items per thread in a tile of the global path
-constexpr int kTile = kT * kTileItems;
 constexpr double kTauScale = 1099511627776.0;       // 2^40
 constexpr double kTauInv = 1.0 / 1099511627776.0;   // 2^-40
+
 
 struct SchedShared {
   int cnt[kW * kDig];        // per-wave digit counters, then offsets
@@ -163,12 +162,35 @@ __device__ __forceinline__ void better(Best& b, const Best& o) {
   if (o.theta > b.theta || (o.theta == b.theta && o.m < b.m)) b = o;
 }
 
+// Block argmax of Theta (largest Theta, smallest m); every thread gets the result.
+__device__ __forceinline__ void block_best(SchedShared& sh, Best& best) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Best o;
+    o.theta = __shfl_xor(best.theta, off);
+    o.m = __shfl_xor(best.m, off);
+    o.S = __shfl_xor(best.S, off);
+    better(best, o);
+  }
+  if (lane == 0) {
+    sh.bval[w] = best.theta;
+    sh.bidx[w] = best.m;
+    sh.bsum[w] = best.S;
+  }
+  __syncthreads();
+  best = Best{sh.bval[0], sh.bidx[0], sh.bsum[0]};
+#pragma unroll
+  for (int j = 1; j < kW; ++j) better(best, Best{sh.bval[j], sh.bidx[j], sh.bsum[j]});
+}
+
 // Phase 3 + 4 for a sorted array (keys ck, ids) given in blocked chunks.
 // load(p, ck, id) fetches the element at sorted position p.
-template <int ITEMS, typename Load, typename SetRank>
+template <int ITEMS, typename Load, typename SetRank, typename SpsAt>
 __device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restrict__ sps,
                            int32_t* __restrict__ order, Load load, SetRank set_rank,
-                           Best& best) {
+                           SpsAt sps_at, Best& best) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.carry = 0ull;
   best.theta = -1.0;
@@ -207,7 +229,7 @@ __device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restric
       if (p < N) {
         S += q[i];
         const double tau = __ull2double_rn(rfx + S) * kTauInv;
-        const double th = tau * (double)sps[R + p];   // budget B = R + p + 1
+        const double th = tau * (double)sps_at(p, i);   // sps[R + p]: budget B = R + p + 1
         if (th > best.theta) {
           best.theta = th;
           best.m = p + 1;
@@ -224,26 +246,7 @@ __device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restric
     }
     __syncthreads();
   }
-  // block argmax (largest Theta, smallest m)
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    Best o;
-    o.theta = __shfl_xor(best.theta, off);
-    o.m = __shfl_xor(best.m, off);
-    o.S = __shfl_xor(best.S, off);
-    better(best, o);
-  }
-  if (lane == 0) {
-    sh.bval[w] = best.theta;
-    sh.bidx[w] = best.m;
-    sh.bsum[w] = best.S;
-  }
-  __syncthreads();
-  best = Best{sh.bval[0], sh.bidx[0], sh.bsum[0]};
-#pragma unroll
-  for (int j = 1; j < kW; ++j) better(best, Best{sh.bval[j], sh.bidx[j], sh.bsum[j]});
+  block_best(sh, best);
 }
 
 __device__ void write_results(int R, int gamma, const Best& best, const int* rank,
@@ -293,6 +296,14 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
     ck[i] = ok[i] ? key_of(surv[e]) : 0xffffffffu;
     id[i] = e;
   }
+  // The SPS entries of this thread's sorted positions, fetched now so that the
+  // latency hides behind the sort.
+  float spv[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int p = threadIdx.x * ITEMS + i;
+    spv[i] = p < N ? sps[R + p] : 0.0f;
+  }
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 8 * pass;
     zero_my_counters(sh);
@@ -335,92 +346,365 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
   Best best;
   scan_theta<ITEMS>(
       sh, N, R, sps, order, [&](int p, uint32_t& k, int& i) { k = skey[p]; i = sid[p]; },
-      [&](int i, int p) { sid[i] = p; }, best);
+      [&](int i, int p) { sid[i] = p; }, [&](int, int i) { return spv[i]; }, best);
   write_results(R, gamma, best, sid, lengths, info);
 }
 
 // ---------------------------------------------------------------------------
-// Global path: any N, tiles of kTile elements, ping-pong in workspace.
+// Global path (N > 8192): the same stable LSD radix sort spread over the
+// device, then the scan spread over the same tiles.  Per 8-bit pass:
+//   hist:    each workgroup counts the digits of its tile of kGTile candidates;
+//   scatter: each workgroup derives its tile's base of every digit from all the
+//            counts (or, with many tiles, reads it from one separate scan), ranks
+//            its tile stably (the ballot ranking of the single-tile path) and
+//            writes keys and ids to their places.
+// Then: per tile, the sum of its fixed-point survivals; per tile, the carry of
+// the tiles before it, the prefix sums, Theta at each position and the tile's
+// best; one workgroup picks m* over the tiles; lengths count the candidates
+// ranked below m*.  All on the caller's stream, no host sync.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void schedule_global_kernel(
-    const float* __restrict__ surv, const float* __restrict__ sps, int R, int gamma, int N,
-    uint32_t* __restrict__ k0, int* __restrict__ i0, uint32_t* __restrict__ k1,
-    int* __restrict__ i1, int* __restrict__ rank, int32_t* __restrict__ lengths,
-    int32_t* __restrict__ order, dspark_schedule_info* info) {
-  __shared__ SchedShared sh;
+constexpr int kGT = 256;                  // threads of a sort workgroup
+constexpr int kGW = kGT / 64;
+constexpr int kGItems = 4;
+constexpr int kGTile = kGT * kGItems;     // candidates per tile
+static_assert(kGT == kDig, "one thread per digit in the tile kernels");
+
+__device__ __forceinline__ int tile_elem(int t, int w, int i, int lane) {
+  return t * kGTile + w * 64 * kGItems + i * 64 + lane;   // (wave, item, lane) order
+}
+
+// Digit counts and bases are kept tile-major: hist[t * 256 + d].
+template <bool FIRST>
+__global__ __launch_bounds__(kGT) void sched_hist_kernel(const float* __restrict__ surv,
+                                                         const uint32_t* __restrict__ keys,
+                                                         int N, int shift,
+                                                         int* __restrict__ hist) {
+  __shared__ int h[kDig];
+  const int t = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < N; e += kT) {
-    k0[e] = key_of(surv[e]);
-    i0[e] = e;
+  h[threadIdx.x] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kGItems; ++i) {
+    const int e = tile_elem(t, w, i, lane);
+    if (e < N) atomicAdd(&h[((FIRST ? key_of(surv[e]) : keys[e]) >> shift) & 0xff], 1);
   }
   __syncthreads();
-  uint32_t* sk = k0;
-  int* si = i0;
-  uint32_t* dk = k1;
-  int* di = i1;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 8 * pass;
-    // digit histogram of the whole array (per-wave counters, ballot-aggregated)
-    zero_my_counters(sh);
-    for (int t0 = 0; t0 < N; t0 += kTile) {
-      uint32_t ck[kTileItems];
-      bool ok[kTileItems];
-      int rk[kTileItems];
+  hist[t * kDig + threadIdx.x] = h[threadIdx.x];
+}
+
+// Exclusive scan, in place, of the tile-major counts taken in (digit, tile)
+// order: one workgroup, chunks of 4 * kT with carry.  Used when there are too
+// many tiles for each scatter workgroup to derive its bases itself.
+__global__ __launch_bounds__(kT) void sched_scan_kernel(int* __restrict__ a, int ntiles) {
+  __shared__ int wtot[kW];
+  __shared__ int carry;
+  const int M = kDig * ntiles;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  auto at = [&](int k) -> int& { return a[(k % ntiles) * kDig + k / ntiles]; };
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < M; c0 += 4 * kT) {
+    const int b = c0 + 4 * t;
+    int v[4];
 #pragma unroll
-      for (int i = 0; i < kTileItems; ++i) {
-        const int e = t0 + w * 64 * kTileItems + i * 64 + lane;
-        ok[i] = e < N;
-        ck[i] = ok[i] ? sk[e] : 0xffffffffu;
-      }
-      rank_items<kTileItems>(sh, ck, ok, shift, rk);
+    for (int j = 0; j < 4; ++j) v[j] = b + j < M ? at(b + j) : 0;
+    const int s = v[0] + v[1] + v[2] + v[3];
+    int inc = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    int pre = carry, total = 0;
+#pragma unroll
+    for (int j = 0; j < kW; ++j) {
+      pre += j < w ? wtot[j] : 0;
+      total += wtot[j];
+    }
+    int run = pre + inc - s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (b + j < M) at(b + j) = run;
+      run += v[j];
     }
     __syncthreads();
-    if (threadIdx.x < kDig) {
-      int t = 0;
-#pragma unroll
-      for (int ww = 0; ww < kW; ++ww) t += sh.cnt[ww * kDig + threadIdx.x];
-      sh.tot[threadIdx.x] = t;
-    }
+    if (t == 0) carry += total;
     __syncthreads();
-    scan_digits(sh, sh.tot);
-    __syncthreads();
-    for (int t0 = 0; t0 < N; t0 += kTile) {
-      uint32_t ck[kTileItems];
-      int id[kTileItems];
-      bool ok[kTileItems];
-      int rk[kTileItems];
-      zero_my_counters(sh);
-#pragma unroll
-      for (int i = 0; i < kTileItems; ++i) {
-        const int e = t0 + w * 64 * kTileItems + i * 64 + lane;
-        ok[i] = e < N;
-        ck[i] = ok[i] ? sk[e] : 0xffffffffu;
-        id[i] = ok[i] ? si[e] : -1;
-      }
-      rank_items<kTileItems>(sh, ck, ok, shift, rk);
-      __syncthreads();
-      offsets_from_base(sh);
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kTileItems; ++i) {
-        if (ok[i]) {
-          const int d = (ck[i] >> shift) & 0xff;
-          const int dst = sh.cnt[w * kDig + d] + rk[i];
-          dk[dst] = ck[i];
-          di[dst] = id[i];
-        }
-      }
-      __syncthreads();
-    }
-    uint32_t* tk = sk; sk = dk; dk = tk;
-    int* ti = si; si = di; di = ti;
   }
-  Best best;
-  scan_theta<kTileItems>(
-      sh, N, R, sps, order, [&](int p, uint32_t& k, int& i) { k = sk[p]; i = si[p]; },
-      [&](int i, int p) { rank[i] = p; }, best);
-  write_results(R, gamma, best, rank, lengths, info);
+}
+
+// Tiles up to which a scatter workgroup derives its own digit bases from the
+// counts (one coalesced row per tile) instead of a separate scan launch.
+constexpr int kInlineTiles = 512;
+
+// Stable scatter of tile t for the digit at `shift`.  INLINE: `hist` holds the
+// counts of this pass and the bases are derived here; else it holds the bases.
+template <bool FIRST, bool INLINE>
+__global__ __launch_bounds__(kGT) void sched_scatter_kernel(
+    const float* __restrict__ surv, const uint32_t* __restrict__ sk, const int* __restrict__ si,
+    uint32_t* __restrict__ dk, int* __restrict__ di, int N, int shift, int ntiles,
+    const int* __restrict__ hist) {
+  __shared__ SchedShared sh;              // uses the first kGW rows of the counters
+  __shared__ int wtot[kGW];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int d = threadIdx.x;              // kGT == kDig: one thread per digit below
+  uint32_t ck[kGItems];
+  int id[kGItems];
+  bool ok[kGItems];
+  int rk[kGItems];
+#pragma unroll
+  for (int i = 0; i < kGItems; ++i) {
+    const int e = tile_elem(t, w, i, lane);
+    ok[i] = e < N;
+    ck[i] = ok[i] ? (FIRST ? key_of(surv[e]) : sk[e]) : 0xffffffffu;
+    id[i] = FIRST ? e : (ok[i] ? si[e] : -1);
+  }
+  // This tile's global base of digit d.
+  int base;
+  if (INLINE) {
+    int total = 0, pre = 0;
+#pragma unroll 8
+    for (int t2 = 0; t2 < ntiles; ++t2) {
+      const int h = hist[t2 * kDig + d];
+      total += h;
+      pre += t2 < t ? h : 0;
+    }
+    // exclusive scan of the digit totals over the 256 threads
+    int inc = total;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    int dpre = inc - total;
+#pragma unroll
+    for (int j = 0; j < kGW; ++j) dpre += j < w ? wtot[j] : 0;
+    base = dpre + pre;
+  } else {
+    base = hist[t * kDig + d];
+  }
+  zero_my_counters(sh);
+  rank_items<kGItems>(sh, ck, ok, shift, rk);
+  __syncthreads();
+  {   // per digit: the tile's base, then the waves in order
+    int run = base;
+#pragma unroll
+    for (int ww = 0; ww < kGW; ++ww) {
+      const int c = sh.cnt[ww * kDig + d];
+      sh.cnt[ww * kDig + d] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kGItems; ++i) {
+    if (ok[i]) {
+      const int dg = (ck[i] >> shift) & 0xff;
+      const int dst = sh.cnt[w * kDig + dg] + rk[i];
+      dk[dst] = ck[i];
+      di[dst] = id[i];
+    }
+  }
+}
+
+// The fixed-point scan and Theta over the sorted candidates, by tiles of kGTile
+// positions (thread: four consecutive positions, 16-byte loads when aligned).
+__device__ __forceinline__ void load4_sorted(const uint32_t* sk, const int* si, int N, int p0,
+                                             bool vec, uint32_t (&ck)[4], int (&id)[4]) {
+  if (vec && p0 + 3 < N) {
+    const uint4 k4 = *reinterpret_cast<const uint4*>(sk + p0);
+    const int4 i4 = *reinterpret_cast<const int4*>(si + p0);
+    ck[0] = k4.x; ck[1] = k4.y; ck[2] = k4.z; ck[3] = k4.w;
+    id[0] = i4.x; id[1] = i4.y; id[2] = i4.z; id[3] = i4.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = p0 + i < N;
+      ck[i] = in ? sk[p0 + i] : 0xffffffffu;
+      id[i] = in ? si[p0 + i] : -1;
+    }
+  }
+}
+
+__device__ __forceinline__ unsigned long long qfx(uint32_t ck) {
+  return __double2ull_rn((double)value_of(ck) * kTauScale);
+}
+
+// Block sum of one uint64 per thread (kGT threads); every thread gets it.
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long* red,
+                                                            unsigned long long v) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  unsigned long long s = 0;
+#pragma unroll
+  for (int j = 0; j < kGW; ++j) s += red[j];
+  return s;
+}
+
+// Per tile: the sum of its fixed-point survivals.
+__global__ __launch_bounds__(kGT) void sched_tsum_kernel(const uint32_t* __restrict__ sk,
+                                                         const int* __restrict__ si, int N,
+                                                         unsigned long long* __restrict__ tsum) {
+  __shared__ unsigned long long red[kGW];
+  const int p0 = blockIdx.x * kGTile + 4 * threadIdx.x;
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  uint32_t ck[4];
+  int id[4];
+  load4_sorted(sk, si, N, p0, a16(sk) && a16(si), ck, id);
+  unsigned long long v = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v += p0 + i < N ? qfx(ck[i]) : 0ull;
+  v = block_sum_u64(red, v);
+  if (threadIdx.x == 0) tsum[blockIdx.x] = v;
+}
+
+// Per tile: carry from the tiles before it, local scan, Theta at every position
+// of the tile, the tile's best (largest Theta, smallest m); writes order.
+struct TileBest {
+  double theta;
+  int m;
+  int pad;
+  unsigned long long S;
+};
+
+__global__ __launch_bounds__(kGT) void sched_tscan_kernel(
+    const uint32_t* __restrict__ sk, const int* __restrict__ si, const float* __restrict__ sps,
+    int R, int N, const unsigned long long* __restrict__ tsum, int32_t* __restrict__ order,
+    TileBest* __restrict__ tbest) {
+  __shared__ unsigned long long red[kGW];
+  __shared__ double bth[kGW];
+  __shared__ int bm[kGW];
+  __shared__ unsigned long long bs[kGW];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int p0 = t * kGTile + 4 * tid;
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  // carry: sum of the tiles before this one (threads split the tiles)
+  unsigned long long c = 0;
+  for (int t2 = tid; t2 < t; t2 += kGT) c += tsum[t2];
+  const unsigned long long carry = block_sum_u64(red, c);
+  __syncthreads();
+  uint32_t ck[4];
+  int id[4];
+  load4_sorted(sk, si, N, p0, a16(sk) && a16(si), ck, id);
+  float sv[4];
+  if (a16(sps + R) && p0 + 3 < N) {
+    const float4 s4 = *reinterpret_cast<const float4*>(sps + R + p0);
+    sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = p0 + i < N ? sps[R + p0 + i] : 0.0f;
+  }
+  unsigned long long q[4];
+  unsigned long long s4 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[i] = p0 + i < N ? qfx(ck[i]) : 0ull;
+    s4 += q[i];
+  }
+  // exclusive scan of s4 over the tile
+  unsigned long long inc = s4;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  unsigned long long S = carry + inc - s4;
+#pragma unroll
+  for (int j = 0; j < kGW; ++j) S += j < w ? red[j] : 0ull;
+  const unsigned long long rfx = (unsigned long long)R << 40;
+  Best best{-1.0, 0x7fffffff, 0ull};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = p0 + i;
+    if (p < N) {
+      S += q[i];
+      const double th = __ull2double_rn(rfx + S) * kTauInv * (double)sv[i];
+      if (th > best.theta) best = Best{th, p + 1, S};
+    }
+  }
+  if (order) {
+    if (a16(order) && p0 + 3 < N) {
+      *reinterpret_cast<int4*>(order + p0) = make_int4(id[0], id[1], id[2], id[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (p0 + i < N) order[p0 + i] = id[i];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Best o;
+    o.theta = __shfl_xor(best.theta, off);
+    o.m = __shfl_xor(best.m, off);
+    o.S = __shfl_xor(best.S, off);
+    better(best, o);
+  }
+  if (lane == 0) {
+    bth[w] = best.theta;
+    bm[w] = best.m;
+    bs[w] = best.S;
+  }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int j = 1; j < kGW; ++j) better(best, Best{bth[j], bm[j], bs[j]});
+    tbest[t] = TileBest{best.theta, best.m, 0, best.S};
+  }
+}
+
+// First argmax over m = 0 (tau = R) and the tiles' bests; writes m*, info, and
+// clears lengths for the count.  One workgroup.
+__global__ __launch_bounds__(kT) void sched_pick_kernel(const TileBest* __restrict__ tbest,
+                                                        int ntiles, const float* __restrict__ sps,
+                                                        int R, dspark_schedule_info* info,
+                                                        int* __restrict__ mstar,
+                                                        int32_t* __restrict__ lengths) {
+  __shared__ SchedShared sh;
+  const int tid = threadIdx.x;
+  for (int r = tid; r < R; r += kT) lengths[r] = 0;
+  Best best{-1.0, 0x7fffffff, 0ull};
+  if (tid == 0) best = Best{(double)R * (double)sps[R - 1], 0, 0ull};
+  for (int t = tid; t < ntiles; t += kT) better(best, Best{tbest[t].theta, tbest[t].m, tbest[t].S});
+  block_best(sh, best);
+  if (tid == 0) {
+    *mstar = best.m;
+    if (info) {
+      const unsigned long long tau_fx = ((unsigned long long)R << 40) + best.S;
+      info->B_star = R + best.m;
+      info->m_star = best.m;
+      info->tau_fx = tau_fx;
+      info->tau = __ull2double_rn(tau_fx) * kTauInv;
+      info->theta = best.theta;
+    }
+  }
+}
+
+// l_r = number of request r's candidates among the first m* sorted positions
+// (the definition; lengths were cleared by the pick kernel).
+__global__ __launch_bounds__(256) void sched_count_kernel(const int* __restrict__ si, int gamma,
+                                                          const int* __restrict__ mstar,
+                                                          int32_t* __restrict__ lengths) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p < *mstar) atomicAdd(&lengths[si[p] / gamma], 1);
 }
 
 template <int ITEMS>
@@ -442,10 +726,25 @@ dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, 
 
 }  // namespace
 
+// Global-path workspace: k0, i0, k1, i1, rank (Np = N rounded up to 4 each, so
+// every array keeps the base's 16-byte alignment), digit counts, m*.
+// Up to this many candidates the whole schedule runs in one workgroup's LDS.
+constexpr int kLdsMaxN = 8192;
+
 size_t schedule_workspace_bytes(int R, int gamma) {
   const size_t N = (size_t)R * (size_t)gamma;
-  if (N <= (size_t)kTile) return 256;
-  return 5 * N * sizeof(int32_t) + 256;
+  if (N <= (size_t)kLdsMaxN) return 256;
+  const size_t Np = (N + 3) / 4 * 4;
+  const size_t ntiles = (N + kGTile - 1) / kGTile;
+  return 4 * Np * sizeof(int32_t) + (size_t)kDig * ntiles * sizeof(int32_t) +
+         ntiles * (sizeof(unsigned long long) + sizeof(TileBest)) + 256;
+}
+
+template <bool FIRST, bool INLINE>
+void launch_scatter(int ntiles, hipStream_t stream, const float* surv, const uint32_t* sk,
+                    const int* si, uint32_t* dk, int* di, int N, int shift, const int* hist) {
+  hipLaunchKernelGGL((sched_scatter_kernel<FIRST, INLINE>), dim3(ntiles), dim3(kGT), 0, stream,
+                     surv, sk, si, dk, di, N, shift, ntiles, hist);
 }
 
 dspark_status launch_schedule(const float* surv, const float* sps, int R, int gamma,
@@ -455,17 +754,55 @@ dspark_status launch_schedule(const float* surv, const float* sps, int R, int ga
   if (N <= kT * 1) return launch_lds<1>(surv, sps, R, gamma, N, lengths, order, info, stream);
   if (N <= kT * 2) return launch_lds<2>(surv, sps, R, gamma, N, lengths, order, info, stream);
   if (N <= kT * 4) return launch_lds<4>(surv, sps, R, gamma, N, lengths, order, info, stream);
+  static_assert(kLdsMaxN == kT * 8, "the largest LDS variant covers kLdsMaxN");
   if (N <= kT * 8) return launch_lds<8>(surv, sps, R, gamma, N, lengths, order, info, stream);
-  if (N <= kT * 16) return launch_lds<16>(surv, sps, R, gamma, N, lengths, order, info, stream);
+  // Workspace: keys and ids twice (Np each, so every array keeps the base's
+  // 16-byte alignment), digit counts (256 x tiles), tile sums, tile bests, m*.
+  const int ntiles = (N + kGTile - 1) / kGTile;
+  const size_t Np = ((size_t)N + 3) / 4 * 4;
   int* ws = reinterpret_cast<int*>(workspace);
   uint32_t* k0 = reinterpret_cast<uint32_t*>(ws);
-  int* i0 = ws + N;
-  uint32_t* k1 = reinterpret_cast<uint32_t*>(ws + 2 * (size_t)N);
-  int* i1 = ws + 3 * (size_t)N;
-  int* rank = ws + 4 * (size_t)N;
-  hipLaunchKernelGGL(schedule_global_kernel, dim3(1), dim3(kT), 0, stream, surv, sps, R, gamma,
-                     N, k0, i0, k1, i1, rank, lengths, order, info);
-  return check_launch("schedule_global_kernel");
+  int* i0 = ws + Np;
+  uint32_t* k1 = reinterpret_cast<uint32_t*>(ws + 2 * Np);
+  int* i1 = ws + 3 * Np;
+  int* hist = ws + 4 * Np;
+  unsigned long long* tsum =
+      reinterpret_cast<unsigned long long*>(hist + (size_t)kDig * ntiles);   // 8-byte aligned
+  TileBest* tbest = reinterpret_cast<TileBest*>(tsum + ntiles);
+  int* mstar = reinterpret_cast<int*>(tbest + ntiles);
+  const bool inl = ntiles <= kInlineTiles;
+  // Keys and ids: surv -> (k1, i1) -> (k0, i0) -> (k1, i1) -> (k0, i0).
+  uint32_t* dk[4] = {k1, k0, k1, k0};
+  int* di[4] = {i1, i0, i1, i0};
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    const uint32_t* sk = pass == 0 ? nullptr : dk[pass - 1];
+    const int* si = pass == 0 ? nullptr : di[pass - 1];
+    if (pass == 0)
+      hipLaunchKernelGGL(sched_hist_kernel<true>, dim3(ntiles), dim3(kGT), 0, stream, surv, sk, N,
+                         shift, hist);
+    else
+      hipLaunchKernelGGL(sched_hist_kernel<false>, dim3(ntiles), dim3(kGT), 0, stream, surv, sk,
+                         N, shift, hist);
+    if (!inl) hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(kT), 0, stream, hist, ntiles);
+    if (pass == 0) {
+      if (inl) launch_scatter<true, true>(ntiles, stream, surv, sk, si, dk[0], di[0], N, shift, hist);
+      else launch_scatter<true, false>(ntiles, stream, surv, sk, si, dk[0], di[0], N, shift, hist);
+    } else {
+      if (inl) launch_scatter<false, true>(ntiles, stream, surv, sk, si, dk[pass], di[pass], N, shift, hist);
+      else launch_scatter<false, false>(ntiles, stream, surv, sk, si, dk[pass], di[pass], N, shift, hist);
+    }
+    dspark_status st = check_launch("schedule sort pass");
+    if (st != DSPARK_OK) return st;
+  }
+  hipLaunchKernelGGL(sched_tsum_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, N, tsum);
+  hipLaunchKernelGGL(sched_tscan_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, sps, R, N,
+                     tsum, order, tbest);
+  hipLaunchKernelGGL(sched_pick_kernel, dim3(1), dim3(kT), 0, stream, tbest, ntiles, sps, R, info,
+                     mstar, lengths);
+  hipLaunchKernelGGL(sched_count_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, i0, gamma,
+                     mstar, lengths);
+  return check_launch("schedule scan");
 }
 
 }  // namespace dspark

@@ -55,7 +55,7 @@ def test_workspace_queries():
     assert D.dspark_schedule_workspace(1 << 20, 16) == 0       # above the candidate limit
     assert D.dspark_schedule_workspace(256, 5) >= 1
     big = D.dspark_schedule_workspace(8192, 7)
-    assert big >= 5 * 8192 * 7 * 4
+    assert big >= 4 * 8192 * 7 * 4 + 256 * (8192 * 7 // 1024) * 4   # keys, ids x2 + digit counts
 
 
 def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, layout=0, mode=GREEDY, T=1.0,

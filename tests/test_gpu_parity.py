@@ -142,10 +142,12 @@ def _sched_case(c, sps):
     return H.check_schedule(s, sps, lengths, order, info)
 
 
-@pytest.mark.parametrize("R,g", [(1, 1), (4, 5), (1000, 2), (4096, 4), (3277, 5), (5000, 7)])
+@pytest.mark.parametrize("R,g", [(1, 1), (4, 5), (1000, 2), (2048, 4), (2731, 3), (3277, 5),
+                                 (5000, 7), (100003, 6)])
 def test_schedule_sizes_and_paths(R, g):
-    # 4096 x 4 = 16384 is the largest single-tile (LDS) case; 3277 x 5 = 16385 the
-    # smallest tiled (workspace) case.
+    # 2048 x 4 = 8192 is the largest single-workgroup (LDS) case; 2731 x 3 = 8193 the
+    # smallest tiled (workspace) case; 100003 x 6 has 586 tiles, more than a
+    # scatter workgroup sums itself, so the digit bases come from a separate scan.
     _say(f"case schedule R={R} g={g}")
     rng = np.random.default_rng(R * 31 + g)
     c = rng.beta(6, 1.5, size=(R, g)).astype(np.float32)
