@@ -16,9 +16,14 @@
 //     in registers for the whole launch.  The workgroup's waves share 32-column
 //     chunks of W2 staged through LDS (double-buffered, rows padded by 16 bytes
 //     so the A-operand reads hit distinct banks).
-//   * Each workgroup walks a contiguous group of chunks keeping a running
-//     (max, argmax) per request; a tiny second kernel reduces the per-group
-//     partials to the token.  No float atomics: results are deterministic.
+//   * Each workgroup walks a group of chunks keeping a running (max, argmax)
+//     per request, then folds it into one packed 64-bit word per request with
+//     an integer atomic max (order-independent, so results are deterministic).
+//     The next step reads its input tokens from those words (and its first V
+//     group stores them to the output); a small launch unpacks the last
+//     step.  A call is gamma + 2 launches: clear, the steps,
+//     unpack.  (A last-arriving workgroup could do the unpack, but the
+//     device-scope release fence it needs costs more than the launch.)
 //   * Workgroup ids are decoded so that the R-blocks sharing a V group land on
 //     the same XCD (ids congruent mod 8) and are dispatched together, so the
 //     second and later reads of a W2 chunk hit that XCD's L2.
@@ -76,6 +81,45 @@ __device__ __forceinline__ void merge_best(float& bv, int& bi, float ov, int oi)
     bi = oi;
   }
 }
+
+// Per-step results are kept as one 64-bit word per request, combined across
+// workgroups with an unsigned atomic max: the score in the high half (mapped
+// to an unsigned key that orders like the float, -0 taken as +0) and the
+// complement of the token id in the low half, so equal scores keep the
+// smallest id -- the same order as merge_best, independent of arrival order.
+// A cleared word (0) is below every packed value and decodes to token 0.
+__device__ __forceinline__ unsigned long long pack_best(float v, int i) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  const uint32_t key = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
+}
+
+__device__ __forceinline__ int unpack_token(unsigned long long w, int V) {
+  const uint32_t i = 0xffffffffu - (uint32_t)w;
+  return i < (uint32_t)V ? (int)i : 0;
+}
+
+// Where a step kernel takes its input tokens and leaves its results.
+struct StepIO {
+  const int32_t* anchors;              // step 0: x_0
+  const unsigned long long* prev;      // steps > 0: packed results of step k-1
+  unsigned long long* best;            // packed results of step k, cleared before step 0
+  int32_t* tokens;                     // [R][gamma]
+  int gamma;
+  int k;
+};
+
+// Token x_{k-1} of request m (step 0: the anchor).  The first V group of each
+// R block also stores it to tokens, which completes step k-1 there.
+__device__ __forceinline__ int step_input(const StepIO& io, int m, bool m_ok, bool writer,
+                                          int V) {
+  if (!m_ok) return 0;
+  if (!io.prev) return io.anchors[m];
+  const int x = unpack_token(io.prev[m], V);
+  if (writer) io.tokens[(size_t)m * io.gamma + io.k - 1] = x;
+  return x;
+}
+
 
 // Selection score of z = b + a.  Sampling compares the Gumbel-max score in
 // base 2: (z/T - ln(-ln u)) / ln 2 = z * log2(e)/T - log2(-log2 u) + const, the
@@ -335,9 +379,8 @@ __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
-    const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
-    int n_rblocks, int n_vgroups, int cpg, int cstep, int n_chunks, Addr ad,
-    float2* __restrict__ partials, float* __restrict__ bias_out) {
+    StepIO io, int R, int V, int r, float inv_t, int n_rblocks, int n_vgroups, int cpg,
+    int cstep, int n_chunks, Addr ad, float* __restrict__ bias_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int KS = RK / 16;
   constexpr int NT = NW * 64;
@@ -382,7 +425,7 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   const bool m_ok = m < R;
   bf16x8 e[KS];
   {
-    int x = m_ok ? prev[(size_t)m * prev_stride] : 0;
+    int x = step_input(io, m, m_ok, vg == 0 && half == 0, V);
     x = min(max(x, 0), V - 1);                          // out-of-range ids never fault
     const uint16_t* er = W1 + (size_t)x * r + half * 8;
 #pragma unroll
@@ -505,14 +548,13 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   finish(std::true_type{}, cpg - 1, accs[1], eb[NS - 1], eu[NS - 1]);
   if constexpr (DMA) wait_vmcnt<0>();   // no direct load lands in LDS after exit
 
-  // Lanes l and l^32 hold the same request: merge, then one lane writes the partial.
+  // Lanes l and l^32 hold the same request: merge, then one lane publishes.
   float best = am.best;
   int best_i = argmax_id(am, c0, cstep, 4 * half);
   const float ov = __shfl_xor(best, 32);
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
-  if (m_ok && half == 0)
-    partials[(size_t)m * n_vgroups + vg] = make_float2(best, __int_as_float(best_i));
+  if (m_ok && half == 0) atomicMax(io.best + m, pack_best(best, best_i));
 }
 
 // ---------------------------------------------------------------------------
@@ -541,9 +583,8 @@ __global__ __launch_bounds__(NP * 128)
 __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
-    const int32_t* __restrict__ prev, int prev_stride, int R, int V, int r, float inv_t,
-    int n_rblocks, int n_vgroups, int cpg, int cstep, int n_chunks, Addr ad,
-    float2* __restrict__ partials, float* __restrict__ bias_out) {
+    StepIO io, int R, int V, int r, float inv_t, int n_rblocks, int n_vgroups, int cpg,
+    int cstep, int n_chunks, Addr ad, float* __restrict__ bias_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int RK = 512;
   constexpr int NW = 2 * NP;
@@ -591,7 +632,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   const bool m_ok = m < R;
   bf16x8 e[KH];
   {
-    int x = m_ok ? prev[(size_t)m * prev_stride] : 0;
+    int x = step_input(io, m, m_ok, vg == 0 && kh == 0 && half == 0, V);
     x = min(max(x, 0), V - 1);
     const uint16_t* er = W1 + (size_t)x * r + half * 8;
 #pragma unroll
@@ -724,40 +765,27 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   if (kh == 0 && half == 0 && m_ok) {
     const float2 o = xch[pair * 32 + col];
     merge_best(best, best_i, o.x, __float_as_int(o.y));
-    partials[(size_t)m * n_vgroups + vg] = make_float2(best, __int_as_float(best_i));
+    atomicMax(io.best + m, pack_best(best, best_i));
   }
 }
 
-// Reduce the per-group partials [request][group] to x_k: one wave per request,
-// lanes read consecutive groups (coalesced), then a fixed shuffle tree.
-__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float2* __restrict__ partials,
-                                                            int R, int n_groups, int V,
-                                                            int gamma, int k,
-                                                            int32_t* __restrict__ tokens) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (m >= R) return;
-  float best = -INFINITY;
-  int best_i = 0x7fffffff;
-#pragma unroll 4
-  for (int g = lane; g < n_groups; g += 64) {
-    const float2 p = partials[(size_t)m * n_groups + g];
-    merge_best(best, best_i, p.x, __float_as_int(p.y));
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(best, off);
-    const int oi = __shfl_xor(best_i, off);
-    merge_best(best, best_i, ov, oi);
-  }
-  if (lane == 0) tokens[(size_t)m * gamma + k] = best_i < V ? best_i : 0;
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// tokens[m][k] from the packed results of the last step.
+__global__ __launch_bounds__(256) void last_tokens_kernel(const unsigned long long* __restrict__ w,
+                                                          int R, int V, int gamma, int k,
+                                                          int32_t* __restrict__ tokens) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m < R) tokens[(size_t)m * gamma + k] = unpack_token(w[m], V);
 }
 
 // ---- host side: kernel variants ----
 
 using StepKernel = void (*)(const uint16_t*, const uint16_t*, const float*, const float*,
-                            const int32_t*, int, int, int, int, float, int, int, int, int, int,
-                            Addr, float2*, float*);
+                            StepIO, int, int, int, float, int, int, int, int, int, Addr, float*);
 
 struct StepVariant {
   StepKernel fn;
@@ -853,7 +881,6 @@ int env_int(const char* name, int dflt) {
 }  // namespace
 
 MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch) {
-  (void)gamma;
   (void)for_launch;
   MarkovPlan p{};
   p.rk = r <= 64 ? 64 : r <= 128 ? 128 : r <= 256 ? 256 : 512;
@@ -875,7 +902,8 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
   p.n_rblocks = (R + rows - 1) / rows;
   p.n_chunks = (V + kChunk - 1) / kChunk;
   const int max_groups = p.n_chunks < kMaxGroups ? p.n_chunks : kMaxGroups;
-  p.ws_bytes = (size_t)R * (size_t)max_groups * sizeof(float2);   // partials [R][groups]
+  (void)max_groups;
+  p.ws_bytes = (size_t)gamma * (size_t)R * 8;   // packed per-step results [gamma][R]
   return p;
 }
 
@@ -919,7 +947,10 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   p.n_vgroups = strided ? groups : (p.n_chunks + p.cpg - 1) / p.cpg;
   const int cstep = strided ? groups : 1;
 
-  float2* partials = reinterpret_cast<float2*>(workspace);
+  unsigned long long* packed = reinterpret_cast<unsigned long long*>(workspace);
+  const int nclear = gamma * R * 2;
+  hipLaunchKernelGGL(clear_words_kernel, dim3((nclear + 255) / 256), dim3(256), 0, stream,
+                     reinterpret_cast<uint32_t*>(workspace), nclear);
   const int padded_groups = (p.n_vgroups + 7) / 8 * 8;
   const dim3 grid(padded_groups * p.n_rblocks);
   const float inv_t = mode == DSPARK_SAMPLE ? 1.0f / temperature : 1.0f;
@@ -928,8 +959,8 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   ad.cstride = tiled ? (size_t)R * kChunk : (size_t)kChunk;
   ad.total = tiled ? (size_t)gamma * p.n_chunks * R * kChunk : (size_t)R * gamma * V;
   for (int k = 0; k < gamma; ++k) {
-    const int32_t* prev = k == 0 ? anchors : tokens + (k - 1);
-    const int prev_stride = k == 0 ? 1 : gamma;
+    const StepIO io{anchors, k == 0 ? nullptr : packed + (size_t)(k - 1) * R,
+                    packed + (size_t)k * R, tokens, gamma, k};
     ad.k_off = tiled ? (size_t)k * p.n_chunks * R * kChunk : (size_t)k * V;
     // Timing hooks ride on the dispatch itself (start / stop timestamps of the
     // kernel's packet), so they add no marker packets between kernels.
@@ -939,17 +970,14 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
       if (events->end) ev_end = reinterpret_cast<hipEvent_t>(events->end[k]);
     }
     hipExtLaunchKernelGGL(var.fn, grid, dim3(var.threads), (uint32_t)var.lds, stream, ev_begin,
-                          ev_end, 0u, W1, W2, base, uniforms, prev, prev_stride, R, V, r, inv_t,
-                          p.n_rblocks, p.n_vgroups, p.cpg, cstep, p.n_chunks, ad, partials,
-                          bias_out);
+                          ev_end, 0u, W1, W2, base, uniforms, io, R, V, r, inv_t, p.n_rblocks,
+                          p.n_vgroups, p.cpg, cstep, p.n_chunks, ad, bias_out);
     dspark_status st = check_launch("markov_step_kernel");
     if (st != DSPARK_OK) return st;
-    hipLaunchKernelGGL(argmax_reduce_kernel, dim3((R + 3) / 4), dim3(256), 0, stream, partials,
-                       R, p.n_vgroups, V, gamma, k, tokens);
-    st = check_launch("argmax_reduce_kernel");
-    if (st != DSPARK_OK) return st;
   }
-  return DSPARK_OK;
+  hipLaunchKernelGGL(last_tokens_kernel, dim3((R + 255) / 256), dim3(256), 0, stream,
+                     packed + (size_t)(gamma - 1) * R, R, V, gamma, gamma - 1, tokens);
+  return check_launch("last_tokens_kernel");
 }
 
 }  // namespace dspark

@@ -131,7 +131,9 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *   tokens    [R, gamma] int32 output, tokens[m * gamma + k - 1] = x_k.
  *   bias_out  optional [R, gamma, V] fp32 output (in `layout` order) of the
  *             Markov bias of every step (a debugging aid; NULL on the hot path).
- *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...).
+ *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...):
+ *             gamma * R packed 64-bit step results.  Its contents on entry do
+ *             not matter (the call clears what it uses in its first launch).
  *   events    optional timing hooks (NULL on the hot path).
  * Errors: EINVAL for NULL required pointers (base is optional only in GREEDY
  * mode), R/gamma/V/r <= 0, V < 2, a bad layout or mode, a non-positive or

@@ -75,6 +75,26 @@ def test_deterministic_repeat():
     assert np.array_equal(a, b) and np.array_equal(ba.view(np.uint32), bb.view(np.uint32))
 
 
+def test_workspace_contents_do_not_matter():
+    # The call clears the words it combines into: a workspace full of 0xff, and
+    # the same workspace again after a call on other inputs, give the same tokens.
+    _say("case dirty workspace")
+    cfg = dataclasses.replace(CONFIGS["tiny"], mode=SAMPLE, temperature=0.8)
+    wl = make_workload(cfg, w_std=0.3)
+    g = H.to_device(wl, DEV)
+    R, gm, V = wl["base"].shape
+    need = D.dspark_markov_draft_workspace(R, gm, V, wl["r"])
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    args = (g["W1"], g["W2"], g["base"], g["anchors"], SAMPLE, 0.8, g["uniforms"])
+    a = D.dspark_markov_draft(*args, workspace=ws).cpu().numpy()
+    other = torch.flip(g["anchors"], [0]).contiguous()
+    D.dspark_markov_draft(g["W1"], g["W2"], g["base"], other, SAMPLE, 0.8, g["uniforms"],
+                          workspace=ws)
+    b = D.dspark_markov_draft(*args, workspace=ws).cpu().numpy()
+    assert np.array_equal(a, b)
+    H.check_draft(wl, a)
+
+
 # --------------------------------------------------------------------------- edges
 
 EDGE = [
@@ -128,6 +148,28 @@ def test_exact_ties_resolve_to_smallest_id():
     toks, _ = H.run_draft(wl, g)
     want = np.argmax(base, axis=2)
     assert np.array_equal(toks, want)
+
+
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
+def test_negative_maxima_and_zero_ties(layout):
+    # Every logit negative, with exact ties at the maximum (-1.5 in the first
+    # position, signed zeros in the second) spread over distant V groups: the
+    # cross-group combine must order negative scores and treat -0 == +0.
+    _say(f"case negative maxima layout={layout}")
+    R, gm, V, r = 70, 2, 20000, 64
+    rng = np.random.default_rng(11)
+    base = rng.uniform(-10, -2, size=(R, gm, V)).astype(np.float32)
+    for m in range(R):
+        ids = np.sort(rng.choice(V, size=3, replace=False))
+        base[m, 0, ids] = -1.5
+        ids = np.sort(rng.choice(V, size=4, replace=False))
+        base[m, 1, ids] = np.array([-0.0, 0.0, -0.0, 0.0], np.float32)[rng.permutation(4)]
+    wl = {"W1": np.zeros((V, r), np.uint16), "W2": np.zeros((V, r), np.uint16), "base": base,
+          "anchors": rng.integers(0, V, size=R).astype(np.int32), "mode": GREEDY,
+          "temperature": 1.0, "uniforms": None}
+    g = H.to_device(wl, DEV)
+    toks, _ = H.run_draft(wl, g, layout=layout)
+    assert np.array_equal(toks, np.argmax(base, axis=2))
 
 
 # --------------------------------------------------------------------------- scheduler
