@@ -73,6 +73,52 @@ def read_traffic(cfg, layout):
         return None
 
 
+def device_workload(cfg, dev, seed=None):
+    """Inputs of ``cfg`` drawn on the device (seeded torch generator) with the same
+    shapes and distributions as draft_head_step_amd.inputs.make_workload; used
+    for timing-only configurations whose logits are too large to draw on the
+    host quickly (the parity tests use the host workloads)."""
+    import torch
+    from draft_head_step_amd.inputs import sps_table
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed if seed is None else seed)
+    R, g, V, r, d = cfg.R, cfg.gamma, cfg.V, cfg.r, cfg.d
+
+    def normal(shape, std):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32).mul_(std)
+
+    base = normal((R, g, V), cfg.base_std)
+    if cfg.boost_count:
+        ids = torch.randint(0, V, (R, g, cfg.boost_count), generator=gen, device=dev)
+        base.scatter_(2, ids, base.gather(2, ids) + cfg.boost_value)
+    uniforms = None
+    if cfg.mode == 1:
+        k = torch.randint(0, 1 << 23, (R, g, V), generator=gen, device=dev, dtype=torch.int32)
+        uniforms = k.to(torch.float32).add_(0.5).mul_(2.0 ** -23)
+    b_max = max(cfg.b_max, R * (1 + g))
+    return {"R": R, "gamma": g, "V": V, "r": r, "d": d, "mode": cfg.mode,
+            "temperature": cfg.temperature,
+            "W1": normal((V, r), cfg.w_std).to(torch.bfloat16),
+            "W2": normal((V, r), cfg.w_std).to(torch.bfloat16),
+            "base": base, "uniforms": uniforms,
+            "h": normal((R, g, d), cfg.h_std).to(torch.bfloat16),
+            "w_conf": normal((d + r,), cfg.wconf_std),
+            "anchors": torch.randint(0, V, (R,), generator=gen, device=dev, dtype=torch.int32),
+            "sts": None if cfg.sts is None else torch.tensor(cfg.sts, dtype=torch.float32,
+                                                               device=dev),
+            "sps": torch.from_numpy(sps_table(cfg.sps_kind, b_max)).to(dev)}
+
+
+def tiled_on_device(x):
+    """[R, gamma, V] -> [gamma, ceil(V/32), R, 32] on the device (tail columns zero)."""
+    import torch
+    R, g, V = x.shape
+    C = (V + 31) // 32
+    if C * 32 != V:
+        x = torch.nn.functional.pad(x, (0, C * 32 - V))
+    return x.view(R, g, C, 32).permute(1, 2, 0, 3).contiguous()
+
+
 def cpu_baseline(wl):
     """Time the CPU oracle (as it stands) on one whole call of the same workload."""
     from oracle import dspark_oracle as O
@@ -101,7 +147,8 @@ def main():
     ap.add_argument("--no-row-major", action="store_true",
                     help="skip the secondary timing in the row-major layout")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the cold-cache, GEMM-only and row-major side measurements")
+                    help="skip the side measurements (cold caches, GEMM-only, scheduler "
+                         "stress, other configurations, measured bandwidth, row-major)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
@@ -248,6 +295,112 @@ def main():
         return {"shape": f"{name}: R={gR}, r={gr}, V={gV}", "avg_launch_ms": round(ms, 5),
                 "tflops": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
 
+    def whole_step_config(name, steps=10, warmup=3):
+        """Another configuration's whole step (draft + confidence + schedule) with
+        inputs drawn on the device, tiled logits; per-step ms and fused-launch us."""
+        c = CONFIGS[name]
+        w = device_workload(c, dev)
+        cR, cg, cV, cr = w["R"], w["gamma"], w["V"], w["r"]
+        cb = tiled_on_device(w["base"])
+        del w["base"]
+        cu = tiled_on_device(w["uniforms"]) if w["uniforms"] is not None else None
+        w["uniforms"] = None
+        ctok = torch.empty((cR, cg), dtype=torch.int32, device=dev)
+        cconf = torch.empty((cR, cg), dtype=torch.float32, device=dev)
+        csurv = torch.empty((cR, cg), dtype=torch.float32, device=dev)
+        clen = torch.empty((cR,), dtype=torch.int32, device=dev)
+        cwd = torch.empty(D.dspark_markov_draft_workspace(cR, cg, cV, cr), dtype=torch.uint8,
+                          device=dev)
+        cws = torch.empty(max(D.dspark_schedule_workspace(cR, cg), 1), dtype=torch.uint8,
+                          device=dev)
+
+        def one(ev=None):
+            D.dspark_markov_draft(w["W1"], w["W2"], cb, w["anchors"], c.mode, c.temperature, cu,
+                                  tokens=ctok, workspace=cwd, events=ev, stream=stream,
+                                  layout=D.LAYOUT_TILED)
+            D.dspark_confidence(w["h"], w["W1"], w["anchors"], ctok, w["w_conf"], w["sts"],
+                                conf=cconf, surv=csurv, stream=stream)
+            D.dspark_schedule(csurv, w["sps"], lengths=clen, workspace=cws, stream=stream)
+
+        for _ in range(warmup):
+            one()
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(cg)] for _ in range(steps)]
+        eve = [[torch.cuda.Event(enable_timing=True) for _ in range(cg)] for _ in range(steps)]
+        for lst in evb + eve:
+            for e in lst:
+                e.record(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            one(([e.cuda_event for e in evb[i]], [e.cuda_event for e in eve[i]]))
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        kd = [evb[i][k].elapsed_time(eve[i][k]) for i in range(steps) for k in range(cg)]
+        kms = float(np.mean(kd))
+        nb = cV * cr * 2 + cR * cV * 4 * (2 if cu is not None else 1) + cR * cr * 2 + cR * 4
+        del w, cb, cu, cwd, cws
+        return {"workload": f"{name}: R={cR}, gamma={cg}, V={cV}, r={cr}, d={c.d}, "
+                            f"{'sampling' if c.mode else 'greedy'}",
+                "ms_per_step": round(ms, 4), "value": round(cR * cg / (ms / 1e3), 1),
+                "unit": "draft tokens/s", "avg_launch_ms": round(kms, 5),
+                "launch_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(kd, [10, 50, 90])],
+                "frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "data": "synthetic, drawn on the device (seeded torch generator)"}
+
+    def scheduler_only(calls=30, warmup=5):
+        """dspark_survival + dspark_schedule on the scheduler stress workload (R = 8192,
+        gamma = 7, SPS over B = 1..65536): microseconds per call from HIP events."""
+        sw = make_workload(CONFIGS["sched_stress"])
+        sc = torch.from_numpy(sw["conf"]).to(dev)
+        ssps = torch.from_numpy(sw["sps"]).to(dev)
+        sR, sg = sw["conf"].shape
+        ssurv = torch.empty_like(sc)
+        slen = torch.empty((sR,), dtype=torch.int32, device=dev)
+        sws = torch.empty(D.dspark_schedule_workspace(sR, sg), dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            D.dspark_survival(sc, surv=ssurv, stream=stream)
+            D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws, stream=stream)
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(calls):
+            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b.record(stream)
+            D.dspark_survival(sc, surv=ssurv, stream=stream)
+            D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws, stream=stream)
+            e.record(stream)
+            torch.cuda.synchronize()
+            us.append(b.elapsed_time(e) * 1e3)
+        nbytes = sR * sg * 4 * 2 + sw["sps"].nbytes + sR * 4
+        p10, p50, p90 = (float(x) for x in np.percentile(us, [10, 50, 90]))
+        return {"workload": f"sched_stress: R={sR}, gamma={sg}, B_max={sw['B_max']}",
+                "us_per_call_p10_p50_p90": [round(p10, 1), round(p50, 1), round(p90, 1)],
+                "algorithmic_bytes": int(nbytes),
+                "achieved_GBps_at_p50": round(nbytes / (p50 / 1e6) / 1e9, 2),
+                "bound": "latency (launches: 1 survival + 12 schedule)"}
+
+    def hbm_measured(nbytes=1 << 31, reps=5):
+        """Large-copy and large-read bandwidth with plain torch kernels (a reference
+        beside the published peak)."""
+        n = nbytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        res = {}
+        for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                                ("read (sum)", lambda: src.sum(), nbytes)):
+            fn()
+            ts = []
+            for _ in range(reps):
+                b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                b.record(stream)
+                fn()
+                e.record(stream)
+                torch.cuda.synchronize()
+                ts.append(b.elapsed_time(e))
+            res[name + "_GBps"] = round(moved / (float(np.median(ts)) / 1e3) / 1e9, 1)
+        del src, dst
+        res["bytes"] = nbytes
+        return res
+
     ms_per_step, durs = run(args.layout, args.steps, args.warmup)
     k_ms = float(np.mean(durs))
     value = R * g / (ms_per_step / 1e3)
@@ -288,6 +441,9 @@ def main():
         out["cold"] = {"ms_per_step_median": round(cold, 4), "value": round(R * g / (cold / 1e3), 1),
                        "note": "512 MB cache flush before each step, outside its events"}
         out["gemm_only"] = [gemm_only(args.config), gemm_only("long_block")]
+        out["scheduler"] = scheduler_only()
+        out["other_configs"] = [whole_step_config("qwen3_8b"), whole_step_config("long_block")]
+        out["hbm_measured"] = hbm_measured()
     if not args.no_row_major and not args.no_extras and args.layout != "rgv":
         ms2, d2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1))
         k2 = float(np.mean(d2))

@@ -100,6 +100,8 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   if (!workspace || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "markov_draft: workspace needs %zu bytes (got %zu)", need,
                 workspace ? ws_bytes : (size_t)0);
+  if (!aligned16(workspace))
+    return fail(DSPARK_EINVAL, "markov_draft: workspace must be 16-byte aligned");
   return dspark::launch_markov_draft(W1, W2, base, anchors, R, gamma, V, r, layout, mode,
                                      temperature, uniforms, tokens, bias_out, workspace, events,
                                      reinterpret_cast<hipStream_t>(stream));

@@ -88,6 +88,15 @@ __device__ __forceinline__ void merge_best(float& bv, int& bi, float ov, int oi)
 // complement of the token id in the low half, so equal scores keep the
 // smallest id -- the same order as merge_best, independent of arrival order.
 // A cleared word (0) is below every packed value and decodes to token 0.
+// Each request has S words (1 or kMaxSubWords, chosen per call) and V group g
+// combines into word g % S.  The atomics of a launch all land at its end, R x
+// (V groups) of them on R x S words.  With many groups per request (small R,
+// e.g. 64 requests x 512 groups) one word per request serialises them on a few
+// lines (measured: 25.0 us per launch at S = 1 or 4, 21.7 us at S = 16); with
+// fewer groups, reading S words at the start of the next step costs more than
+// the contention saves (DeepSeek-V4 shape, 128 groups: 74.5 us at S = 1, 76.2 at 16).
+constexpr int kMaxSubWords = 16;
+constexpr int kSubWordsAboveGroups = 256;
 __device__ __forceinline__ unsigned long long pack_best(float v, int i) {
   const uint32_t b = __float_as_uint(v + 0.0f);
   const uint32_t key = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -99,14 +108,32 @@ __device__ __forceinline__ int unpack_token(unsigned long long w, int V) {
   return i < (uint32_t)V ? (int)i : 0;
 }
 
+// Token of request m from its S packed words (S a power of two).
+__device__ __forceinline__ int read_token(const unsigned long long* w, int m, int S, int V) {
+  unsigned long long b;
+  if (S == 1) {
+    b = w[m];
+  } else {   // S even: 16-byte loads
+    const ulonglong2* p = reinterpret_cast<const ulonglong2*>(w + (size_t)m * S);
+    b = 0;
+    for (int j = 0; j < S / 2; ++j) {
+      const ulonglong2 v = p[j];
+      b = v.x > b ? v.x : b;
+      b = v.y > b ? v.y : b;
+    }
+  }
+  return unpack_token(b, V);
+}
+
 // Where a step kernel takes its input tokens and leaves its results.
 struct StepIO {
   const int32_t* anchors;              // step 0: x_0
-  const unsigned long long* prev;      // steps > 0: packed results of step k-1
+  const unsigned long long* prev;      // steps > 0: packed results of step k-1 [R][sub]
   unsigned long long* best;            // packed results of step k, cleared before step 0
   int32_t* tokens;                     // [R][gamma]
   int gamma;
   int k;
+  int sub;                             // words per request (power of two)
 };
 
 // Token x_{k-1} of request m (step 0: the anchor).  The first V group of each
@@ -115,7 +142,7 @@ __device__ __forceinline__ int step_input(const StepIO& io, int m, bool m_ok, bo
                                           int V) {
   if (!m_ok) return 0;
   if (!io.prev) return io.anchors[m];
-  const int x = unpack_token(io.prev[m], V);
+  const int x = read_token(io.prev, m, io.sub, V);
   if (writer) io.tokens[(size_t)m * io.gamma + io.k - 1] = x;
   return x;
 }
@@ -554,7 +581,8 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   const float ov = __shfl_xor(best, 32);
   const int oi = __shfl_xor(best_i, 32);
   merge_best(best, best_i, ov, oi);
-  if (m_ok && half == 0) atomicMax(io.best + m, pack_best(best, best_i));
+  if (m_ok && half == 0)
+    atomicMax(io.best + (size_t)m * io.sub + (vg & (io.sub - 1)), pack_best(best, best_i));
 }
 
 // ---------------------------------------------------------------------------
@@ -765,21 +793,21 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   if (kh == 0 && half == 0 && m_ok) {
     const float2 o = xch[pair * 32 + col];
     merge_best(best, best_i, o.x, __float_as_int(o.y));
-    atomicMax(io.best + m, pack_best(best, best_i));
+    atomicMax(io.best + (size_t)m * io.sub + (vg & (io.sub - 1)), pack_best(best, best_i));
   }
 }
 
-__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
+__global__ __launch_bounds__(256) void clear_words_kernel(uint4* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // tokens[m][k] from the packed results of the last step.
 __global__ __launch_bounds__(256) void last_tokens_kernel(const unsigned long long* __restrict__ w,
-                                                          int R, int V, int gamma, int k,
+                                                          int S, int R, int V, int gamma, int k,
                                                           int32_t* __restrict__ tokens) {
   const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m < R) tokens[(size_t)m * gamma + k] = unpack_token(w[m], V);
+  if (m < R) tokens[(size_t)m * gamma + k] = read_token(w, m, S, V);
 }
 
 // ---- host side: kernel variants ----
@@ -890,7 +918,7 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
   // plain wave would need the whole SIMD); rank 512 greedy: eight plain waves;
   // up to 64 requests: two-wave workgroups, at most two per CU (fewer,
   // longer groups).  DSPARK_MARKOV_KSPLIT / _NW / _WG / _STRIDED override the
-  // choice for tuning.
+  // choice for tuning (and DSPARK_MARKOV_SUBWORDS the words per request).
   if (p.rk == 512 && mode == DSPARK_SAMPLE && nw == 8) nw = 4;
   const int ks_env = env_int("DSPARK_MARKOV_KSPLIT", -1);
   p.ksplit = p.rk == 512 && (ks_env < 0 ? mode == DSPARK_SAMPLE : ks_env != 0);
@@ -901,9 +929,8 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
   const int rows = p.ksplit ? nw / 2 * 32 : nw * 32;
   p.n_rblocks = (R + rows - 1) / rows;
   p.n_chunks = (V + kChunk - 1) / kChunk;
-  const int max_groups = p.n_chunks < kMaxGroups ? p.n_chunks : kMaxGroups;
-  (void)max_groups;
-  p.ws_bytes = (size_t)gamma * (size_t)R * 8;   // packed per-step results [gamma][R]
+  // packed per-step results [gamma][R][S], sized for the largest S
+  p.ws_bytes = (size_t)gamma * (size_t)R * kMaxSubWords * 8;
   return p;
 }
 
@@ -948,9 +975,14 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   const int cstep = strided ? groups : 1;
 
   unsigned long long* packed = reinterpret_cast<unsigned long long*>(workspace);
-  const int nclear = gamma * R * 2;
-  hipLaunchKernelGGL(clear_words_kernel, dim3((nclear + 255) / 256), dim3(256), 0, stream,
-                     reinterpret_cast<uint32_t*>(workspace), nclear);
+  int sub = p.n_vgroups > kSubWordsAboveGroups ? kMaxSubWords : 1;
+  const int sub_env = env_int("DSPARK_MARKOV_SUBWORDS", 0);
+  if (sub_env == 1 || sub_env == 2 || sub_env == 4 || sub_env == 8 || sub_env == 16) sub = sub_env;
+  const size_t words = (size_t)R * sub;
+  const size_t nclear = ((size_t)gamma * words + 1) / 2;   // 16-byte stores
+  const size_t cblocks = (nclear + 255) / 256;
+  hipLaunchKernelGGL(clear_words_kernel, dim3(cblocks < 1024 ? (unsigned)cblocks : 1024u),
+                     dim3(256), 0, stream, reinterpret_cast<uint4*>(workspace), nclear);
   const int padded_groups = (p.n_vgroups + 7) / 8 * 8;
   const dim3 grid(padded_groups * p.n_rblocks);
   const float inv_t = mode == DSPARK_SAMPLE ? 1.0f / temperature : 1.0f;
@@ -959,8 +991,8 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   ad.cstride = tiled ? (size_t)R * kChunk : (size_t)kChunk;
   ad.total = tiled ? (size_t)gamma * p.n_chunks * R * kChunk : (size_t)R * gamma * V;
   for (int k = 0; k < gamma; ++k) {
-    const StepIO io{anchors, k == 0 ? nullptr : packed + (size_t)(k - 1) * R,
-                    packed + (size_t)k * R, tokens, gamma, k};
+    const StepIO io{anchors, k == 0 ? nullptr : packed + (size_t)(k - 1) * words,
+                    packed + (size_t)k * words, tokens, gamma, k, sub};
     ad.k_off = tiled ? (size_t)k * p.n_chunks * R * kChunk : (size_t)k * V;
     // Timing hooks ride on the dispatch itself (start / stop timestamps of the
     // kernel's packet), so they add no marker packets between kernels.
@@ -976,7 +1008,8 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
     if (st != DSPARK_OK) return st;
   }
   hipLaunchKernelGGL(last_tokens_kernel, dim3((R + 255) / 256), dim3(256), 0, stream,
-                     packed + (size_t)(gamma - 1) * R, R, V, gamma, gamma - 1, tokens);
+                     packed + (size_t)(gamma - 1) * words, sub, R, V, gamma, gamma - 1,
+                     tokens);
   return check_launch("last_tokens_kernel");
 }
 

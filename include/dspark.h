@@ -131,9 +131,10 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *   tokens    [R, gamma] int32 output, tokens[m * gamma + k - 1] = x_k.
  *   bias_out  optional [R, gamma, V] fp32 output (in `layout` order) of the
  *             Markov bias of every step (a debugging aid; NULL on the hot path).
- *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...):
- *             gamma * R packed 64-bit step results.  Its contents on entry do
- *             not matter (the call clears what it uses in its first launch).
+ *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...),
+ *             16-byte aligned: up to 16 packed 64-bit partial results per
+ *             request and step.  Its contents on entry do not matter (the call clears what
+ *             it uses in its first launch).
  *   events    optional timing hooks (NULL on the hot path).
  * Errors: EINVAL for NULL required pointers (base is optional only in GREEDY
  * mode), R/gamma/V/r <= 0, V < 2, a bad layout or mode, a non-positive or
@@ -141,7 +142,8 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  * where one step of one block of requests would not fit 32-bit byte offsets:
  * ceil(V/32)*32*r > 2^30, gamma*V >= 2^22 (DSPARK_LAYOUT_RGV) or
  * ceil(V/32)*R + 256 > 2^25 (DSPARK_LAYOUT_TILED); EWORKSPACE if the workspace
- * is too small; EDEVICE on a launch failure.
+ * is NULL or too small, EINVAL if it is not 16-byte aligned; EDEVICE on a
+ * launch failure.
  */
 dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
                                   const int32_t* anchors, int R, int gamma, int V, int r,

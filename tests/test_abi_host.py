@@ -83,7 +83,7 @@ def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, layout=0, mode
     (dict(g=1, V=1 << 22), EUNSUPPORTED),                       # gamma*V = 2^22, RGV
     (dict(V=(1 << 21) + 32, r=512, layout=1), EUNSUPPORTED),   # ceil(V/32)*32*r > 2^30
     (dict(R=1 << 20, V=4096, layout=1), EUNSUPPORTED),         # ceil(V/32)*R > 2^25
-    (dict(ws=None), EWORKSPACE), (dict(ws_bytes=8), EWORKSPACE),
+    (dict(ws=None), EWORKSPACE), (dict(ws_bytes=8), EWORKSPACE), (dict(ws=P + 8), EINVAL),
 ])
 def test_markov_draft_rejects(kw, want):
     assert _draft(**kw) == want
