@@ -139,8 +139,8 @@ def cpu_baseline(wl):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="dsv4")
     ap.add_argument("--layout", choices=["tiled", "rgv"], default="tiled",
                     help="storage order of base / uniforms handed to the draft")
@@ -203,8 +203,23 @@ def main():
     ws_s = torch.empty(D.dspark_schedule_workspace(R, g), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def run(layout, steps, warmup):
-        """Time `steps` whole steps; return (ms per step, fused-step launch durations in ms)."""
+    def warm(fn, ms=40.0):
+        """Run fn until about `ms` of GPU work has passed (sustained clocks)."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+
+    def run(layout, steps, warmup, ev_steps=50):
+        """Time `steps` whole steps; return (ms per step, fused-step launch durations in ms).
+
+        Everything the timed region needs (events included) is made before the
+        warm-up, and the timed steps follow the warm-up at once: the GPU runs at
+        its sustained clocks (after an idle gap the first ~20 ms of steps run
+        about 10% slower).  The per-launch durations come from a second run of
+        `ev_steps` steps with HIP events attached to each fused launch's dispatch."""
         base, unif = inputs(layout)
         lay = layouts[layout]
 
@@ -216,25 +231,29 @@ def main():
                                 stream=stream)
             D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
 
-        for _ in range(warmup):
-            one_step()
-        torch.cuda.synchronize()
-
-        # HIP events bracketing every fused Markov step launch inside the timed region.
         def mk():
             e = torch.cuda.Event(enable_timing=True)
             e.record(stream)   # materialise the underlying hipEvent_t
             return e
-        begins = [[mk() for _ in range(g)] for _ in range(steps)]
-        ends = [[mk() for _ in range(g)] for _ in range(steps)]
+        begins = [[mk() for _ in range(g)] for _ in range(ev_steps)]
+        ends = [[mk() for _ in range(g)] for _ in range(ev_steps)]
+        evs = [([e.cuda_event for e in begins[i]], [e.cuda_event for e in ends[i]])
+               for i in range(ev_steps)]
         torch.cuda.synchronize()
 
+        for _ in range(warmup):
+            one_step()
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            one_step(([e.cuda_event for e in begins[i]], [e.cuda_event for e in ends[i]]))
+        for _ in range(steps):
+            one_step()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        durs = [begins[i][k].elapsed_time(ends[i][k]) for i in range(steps) for k in range(g)]
+        # HIP events bracketing every fused Markov step launch.
+        for i in range(ev_steps):
+            one_step(evs[i])
+        torch.cuda.synchronize()
+        durs = [begins[i][k].elapsed_time(ends[i][k]) for i in range(ev_steps) for k in range(g)]
         del base, unif
         return (t1 - t0) * 1e3 / steps, durs
 
@@ -244,10 +263,13 @@ def main():
         base, unif = inputs(layout)
         lay = layouts[layout]
         scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n + 1)]
+        warm(lambda: scratch.fill_(0.0))
         times = []
         for i in range(n + 1):
             scratch.fill_(float(i))
-            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b, e = evs[i]
             b.record(stream)
             D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
                                   tokens=tokens, workspace=ws_d, stream=stream, layout=lay)
@@ -272,16 +294,13 @@ def main():
         gtok = torch.empty((gR, gg), dtype=torch.int32, device=dev)
         gws = torch.empty(D.dspark_markov_draft_workspace(gR, gg, gV, gr), dtype=torch.uint8,
                           device=dev)
-        for _ in range(2):
-            D.dspark_markov_draft(gW1, gW2, None, ganc, 0, gamma=gg, tokens=gtok, workspace=gws,
-                                  stream=stream)
-        torch.cuda.synchronize()
         evb = [[torch.cuda.Event(enable_timing=True) for _ in range(gg)] for _ in range(steps)]
         eve = [[torch.cuda.Event(enable_timing=True) for _ in range(gg)] for _ in range(steps)]
         for lst in evb + eve:
             for e in lst:
                 e.record(stream)
-        torch.cuda.synchronize()
+        warm(lambda: D.dspark_markov_draft(gW1, gW2, None, ganc, 0, gamma=gg, tokens=gtok,
+                                           workspace=gws, stream=stream))
         for i in range(steps):
             D.dspark_markov_draft(gW1, gW2, None, ganc, 0, gamma=gg, tokens=gtok, workspace=gws,
                                   stream=stream,
@@ -295,7 +314,7 @@ def main():
         return {"shape": f"{name}: R={gR}, r={gr}, V={gV}", "avg_launch_ms": round(ms, 5),
                 "tflops": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
 
-    def whole_step_config(name, steps=10, warmup=3):
+    def whole_step_config(name, steps=20):
         """Another configuration's whole step (draft + confidence + schedule) with
         inputs drawn on the device, tiled logits; per-step ms and fused-launch us."""
         c = CONFIGS[name]
@@ -322,19 +341,20 @@ def main():
                                 conf=cconf, surv=csurv, stream=stream)
             D.dspark_schedule(csurv, w["sps"], lengths=clen, workspace=cws, stream=stream)
 
-        for _ in range(warmup):
-            one()
         evb = [[torch.cuda.Event(enable_timing=True) for _ in range(cg)] for _ in range(steps)]
         eve = [[torch.cuda.Event(enable_timing=True) for _ in range(cg)] for _ in range(steps)]
         for lst in evb + eve:
             for e in lst:
                 e.record(stream)
-        torch.cuda.synchronize()
+        warm(one)
         t0 = time.perf_counter()
+        for _ in range(steps):
+            one()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
         for i in range(steps):
             one(([e.cuda_event for e in evb[i]], [e.cuda_event for e in eve[i]]))
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
         kd = [evb[i][k].elapsed_time(eve[i][k]) for i in range(steps) for k in range(cg)]
         kms = float(np.mean(kd))
         nb = cV * cr * 2 + cR * cV * 4 * (2 if cu is not None else 1) + cR * cr * 2 + cR * 4
@@ -347,7 +367,7 @@ def main():
                 "frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                 "data": "synthetic, drawn on the device (seeded torch generator)"}
 
-    def scheduler_only(calls=30, warmup=5):
+    def scheduler_only(calls=30):
         """dspark_survival + dspark_schedule on the scheduler stress workload (R = 8192,
         gamma = 7, SPS over B = 1..65536): microseconds per call from HIP events."""
         sw = make_workload(CONFIGS["sched_stress"])
@@ -357,16 +377,17 @@ def main():
         ssurv = torch.empty_like(sc)
         slen = torch.empty((sR,), dtype=torch.int32, device=dev)
         sws = torch.empty(D.dspark_schedule_workspace(sR, sg), dtype=torch.uint8, device=dev)
-        for _ in range(warmup):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+
+        def one():
             D.dspark_survival(sc, surv=ssurv, stream=stream)
             D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws, stream=stream)
-        torch.cuda.synchronize()
+        warm(one, 20.0)
         us = []
-        for _ in range(calls):
-            b, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for b, e in evs:
             b.record(stream)
-            D.dspark_survival(sc, surv=ssurv, stream=stream)
-            D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws, stream=stream)
+            one()
             e.record(stream)
             torch.cuda.synchronize()
             us.append(b.elapsed_time(e) * 1e3)
@@ -441,7 +462,7 @@ def main():
         out["other_configs"] = [whole_step_config("qwen3_8b"), whole_step_config("long_block")]
         out["hbm_measured"] = hbm_measured()
     if not args.no_row_major and not args.no_extras and args.layout != "rgv":
-        ms2, d2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1))
+        ms2, d2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1), ev_steps=20)
         k2 = float(np.mean(d2))
         out["row_major"] = {"layout": "rgv", "ms_per_step": round(ms2, 4),
                             "value": round(R * g / (ms2 / 1e3), 1),

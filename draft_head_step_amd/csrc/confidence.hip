@@ -8,10 +8,13 @@
 //
 // The work is a dot product of length d + r per (request, position), bound by
 // the HBM read of h.  One workgroup handles all gamma positions of one
-// request (one wavefront per position), so the survival products are a short
-// sequential tail in the same workgroup.  Each lane streams 16-byte pieces of h
-// (8 bf16) with the matching two float4 pieces of w_h, four pieces in flight;
-// the wavefront reduces with a fixed shuffle tree, so results are deterministic.
+// request, so the survival products are a short sequential tail in the same
+// workgroup.  Each position's h row is split over P = 16 / gamma wavefronts
+// (P >= 1), so that every lane has only a few 16-byte pieces of h (8 bf16, with
+// the matching two float4 pieces of w_h) and issues them all at once; the
+// token is read first so that the W1-row chain overlaps the h stream.  Lanes
+// reduce with a fixed shuffle tree and the P parts are added in a fixed order,
+// so results are deterministic.
 #include <math.h>
 
 #include "dspark_internal.h"
@@ -32,95 +35,108 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum of w[i] * x[i] (x bf16) over this lane's share of [0, n): 16-byte pieces
-// strided by the wavefront, four independent partial sums so that several
-// loads are in flight per lane.
+// Sum of w[i] * x[i] (x bf16) over this lane's share of elements [i0, i1):
+// 16-byte pieces strided by the wavefront (vec: i0, i1 multiples of 8 and both
+// arrays 16-byte aligned), eight pieces per lane in flight per round.
 __device__ __forceinline__ float dot_part(const float* __restrict__ w,
-                                          const uint16_t* __restrict__ x, int n, bool vec,
-                                          int lane) {
+                                          const uint16_t* __restrict__ x, int i0, int i1,
+                                          bool vec, int lane) {
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  int tail_from = 0;
   if (vec) {
-    const int n8 = n >> 3;
-    int p = lane;
-    for (; p + 192 < n8; p += 256) {
+    const int p1 = i1 >> 3;
+    for (int p = (i0 >> 3) + lane; p < p1; p += 512) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int pp = p + 64 * u;
-        const u32x4 hv = *reinterpret_cast<const u32x4*>(x + 8 * pp);
-        const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * pp);
-        const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * pp + 4);
-        float a = acc[u];
-        a = fmaf(w0.x, bf16_lo(hv.x), a);
-        a = fmaf(w0.y, bf16_hi(hv.x), a);
-        a = fmaf(w0.z, bf16_lo(hv.y), a);
-        a = fmaf(w0.w, bf16_hi(hv.y), a);
-        a = fmaf(w1.x, bf16_lo(hv.z), a);
-        a = fmaf(w1.y, bf16_hi(hv.z), a);
-        a = fmaf(w1.z, bf16_lo(hv.w), a);
-        a = fmaf(w1.w, bf16_hi(hv.w), a);
-        acc[u] = a;
+        if (pp < p1) {
+          const u32x4 hv = *reinterpret_cast<const u32x4*>(x + 8 * pp);
+          const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * pp);
+          const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * pp + 4);
+          float a = acc[u & 3];
+          a = fmaf(w0.x, bf16_lo(hv.x), a);
+          a = fmaf(w0.y, bf16_hi(hv.x), a);
+          a = fmaf(w0.z, bf16_lo(hv.y), a);
+          a = fmaf(w0.w, bf16_hi(hv.y), a);
+          a = fmaf(w1.x, bf16_lo(hv.z), a);
+          a = fmaf(w1.y, bf16_hi(hv.z), a);
+          a = fmaf(w1.z, bf16_lo(hv.w), a);
+          a = fmaf(w1.w, bf16_hi(hv.w), a);
+          acc[u & 3] = a;
+        }
       }
     }
-    for (; p < n8; p += 64) {
-      const u32x4 hv = *reinterpret_cast<const u32x4*>(x + 8 * p);
-      const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * p);
-      const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * p + 4);
-      float a = acc[0];
-      a = fmaf(w0.x, bf16_lo(hv.x), a);
-      a = fmaf(w0.y, bf16_hi(hv.x), a);
-      a = fmaf(w0.z, bf16_lo(hv.y), a);
-      a = fmaf(w0.w, bf16_hi(hv.y), a);
-      a = fmaf(w1.x, bf16_lo(hv.z), a);
-      a = fmaf(w1.y, bf16_hi(hv.z), a);
-      a = fmaf(w1.z, bf16_lo(hv.w), a);
-      a = fmaf(w1.w, bf16_hi(hv.w), a);
-      acc[0] = a;
-    }
-    tail_from = 8 * n8;
+  } else {
+    for (int i = i0 + lane; i < i1; i += 64)
+      acc[0] = fmaf(w[i], __uint_as_float((unsigned)x[i] << 16), acc[0]);
   }
-  for (int i = tail_from + lane; i < n; i += 64)
-    acc[1] = fmaf(w[i], __uint_as_float((unsigned)x[i] << 16), acc[1]);
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-// One workgroup per request, one wavefront per draft position (looping when
-// gamma exceeds the wavefront count).
+// Element range [lo, hi) of part j of P over n elements, in whole pieces of 8
+// when vec.
+__device__ __forceinline__ void part_range(int n, int P, int j, bool vec, int& lo, int& hi) {
+  if (vec) {
+    const int n8 = n >> 3;
+    lo = 8 * (int)(((long long)n8 * j) / P);
+    hi = 8 * (int)(((long long)n8 * (j + 1)) / P);
+  } else {
+    lo = (int)(((long long)n * j) / P);
+    hi = (int)(((long long)n * (j + 1)) / P);
+  }
+}
+
+// One workgroup per request.  With P wavefronts per position and G positions
+// per round (G * P wavefronts), wavefront w takes part w % P of position
+// w / P; part P - 1 also adds the W1-row term.
 __global__ __launch_bounds__(1024) void confidence_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ W1,
     const int32_t* __restrict__ anchors, const int32_t* __restrict__ tokens,
     const float* __restrict__ w_conf, const float* __restrict__ sts_temp, int gamma, int d,
-    int V, int r, int vec_h, int vec_e, float* __restrict__ conf, float* __restrict__ surv) {
+    int V, int r, int P, int vec_h, int vec_e, float* __restrict__ conf,
+    float* __restrict__ surv) {
+  __shared__ float parts[1024 / 64];
   __shared__ float cval[kMaxGamma];
   const int m = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
+  const int G = (blockDim.x >> 6) / P;   // positions per round
   const float* w_h = w_conf;
   const float* w_e = w_conf + d;
   float a = 1.0f;   // running survival product (thread 0)
-  for (int k0 = 0; k0 < gamma; k0 += kMaxGamma) {
-    const int kn = min(kMaxGamma, gamma - k0);
-    for (int kk = wave; kk < kn; kk += nwaves) {
-      const int k = k0 + kk;
-      int x = k == 0 ? anchors[m] : tokens[(size_t)m * gamma + k - 1];
-      x = min(max(x, 0), V - 1);
-      float part = dot_part(w_h, h + ((size_t)m * gamma + k) * d, d, vec_h, lane);
-      part += dot_part(w_e, W1 + (size_t)x * r, r, vec_e, lane);
-      const float s = wave_sum(part);
-      if (lane == 0) {
-        const float t = sts_temp ? sts_temp[k] : 1.0f;
-        const float c = 1.0f / (1.0f + expf(-(s / t)));
-        conf[(size_t)m * gamma + k] = c;
-        cval[kk] = c;
+  for (int k0 = 0; k0 < gamma; k0 += G) {
+    const int kk = wave / P;
+    const int j = wave % P;
+    const int k = k0 + kk;
+    if (kk < G && k < gamma) {
+      int x = 0;
+      if (j == P - 1) x = k == 0 ? anchors[m] : tokens[(size_t)m * gamma + k - 1];
+      int lo, hi;
+      part_range(d, P, j, vec_h, lo, hi);
+      float part = dot_part(w_h, h + ((size_t)m * gamma + k) * d, lo, hi, vec_h, lane);
+      if (j == P - 1) {
+        x = min(max(x, 0), V - 1);
+        part += dot_part(w_e, W1 + (size_t)x * r, 0, r, vec_e, lane);
       }
+      const float s = wave_sum(part);
+      if (lane == 0) parts[wave] = s;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < G && k0 + (int)threadIdx.x < gamma) {
+      const int kt = k0 + threadIdx.x;
+      float s = 0.0f;
+      for (int jj = 0; jj < P; ++jj) s += parts[threadIdx.x * P + jj];
+      const float t = sts_temp ? sts_temp[kt] : 1.0f;
+      const float c = 1.0f / (1.0f + expf(-(s / t)));
+      conf[(size_t)m * gamma + kt] = c;
+      cval[threadIdx.x] = c;
     }
     __syncthreads();
     if (surv && threadIdx.x == 0) {
-      for (int kk = 0; kk < kn; ++kk) {
-        const int k = k0 + kk;
-        a = k == 0 ? cval[kk] : a * cval[kk];
-        surv[(size_t)m * gamma + k] = a;
+      const int kn = min(G, gamma - k0);
+      for (int q = 0; q < kn; ++q) {
+        const int kt = k0 + q;
+        a = kt == 0 ? cval[q] : a * cval[q];
+        surv[(size_t)m * gamma + kt] = a;
       }
     }
     __syncthreads();
@@ -148,9 +164,11 @@ dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const int vec_h = (d % 8 == 0) && a16(h) && a16(w_conf);
   const int vec_e = (r % 8 == 0) && (d % 4 == 0) && a16(W1) && a16(w_conf);
-  const int waves = gamma < 16 ? gamma : 16;
-  hipLaunchKernelGGL(confidence_kernel, dim3(R), dim3(64 * waves), 0, stream, h, W1, anchors,
-                     tokens, w_conf, sts_temp, gamma, d, V, r, vec_h, vec_e, conf, surv);
+  // P wavefronts per position, G positions per round, at most 16 wavefronts.
+  const int P = gamma < 16 ? 16 / gamma : 1;
+  const int G = gamma < 16 ? gamma : 16;
+  hipLaunchKernelGGL(confidence_kernel, dim3(R), dim3(64 * P * G), 0, stream, h, W1, anchors,
+                     tokens, w_conf, sts_temp, gamma, d, V, r, P, vec_h, vec_e, conf, surv);
   return check_launch("confidence_kernel");
 }
 
