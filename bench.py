@@ -174,7 +174,60 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_dispatch": n * 4, "dispatches": 3}), flush=True)
         return
+    stream = torch.cuda.current_stream()
+
+    def warm(fn, ms=40.0):
+        """Run fn until about `ms` of GPU work has passed (sustained clocks)."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+
+    def scheduler_only(calls=30):
+        """dspark_survival + dspark_schedule on the scheduler stress workload (R = 8192,
+        gamma = 7, SPS over B = 1..65536): microseconds per call from HIP events."""
+        sw = make_workload(CONFIGS["sched_stress"])
+        sc = torch.from_numpy(sw["conf"]).to(dev)
+        ssps = torch.from_numpy(sw["sps"]).to(dev)
+        sR, sg = sw["conf"].shape
+        ssurv = torch.empty_like(sc)
+        slen = torch.empty((sR,), dtype=torch.int32, device=dev)
+        sws = torch.empty(D.dspark_schedule_workspace(sR, sg), dtype=torch.uint8, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+
+        def one():
+            D.dspark_survival(sc, surv=ssurv, stream=stream)
+            D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws, stream=stream)
+        warm(one, 20.0)
+        us = []
+        for b, e in evs:
+            b.record(stream)
+            one()
+            e.record(stream)
+            torch.cuda.synchronize()
+            us.append(b.elapsed_time(e) * 1e3)
+        nbytes = sR * sg * 4 * 2 + sw["sps"].nbytes + sR * 4
+        p10, p50, p90 = (float(x) for x in np.percentile(us, [10, 50, 90]))
+        return {"workload": f"sched_stress: R={sR}, gamma={sg}, B_max={sw['B_max']}",
+                "us_per_call_p10_p50_p90": [round(p10, 1), round(p50, 1), round(p90, 1)],
+                "algorithmic_bytes": int(nbytes),
+                "achieved_GBps_at_p50": round(nbytes / (p50 / 1e6) / 1e9, 2),
+                "bound": "latency (launches: 1 survival + 12 schedule)"}
+
     cfg = CONFIGS[args.config]
+    if cfg.beta_means is not None:
+        # Scheduler-only workload: survival + schedule per call.
+        res = scheduler_only(calls=args.steps)
+        p50 = res["us_per_call_p10_p50_p90"][1]
+        print(json.dumps({"metric": "schedule latency (survival + schedule) per call",
+                          "value": p50, "unit": "us", "n_gpus": 1, "steps": args.steps,
+                          "warmup": "20 ms", "higher_is_better": False, "dtype": "f32/u64",
+                          "data": "synthetic", "config": {"workload": res["workload"]},
+                          "scheduler": res}), flush=True)
+        return
     wl = make_workload(cfg)
     R, g, V = wl["base"].shape
     r = wl["W1"].shape[1]
@@ -201,16 +254,6 @@ def main():
     lengths = torch.empty((R,), dtype=torch.int32, device=dev)
     ws_d = torch.empty(D.dspark_markov_draft_workspace(R, g, V, r), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(D.dspark_schedule_workspace(R, g), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def warm(fn, ms=40.0):
-        """Run fn until about `ms` of GPU work has passed (sustained clocks)."""
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        while (time.perf_counter() - t0) * 1e3 < ms:
-            for _ in range(4):
-                fn()
-            torch.cuda.synchronize()
 
     def run(layout, steps, warmup, ev_steps=50):
         """Time `steps` whole steps; return (ms per step, fused-step launch durations in ms).
@@ -366,38 +409,6 @@ def main():
                 "launch_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(kd, [10, 50, 90])],
                 "frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                 "data": "synthetic, drawn on the device (seeded torch generator)"}
-
-    def scheduler_only(calls=30):
-        """dspark_survival + dspark_schedule on the scheduler stress workload (R = 8192,
-        gamma = 7, SPS over B = 1..65536): microseconds per call from HIP events."""
-        sw = make_workload(CONFIGS["sched_stress"])
-        sc = torch.from_numpy(sw["conf"]).to(dev)
-        ssps = torch.from_numpy(sw["sps"]).to(dev)
-        sR, sg = sw["conf"].shape
-        ssurv = torch.empty_like(sc)
-        slen = torch.empty((sR,), dtype=torch.int32, device=dev)
-        sws = torch.empty(D.dspark_schedule_workspace(sR, sg), dtype=torch.uint8, device=dev)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(calls)]
-
-        def one():
-            D.dspark_survival(sc, surv=ssurv, stream=stream)
-            D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws, stream=stream)
-        warm(one, 20.0)
-        us = []
-        for b, e in evs:
-            b.record(stream)
-            one()
-            e.record(stream)
-            torch.cuda.synchronize()
-            us.append(b.elapsed_time(e) * 1e3)
-        nbytes = sR * sg * 4 * 2 + sw["sps"].nbytes + sR * 4
-        p10, p50, p90 = (float(x) for x in np.percentile(us, [10, 50, 90]))
-        return {"workload": f"sched_stress: R={sR}, gamma={sg}, B_max={sw['B_max']}",
-                "us_per_call_p10_p50_p90": [round(p10, 1), round(p50, 1), round(p90, 1)],
-                "algorithmic_bytes": int(nbytes),
-                "achieved_GBps_at_p50": round(nbytes / (p50 / 1e6) / 1e9, 2),
-                "bound": "latency (launches: 1 survival + 12 schedule)"}
 
     def hbm_measured(nbytes=1 << 31, reps=5):
         """Large-copy bandwidth (read + write bytes over time) of torch's device copy:
