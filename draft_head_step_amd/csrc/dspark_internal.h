@@ -21,11 +21,12 @@ struct MarkovPlan {
   int rk;          // compiled rank bucket (64, 128, 256, 512)
   int nw;          // waves per workgroup (32 requests per wave, or per wave pair if ksplit)
   bool ksplit;     // rank-512 K-split pairs
-  int n_rblocks;   // ceil(R / (32 * nw))
+  int tw;          // 32-request tiles per wave (plain kernel; 2 shares each LDS read)
+  int n_rblocks;   // ceil(R / (32 * nw * tw))
   int n_chunks;    // ceil(V / 32): 32-column chunks of V
   int n_vgroups;   // groups of consecutive chunks, one per workgroup (per R block)
   int cpg;         // chunks per group
-  size_t ws_bytes; // partial (max, argmax) pairs: R * 2 * max groups * 8 bytes
+  size_t ws_bytes; // packed per-step results: gamma * R * 16 words of 8 bytes
 };
 
 // for_launch = false: only the static parts (buckets, workspace); no device queries.

@@ -401,7 +401,7 @@ constexpr int plain_unroll() { return lcm_small(plain_wd<RK, NW>(), plain_pd<RK,
 template <int RK>
 constexpr int plain_max_waves() { return RK == 512 ? 2 : 8; }
 
-template <int RK, int NW, int MODE, bool VEC4, bool BIAS>
+template <int RK, int NW, int MODE, bool VEC4, bool BIAS, int TW>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
@@ -411,7 +411,7 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int KS = RK / 16;
   constexpr int NT = NW * 64;
-  constexpr int ROWS = NW * 32;
+  constexpr int ROWS = NW * 32 * TW;
   constexpr int PMAX = (kChunk * (RK / 8) + NT - 1) / NT;
   constexpr int PITCH = RK + 8;
   constexpr int BUF = kChunk * PITCH;
@@ -421,6 +421,7 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   constexpr int UNR = plain_unroll<RK, NW>();
   constexpr bool DMA = RK == 512;                  // W2 staged by direct loads into LDS
   constexpr int NBUF = DMA ? WD + 1 : 2;           // LDS stage buffers
+  static_assert(TW == 1 || !DMA, "two tiles per wave only with register staging");
   // vmcnt at the top of an iteration that leaves only the loads issued after
   // the DMA of its own chunk outstanding (0 with bias stores in flight).
   constexpr int EL = epi_load_count<MODE, VEC4, 4>();
@@ -447,16 +448,23 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   auto chunk = [&](int i) { return c0 + min(i, n_valid - 1) * cstep; };
   uint16_t* lds = reinterpret_cast<uint16_t*>(smem);
 
-  const int m_loc = wave * 32 + col;
-  const int m = rb * ROWS + m_loc;
-  const bool m_ok = m < R;
-  bf16x8 e[KS];
-  {
-    int x = step_input(io, m, m_ok, vg == 0 && half == 0, V);
+  // Tile t of this wave holds requests (wave * TW + t) * 32 + col of the R block.
+  int m[TW];
+  bool m_ok[TW];
+  uint32_t e_off[TW];
+  bf16x8 e[TW][KS];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int m_loc = (wave * TW + t) * 32 + col;
+    m[t] = rb * ROWS + m_loc;
+    m_ok[t] = m[t] < R;
+    e_off[t] = (uint32_t)(m_loc * ad.row_stride + 4 * half) * 4u;
+    int x = step_input(io, m[t], m_ok[t], vg == 0 && half == 0, V);
     x = min(max(x, 0), V - 1);                          // out-of-range ids never fault
     const uint16_t* er = W1 + (size_t)x * r + half * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) e[s] = (s * 16 < r && m_ok) ? ld_bf16x8(er + s * 16) : bf16x8{};
+    for (int s = 0; s < KS; ++s)
+      e[t][s] = (s * 16 < r && m_ok[t]) ? ld_bf16x8(er + s * 16) : bf16x8{};
   }
 
   const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
@@ -464,33 +472,36 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   const uint32_t w2_off = DMA ? w2_dma_lane_offset(lane, r) : w2_lane_offset<RK, NT>(tid, r);
   const Rsrc rbase = MODE == kBiasOnly ? make_rsrc(W2, 0u) : block_rsrc(base, ad, rb, ROWS);
   const Rsrc runif = MODE == DSPARK_SAMPLE ? block_rsrc(unif, ad, rb, ROWS) : rbase;
-  const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 4 * half) * 4u;
   const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
 
   u32x4 stage[DMA ? 1 : WD][DMA ? 1 : PMAX];
-  float eb[NS][16];
-  float eu[NS][16];
-  f32x16 accs[2];
-  Argmax am;
+  float eb[NS][TW][16];
+  float eu[NS][TW][16];
+  f32x16 accs[2][TW];
+  Argmax am[TW];
   static_assert(UNR % 2 == 0 && UNR % NS == 0, "the unroll must cycle the rings");
 
   // Fused bias-add + select of iteration i.  Rows past R are never written, so
   // they need no mask.
-  auto finish = [&](auto masked, int i, const f32x16& acc, const float (&cb)[16],
-                    const float (&cu)[16]) {
+  auto finish = [&](auto masked, int i, const f32x16 (&acc)[TW], const float (&cb)[TW][16],
+                    const float (&cu)[TW][16]) {
     constexpr bool MASKED = decltype(masked)::value;
     const int cv = (c0 + i * cstep) * kChunk;
     const int vlim = i < n_valid ? V : 0;
-    float av[16];
 #pragma unroll
-    for (int qq = 0; qq < 16; ++qq) av[qq] = acc[qq];
-    select_chunk<MODE, 16, MASKED>(am, cb, av, cu, kscale, i, vlim - cv - 4 * half);
-    if (BIAS && m_ok) {
-      float* oc = bias_out + ad.k_off + (size_t)m * ad.row_stride + (size_t)chunk(i) * ad.cstride;
+    for (int t = 0; t < TW; ++t) {
+      float av[16];
 #pragma unroll
-      for (int qq = 0; qq < 16; ++qq) {
-        const int o = 8 * (qq >> 2) + 4 * half + (qq & 3);
-        if (cv + o < vlim) oc[o] = acc[qq];
+      for (int qq = 0; qq < 16; ++qq) av[qq] = acc[t][qq];
+      select_chunk<MODE, 16, MASKED>(am[t], cb[t], av, cu[t], kscale, i, vlim - cv - 4 * half);
+      if (BIAS && m_ok[t]) {
+        float* oc =
+            bias_out + ad.k_off + (size_t)m[t] * ad.row_stride + (size_t)chunk(i) * ad.cstride;
+#pragma unroll
+        for (int qq = 0; qq < 16; ++qq) {
+          const int o = 8 * (qq >> 2) + 4 * half + (qq & 3);
+          if (cv + o < vlim) oc[o] = acc[t][qq];
+        }
       }
     }
   };
@@ -499,8 +510,8 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   // iteration i-1 from the other beside them (the select does not wait for this
   // chunk's MFMAs), then refill the epilogue slot it freed with iteration i + PD.
   // Iteration i's epilogue inputs live in slot i % NS.
-  auto body = [&](auto masked, auto first, int i, auto& st, f32x16& acc, const f32x16& pacc,
-                  float (&pb)[16], float (&pu)[16]) {
+  auto body = [&](auto masked, auto first, int i, auto& st, f32x16 (&acc)[TW],
+                  const f32x16 (&pacc)[TW], float (&pb)[TW][16], float (&pu)[TW][16]) {
     const int b = NBUF == 2 ? (i & 1) : i % NBUF;
     if constexpr (DMA) {
       // This wave's rows of chunk i have landed; the barrier publishes all rows.
@@ -517,8 +528,10 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
 
     // Bias tile: 32 vocabulary rows x 32 requests over the compiled K = RK
     // (steps past r multiply zero-filled LDS columns by zero registers).
+    // With two tiles per wave each A read feeds two MFMAs.
     const uint16_t* abase = lds + b * BUF + col * PITCH + half * 8;
-    acc = f32x16{};
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[t] = f32x16{};
 #pragma unroll
     for (int s0 = 0; s0 < KS; s0 += 4) {
       bf16x8 a[4];
@@ -526,14 +539,18 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
       for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(abase + (s0 + i) * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], e[s0 + i], acc, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], e[t][s0 + i], acc[t], 0, 0, 0);
     }
     if (!decltype(first)::value || i >= 1) finish(masked, i - 1, pacc, pb, pu);
     // Rank 512: LDS reads run kLdsAhead K-steps ahead of the MFMAs, and the
     // previous chunk's select fills the issue slots between them (measured
     // slower at rank 256, where the compiler's own order wins).
     if constexpr (RK == 512) mfma_pipeline<KS>();
-    epi_load<MODE, VEC4, 4>(pb, pu, rbase, runif, e_off + (uint32_t)chunk(i + PD) * e_cb);
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+      epi_load<MODE, VEC4, 4>(pb[t], pu[t], rbase, runif, e_off[t] + (uint32_t)chunk(i + PD) * e_cb);
     // Keep each chunk's arithmetic in its own iteration: hoisting the noise of
     // a prefetched chunk next to its load would wait for that load.
     __builtin_amdgcn_sched_barrier(0);
@@ -547,7 +564,12 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
       if constexpr (DMA) w2_dma<NW>(lds + t * BUF, dw2, w2_off, chunk(t), r, wave);
       else w2_load<RK, NT, PMAX>(stage[t % (DMA ? 1 : WD)], rw2, w2_off, chunk(t), r);
     }
-    if (t < PD) epi_load<MODE, VEC4, 4>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb);
+    if (t < PD) {
+#pragma unroll
+      for (int u = 0; u < TW; ++u)
+        epi_load<MODE, VEC4, 4>(eb[t][u], eu[t][u], rbase, runif,
+                                e_off[u] + (uint32_t)chunk(t) * e_cb);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   // The first UNR iterations (the first has nothing to finish) and those from
@@ -576,13 +598,16 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   if constexpr (DMA) wait_vmcnt<0>();   // no direct load lands in LDS after exit
 
   // Lanes l and l^32 hold the same request: merge, then one lane publishes.
-  float best = am.best;
-  int best_i = argmax_id(am, c0, cstep, 4 * half);
-  const float ov = __shfl_xor(best, 32);
-  const int oi = __shfl_xor(best_i, 32);
-  merge_best(best, best_i, ov, oi);
-  if (m_ok && half == 0)
-    atomicMax(io.best + (size_t)m * io.sub + (vg & (io.sub - 1)), pack_best(best, best_i));
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    float best = am[t].best;
+    int best_i = argmax_id(am[t], c0, cstep, 4 * half);
+    const float ov = __shfl_xor(best, 32);
+    const int oi = __shfl_xor(best_i, 32);
+    merge_best(best, best_i, ov, oi);
+    if (m_ok[t] && half == 0)
+      atomicMax(io.best + (size_t)m[t] * io.sub + (vg & (io.sub - 1)), pack_best(best, best_i));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -823,10 +848,10 @@ struct StepVariant {
   int unroll;   // chunks per group must be a multiple of this
 };
 
-template <int RK, int NW, int MODE, bool VEC4, bool BIAS>
+template <int RK, int NW, int MODE, bool VEC4, bool BIAS, int TW = 1>
 StepVariant plain_variant() {
-  return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS>, NW * 64,
-          (size_t)(RK == 512 ? plain_wd<RK, NW>() + 1 : 2) * kChunk * (RK + 8) * 2, NW * 32,
+  return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS, TW>, NW * 64,
+          (size_t)(RK == 512 ? plain_wd<RK, NW>() + 1 : 2) * kChunk * (RK + 8) * 2, NW * 32 * TW,
           plain_unroll<RK, NW>()};
 }
 template <int NP, int MODE, bool VEC4, bool BIAS>
@@ -836,7 +861,14 @@ StepVariant ksplit_variant() {
 }
 
 template <int RK, int MODE, bool VEC4, bool BIAS>
-StepVariant plain_by_nw(int nw) {
+StepVariant plain_by_nw(int nw, int tw) {
+  // Two tiles per wave: bias-only GEMM at ranks 128 and 256, 4 or 8 waves, no
+  // bias output (the only combinations built; with the logits streams as well
+  // the registers spill).
+  if constexpr ((RK == 128 || RK == 256) && !BIAS && MODE == kBiasOnly) {
+    if (tw == 2) return nw == 8 ? plain_variant<RK, 8, MODE, VEC4, BIAS, 2>()
+                                : plain_variant<RK, 4, MODE, VEC4, BIAS, 2>();
+  }
   switch (nw) {
     case 1: return plain_variant<RK, 1, MODE, VEC4, BIAS>();
     case 2: return plain_variant<RK, 2, MODE, VEC4, BIAS>();
@@ -854,10 +886,10 @@ StepVariant pick3(const MarkovPlan& p) {
     }
   }
   switch (p.rk) {
-    case 64: return plain_by_nw<64, MODE, VEC4, BIAS>(p.nw);
-    case 128: return plain_by_nw<128, MODE, VEC4, BIAS>(p.nw);
-    case 256: return plain_by_nw<256, MODE, VEC4, BIAS>(p.nw);
-    default: return plain_by_nw<512, MODE, VEC4, BIAS>(p.nw);
+    case 64: return plain_by_nw<64, MODE, VEC4, BIAS>(p.nw, p.tw);
+    case 128: return plain_by_nw<128, MODE, VEC4, BIAS>(p.nw, p.tw);
+    case 256: return plain_by_nw<256, MODE, VEC4, BIAS>(p.nw, p.tw);
+    default: return plain_by_nw<512, MODE, VEC4, BIAS>(p.nw, p.tw);
   }
 }
 template <int MODE>
@@ -926,7 +958,15 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
   const int nw_env = env_int("DSPARK_MARKOV_NW", 0);
   if (!p.ksplit && (nw_env == 1 || nw_env == 2 || nw_env == 4 || nw_env == 8)) nw = nw_env;
   p.nw = nw;
-  const int rows = p.ksplit ? nw / 2 * 32 : nw * 32;
+  // Two tiles per wave halve the LDS reads per MFMA: the bias-only GEMM at
+  // ranks 128-256 (DSPARK_MARKOV_TW=1 turns it off).  With bias output the
+  // table has no such variant; the launch then falls back to one tile and
+  // recomputes the R blocks from the variant's rows.
+  const int tw_env = env_int("DSPARK_MARKOV_TW", 0);
+  p.tw = (tw_env == 1 || tw_env == 2) ? tw_env : (mode == kBiasOnly ? 2 : 1);
+  if (p.ksplit || (p.rk != 128 && p.rk != 256) || (nw != 4 && nw != 8) || mode != kBiasOnly)
+    p.tw = 1;
+  const int rows = p.ksplit ? nw / 2 * 32 : nw * 32 * p.tw;
   p.n_rblocks = (R + rows - 1) / rows;
   p.n_chunks = (V + kChunk - 1) / kChunk;
   // packed per-step results [gamma][R][S], sized for the largest S
@@ -940,14 +980,15 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
                                   const float* uniforms, int32_t* tokens, float* bias_out,
                                   void* workspace, const dspark_step_events* events,
                                   hipStream_t stream) {
-  MarkovPlan p = plan_markov(R, gamma, V, r, mode, true);
+  // No base logits: greedy on the Markov bias alone.
+  const int kmode = base ? mode : kBiasOnly;
+  MarkovPlan p = plan_markov(R, gamma, V, r, kmode, true);
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const bool tiled = layout == DSPARK_LAYOUT_TILED;
   const bool vec4 = (tiled || V % 4 == 0) && V >= 4 && a16(base) &&
                     (!uniforms || a16(uniforms)) && (!bias_out || a16(bias_out));
-  // No base logits: greedy on the Markov bias alone.
-  const int kmode = base ? mode : kBiasOnly;
   const StepVariant var = pick_variant(p, kmode, vec4, bias_out != nullptr);
+  p.n_rblocks = (R + var.rows - 1) / var.rows;   // the variant's requests per workgroup
   const int bpc = prepare_variant(var);
   if (bpc < 0) return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the Markov step kernel");
 

@@ -303,6 +303,33 @@ def test_bias_only_small(R, g, V, r):
     _bias_only_case(make_workload(cfg))
 
 
+@pytest.mark.parametrize("R,g,V,r", [(130, 3, 3000, 256), (600, 2, 5000, 128),
+                                     (1024, 2, 20000, 256)])
+def test_bias_only_two_tiles_per_wave(R, g, V, r):
+    # No bias output, ranks 128-256, >= 128 requests: each wave carries two
+    # 32-request tiles (one partial R block, two blocks with a partial second,
+    # full blocks).
+    _say(f"case bias-only two tiles R={R} g={g} V={V} r={r}")
+    cfg = Config("edge", R=R, gamma=g, V=V, r=r, d=16, mode=GREEDY, temperature=1.0, w_std=0.3,
+                 base_std=1.0, wconf_std=0.1, seed=700 + R)
+    _bias_only_case(make_workload(cfg), bias=False)
+
+
+def test_bias_only_long_block_shape():
+    # R = 1024, r = 256, V = 129280 (two of the 16 positions), sampled rows.
+    _say("case bias-only at R=1024, V=129280, r=256")
+    from draft_head_step_amd.inputs import make_head
+    hd = make_head(CONFIGS["long_block"])
+    R, V, gm = hd["R"], hd["V"], 2
+    wl = {"W1": hd["W1"], "W2": hd["W2"], "anchors": hd["anchors"], "mode": GREEDY,
+          "temperature": 1.0, "uniforms": None,
+          "base": np.zeros((R, gm, V), np.float32)}   # pages touched only for sampled rows
+    g = H.to_device({k: wl[k] for k in ("W1", "W2", "anchors")}, DEV)
+    tok = D.dspark_markov_draft(g["W1"], g["W2"], None, g["anchors"], GREEDY, gamma=gm)
+    torch.cuda.synchronize()
+    H.check_draft(wl, tok.cpu().numpy(), rows=_sample_rows(R, 16, 6))
+
+
 def test_bias_only_dsv4_shape():
     _say("case bias-only at R=256, V=129280, r=512")
     cfg = dataclasses.replace(CONFIGS["dsv4"], mode=GREEDY, w_std=0.05)
