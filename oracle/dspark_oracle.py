@@ -225,6 +225,66 @@ def schedule(surv: np.ndarray, sps: np.ndarray):
             "theta": float(theta[m_star]), "theta_all": theta}
 
 
+def _tau_fx_prefix(a: np.ndarray, order: np.ndarray, m: int) -> int:
+    """R * 2^40 + sum of the fixed-point survivals of the first m sorted candidates."""
+    R = a.shape[0]
+    q = np.rint(a.reshape(-1).astype(np.float64) * TAU_SCALE).astype(np.uint64)
+    return int(R) * (1 << TAU_FRAC_BITS) + int(np.sum(q[order[:m]], dtype=np.uint64))
+
+
+def _result(a: np.ndarray, order: np.ndarray, m: int, theta: float):
+    R, g = a.shape
+    tau_fx = _tau_fx_prefix(a, order, m)
+    lengths = np.bincount(order[:m] // g, minlength=R).astype(np.int32)
+    return {"lengths": lengths, "order": order, "m_star": m, "B_star": R + m,
+            "tau_fx": tau_fx, "tau": float(np.float64(tau_fx) * (1.0 / TAU_SCALE)),
+            "theta": theta}
+
+
+def schedule_early_stop(surv: np.ndarray, sps: np.ndarray):
+    """The greedy scheduler with its early-stop break ([P1] §二 设计二, greedy steps
+    3-5; [P3] part 01, the theoretical version): admit candidates one at a time in
+    the sorted order, look Theta up after each admission, and stop as soon as Theta
+    no longer increases (Theta_m <= Theta_{m-1}: the m-th candidate is not
+    admitted).  Theta_m is computed exactly as in schedule().  Sequential on purpose."""
+    a = np.asarray(surv, dtype=np.float32)
+    R, g = a.shape
+    N = R * g
+    sps = np.asarray(sps, dtype=np.float32)
+    if sps.size < R * (1 + g):
+        raise ValueError("SPS table must cover B up to R * (1 + gamma)")
+    order = candidate_order(a)
+    flat = a.reshape(-1)
+    tau_fx = int(R) * (1 << TAU_FRAC_BITS)
+
+    def theta_of(fx, m):
+        return float(np.float64(fx) * (1.0 / TAU_SCALE)) * float(np.float64(sps[R + m - 1]))
+
+    best = theta_of(tau_fx, 0)
+    m = 0
+    while m < N:
+        fx = tau_fx + int(np.rint(np.float64(flat[order[m]]) * TAU_SCALE))
+        th = theta_of(fx, m + 1)
+        if not th > best:
+            break
+        tau_fx, best, m = fx, th, m + 1
+    return _result(a, order, m, best)
+
+
+def schedule_capacity(surv: np.ndarray, capacity: int):
+    """Capacity-K schedule ([P1] §三 挑战1; [P3] part 01, the asynchronous
+    production form): a verification batch of `capacity` tokens, predicted two
+    steps earlier, is filled with the anchors plus the top candidates by current
+    survival: m* = clamp(K - R, 0, R * gamma) in the sorted order of schedule().
+    There is no SPS table here; Theta is reported as tau*."""
+    a = np.asarray(surv, dtype=np.float32)
+    R, g = a.shape
+    order = candidate_order(a)
+    m = min(max(int(capacity) - R, 0), R * g)
+    tau = float(np.float64(_tau_fx_prefix(a, order, m)) * (1.0 / TAU_SCALE))
+    return _result(a, order, m, tau)
+
+
 def run_path(wl: dict, rows=None):
     """Draft -> confidence -> survival -> schedule for one workload (the whole hot path)."""
     dr = markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"], wl["mode"],
