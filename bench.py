@@ -186,8 +186,10 @@ def main():
             torch.cuda.synchronize()
 
     def scheduler_only(calls=30):
-        """dspark_survival + dspark_schedule on the scheduler stress workload (R = 8192,
-        gamma = 7, SPS over B = 1..65536): microseconds per call from HIP events."""
+        """dspark_survival + the schedule on the scheduler stress workload (R = 8192,
+        gamma = 7, SPS over B = 1..65536): microseconds per call from HIP events, for
+        the global search (dspark_schedule) and for dspark_schedule_ex's early-stop
+        and capacity rules (capacity: half of the candidates)."""
         sw = make_workload(CONFIGS["sched_stress"])
         sc = torch.from_numpy(sw["conf"]).to(dev)
         ssps = torch.from_numpy(sw["sps"]).to(dev)
@@ -195,26 +197,39 @@ def main():
         ssurv = torch.empty_like(sc)
         slen = torch.empty((sR,), dtype=torch.int32, device=dev)
         sws = torch.empty(D.dspark_schedule_workspace(sR, sg), dtype=torch.uint8, device=dev)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(calls)]
+        cap = sR + sR * sg // 2
 
-        def one():
-            D.dspark_survival(sc, surv=ssurv, stream=stream)
-            D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws, stream=stream)
-        warm(one, 20.0)
-        us = []
-        for b, e in evs:
-            b.record(stream)
-            one()
-            e.record(stream)
-            torch.cuda.synchronize()
-            us.append(b.elapsed_time(e) * 1e3)
+        def timed(sched):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(calls)]
+
+            def one():
+                D.dspark_survival(sc, surv=ssurv, stream=stream)
+                sched()
+            warm(one, 20.0)
+            us = []
+            for b, e in evs:
+                b.record(stream)
+                one()
+                e.record(stream)
+                torch.cuda.synchronize()
+                us.append(b.elapsed_time(e) * 1e3)
+            return [round(float(x), 1) for x in np.percentile(us, [10, 50, 90])]
+
+        glob = timed(lambda: D.dspark_schedule(ssurv, ssps, lengths=slen, workspace=sws,
+                                               stream=stream))
+        early = timed(lambda: D.dspark_schedule_ex(ssurv, ssps, mode=D.SCHED_EARLY_STOP,
+                                                   lengths=slen, workspace=sws, stream=stream))
+        capy = timed(lambda: D.dspark_schedule_ex(ssurv, None, mode=D.SCHED_CAPACITY,
+                                                  capacity=cap, lengths=slen, workspace=sws,
+                                                  stream=stream))
         nbytes = sR * sg * 4 * 2 + sw["sps"].nbytes + sR * 4
-        p10, p50, p90 = (float(x) for x in np.percentile(us, [10, 50, 90]))
         return {"workload": f"sched_stress: R={sR}, gamma={sg}, B_max={sw['B_max']}",
-                "us_per_call_p10_p50_p90": [round(p10, 1), round(p50, 1), round(p90, 1)],
+                "us_per_call_p10_p50_p90": glob,
+                "early_stop_us_p10_p50_p90": early,
+                "capacity_us_p10_p50_p90": capy, "capacity_K": cap,
                 "algorithmic_bytes": int(nbytes),
-                "achieved_GBps_at_p50": round(nbytes / (p50 / 1e6) / 1e9, 2),
+                "achieved_GBps_at_p50": round(nbytes / (glob[1] / 1e6) / 1e9, 2),
                 "bound": "latency (launches: 1 survival + 12 schedule)"}
 
     cfg = CONFIGS[args.config]

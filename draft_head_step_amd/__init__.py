@@ -9,7 +9,7 @@ raises: there is no fallback path.
 
 Entry points (same names as the C ABI):
   dspark_markov_draft, dspark_confidence, dspark_survival, dspark_schedule,
-  dspark_markov_draft_workspace, dspark_schedule_workspace.
+  dspark_schedule_ex, dspark_markov_draft_workspace, dspark_schedule_workspace.
 """
 from __future__ import annotations
 
@@ -20,13 +20,17 @@ from typing import Optional
 __all__ = [
     "DsparkError", "GREEDY", "SAMPLE", "LAYOUT_RGV", "LAYOUT_TILED", "lib", "lib_path",
     "dspark_markov_draft", "dspark_confidence", "dspark_survival", "dspark_schedule",
-    "dspark_markov_draft_workspace", "dspark_schedule_workspace", "ScheduleInfo",
+    "dspark_schedule_ex", "dspark_markov_draft_workspace", "dspark_schedule_workspace",
+    "ScheduleInfo", "SCHED_GLOBAL", "SCHED_EARLY_STOP", "SCHED_CAPACITY",
 ]
 
 GREEDY = 0
 SAMPLE = 1
 LAYOUT_RGV = 0     # base / uniforms / bias_out as [R, gamma, V]
 LAYOUT_TILED = 1   # [gamma, ceil(V/32), R, 32]
+SCHED_GLOBAL = 0       # dspark_schedule_ex admission rules
+SCHED_EARLY_STOP = 1
+SCHED_CAPACITY = 2
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -88,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.dspark_schedule_workspace.restype = sz
     L.dspark_schedule.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.dspark_schedule.restype = i32
+    L.dspark_schedule_ex.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    L.dspark_schedule_ex.restype = i32
     _LIB = L
     return L
 
@@ -255,6 +261,41 @@ def dspark_schedule(surv, sps, lengths=None, order=None, want_order: bool = Fals
                            _ptr(order), _ptr(info), _ptr(workspace), workspace.numel(),
                            _stream(stream))
     _check(st, "dspark_schedule")
+    return lengths, order, info
+
+
+def dspark_schedule_ex(surv, sps=None, mode: int = SCHED_GLOBAL, capacity: int = 0,
+                       lengths=None, order=None, want_order: bool = False, info=None,
+                       want_info: bool = False, workspace=None, stream=None):
+    """Prefix scheduler with a choice of admission rule (SCHED_GLOBAL,
+    SCHED_EARLY_STOP, SCHED_CAPACITY with `capacity` = predicted batch tokens;
+    sps may be None for SCHED_CAPACITY).  Returns (lengths, order or None, info
+    or None) like dspark_schedule."""
+    torch = _torch()
+    L = lib()
+    R, gamma = surv.shape
+    dev = surv.device
+    _need(surv, "surv", (torch.float32,), (R, gamma), dev)
+    if sps is not None and (sps.dim() != 1 or sps.dtype != torch.float32 or sps.device != dev
+                            or not sps.is_contiguous()):
+        raise ValueError("sps must be a contiguous 1-D float32 tensor on the same device")
+    if lengths is None:
+        lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+    _need(lengths, "lengths", (torch.int32,), (R,), dev)
+    if order is None and want_order:
+        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
+    if order is not None:
+        _need(order, "order", (torch.int32,), (R * gamma,), dev)
+    if info is None and want_info:
+        info = torch.zeros((32,), dtype=torch.uint8, device=dev)
+    need = int(L.dspark_schedule_workspace(R, gamma))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = L.dspark_schedule_ex(_ptr(surv), _ptr(sps), R, gamma,
+                              0 if sps is None else sps.numel(), int(mode), int(capacity),
+                              _ptr(lengths), _ptr(order), _ptr(info), _ptr(workspace),
+                              workspace.numel(), _stream(stream))
+    _check(st, "dspark_schedule_ex")
     return lengths, order, info
 
 

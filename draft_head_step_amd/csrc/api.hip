@@ -148,7 +148,37 @@ dspark_status dspark_schedule(const float* surv, const float* sps, int R, int ga
   if (!workspace || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "schedule: workspace needs %zu bytes (got %zu)", need,
                 workspace ? ws_bytes : (size_t)0);
-  return dspark::launch_schedule(surv, sps, R, gamma, lengths, order, info, workspace,
+  return dspark::launch_schedule(surv, sps, R, gamma, 0, 0, lengths, order, info, workspace,
+                                 reinterpret_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_schedule_ex(const float* surv, const float* sps, int R, int gamma, int B_max,
+                                 int mode, int capacity, int32_t* lengths, int32_t* order,
+                                 dspark_schedule_info* info, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (mode != DSPARK_SCHED_GLOBAL && mode != DSPARK_SCHED_EARLY_STOP &&
+      mode != DSPARK_SCHED_CAPACITY)
+    return fail(DSPARK_EINVAL, "schedule_ex: unknown mode %d", mode);
+  const bool uses_sps = mode != DSPARK_SCHED_CAPACITY;
+  if (!surv || !lengths || (uses_sps && !sps))
+    return fail(DSPARK_EINVAL, "schedule_ex: NULL required pointer");
+  if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "schedule_ex: sizes must be positive");
+  if (uses_sps && (long long)B_max < (long long)R * (1LL + gamma))
+    return fail(DSPARK_EINVAL, "schedule_ex: B_max %d < R * (1 + gamma)", B_max);
+  if (mode == DSPARK_SCHED_CAPACITY && capacity < 0)
+    return fail(DSPARK_EINVAL, "schedule_ex: negative capacity %d", capacity);
+  if ((long long)R * gamma > DSPARK_MAX_CANDIDATES)
+    return fail(DSPARK_EUNSUPPORTED, "schedule_ex: R * gamma above %d", DSPARK_MAX_CANDIDATES);
+  const size_t need = dspark_schedule_workspace(R, gamma);
+  if (!workspace || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "schedule_ex: workspace needs %zu bytes (got %zu)", need,
+                workspace ? ws_bytes : (size_t)0);
+  const long long n = (long long)R * gamma;
+  long long m_cap = (long long)capacity - R;
+  m_cap = m_cap < 0 ? 0 : m_cap > n ? n : m_cap;
+  return dspark::launch_schedule(surv, uses_sps ? sps : nullptr, R, gamma, mode, (int)m_cap,
+                                 lengths, order, info, workspace,
                                  reinterpret_cast<hipStream_t>(stream));
 }
 

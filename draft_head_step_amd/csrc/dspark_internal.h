@@ -48,8 +48,9 @@ dspark_status launch_survival(const float* conf, int R, int gamma, float* surv, 
 
 // ---- prefix scheduler ----
 size_t schedule_workspace_bytes(int R, int gamma);
-dspark_status launch_schedule(const float* surv, const float* sps, int R, int gamma,
-                              int32_t* lengths, int32_t* order, dspark_schedule_info* info,
-                              void* workspace, hipStream_t stream);
+// mode: 0 global search, 1 early stop, 2 capacity (m_cap = clamp(K - R, 0, R * gamma)).
+dspark_status launch_schedule(const float* surv, const float* sps, int R, int gamma, int mode,
+                              int m_cap, int32_t* lengths, int32_t* order,
+                              dspark_schedule_info* info, void* workspace, hipStream_t stream);
 
 }  // namespace dspark

@@ -185,21 +185,65 @@ __device__ __forceinline__ void block_best(SchedShared& sh, Best& best) {
   for (int j = 1; j < kW; ++j) better(best, Best{sh.bval[j], sh.bidx[j], sh.bsum[j]});
 }
 
+// Block minimum / sum (every thread gets the result; sh's per-wave slots are
+// free again on return).
+__device__ __forceinline__ int block_min_int(SchedShared& sh, int v) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  if (lane == 0) sh.bidx[w] = v;
+  __syncthreads();
+  int r = sh.bidx[0];
+#pragma unroll
+  for (int j = 1; j < kW; ++j) r = min(r, sh.bidx[j]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ unsigned long long block_sum_sh(SchedShared& sh,
+                                                           unsigned long long v) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) sh.wsum[w] = v;
+  __syncthreads();
+  unsigned long long r = 0;
+#pragma unroll
+  for (int j = 0; j < kW; ++j) r += sh.wsum[j];
+  __syncthreads();
+  return r;
+}
+
+// Theta_m with tau from the fixed-point prefix sum S_m (the single definition
+// every mode uses).
+__device__ __forceinline__ double theta_at(int R, unsigned long long S, float sps_b) {
+  return __ull2double_rn(((unsigned long long)R << 40) + S) * kTauInv * (double)sps_b;
+}
+
 // Phase 3 + 4 for a sorted array (keys ck, ids) given in blocked chunks.
 // load(p, ck, id) fetches the element at sorted position p.
+//   mode 0 (global search): first argmax of Theta over every m;
+//   mode 1 (early stop): the first m with Theta_{m+1} <= Theta_m, each element
+//     comparing its Theta with the one before it (tau from S - q, exactly the
+//     value the previous position has); N if Theta keeps rising;
+//   mode 2 (capacity): m = m_cap.
+// Modes 1 and 2 then sum the survivals below m* (tau*) from the sorted keys.
 template <int ITEMS, typename Load, typename SetRank, typename SpsAt>
 __device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restrict__ sps,
-                           int32_t* __restrict__ order, Load load, SetRank set_rank,
-                           SpsAt sps_at, Best& best) {
+                           int mode, int m_cap, int32_t* __restrict__ order, Load load,
+                           SetRank set_rank, SpsAt sps_at, Best& best) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.carry = 0ull;
   best.theta = -1.0;
   best.m = 0x7fffffff;
   best.S = 0ull;
-  if (tid == 0) {
+  if (tid == 0 && mode == 0) {
     best.theta = (double)R * (double)sps[R - 1];  // m = 0: tau = R
     best.m = 0;
   }
+  int brk = 0x7fffffff;
   __syncthreads();
   const unsigned long long rfx = (unsigned long long)R << 40;
   for (int c0 = 0; c0 < N; c0 += kT * ITEMS) {
@@ -228,12 +272,18 @@ __device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restric
       const int p = c0 + tid * ITEMS + i;
       if (p < N) {
         S += q[i];
-        const double tau = __ull2double_rn(rfx + S) * kTauInv;
-        const double th = tau * (double)sps_at(p, i);   // sps[R + p]: budget B = R + p + 1
-        if (th > best.theta) {
-          best.theta = th;
-          best.m = p + 1;
-          best.S = S;
+        if (mode == 0) {
+          const double tau = __ull2double_rn(rfx + S) * kTauInv;
+          const double th = tau * (double)sps_at(p, i);   // sps[R + p]: budget B = R + p + 1
+          if (th > best.theta) {
+            best.theta = th;
+            best.m = p + 1;
+            best.S = S;
+          }
+        } else if (mode == 1) {
+          const double th = theta_at(R, S, sps_at(p, i));
+          const double th_prev = theta_at(R, S - q[i], sps[R + p - 1]);
+          if (!(th > th_prev)) brk = min(brk, p);
         }
         if (order) order[p] = id[i];
       }
@@ -246,7 +296,26 @@ __device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restric
     }
     __syncthreads();
   }
-  block_best(sh, best);
+  if (mode == 0) {
+    block_best(sh, best);
+    return;
+  }
+  int m_star = m_cap;
+  if (mode == 1) {
+    m_star = block_min_int(sh, brk);
+    if (m_star > N) m_star = N;
+  }
+  unsigned long long part = 0;
+  for (int p = tid; p < m_star; p += kT) {
+    uint32_t k;
+    int i;
+    load(p, k, i);
+    part += __double2ull_rn((double)value_of(k) * kTauScale);
+  }
+  const unsigned long long Sm = block_sum_sh(sh, part);
+  best.m = m_star;
+  best.S = Sm;
+  best.theta = theta_at(R, Sm, mode == 1 ? sps[R + m_star - 1] : 1.0f);
 }
 
 __device__ void write_results(int R, int gamma, const Best& best, const int* rank,
@@ -273,7 +342,8 @@ __device__ void write_results(int R, int gamma, const Best& best, const int* ran
 template <int ITEMS>
 __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restrict__ surv,
                                                           const float* __restrict__ sps, int R,
-                                                          int gamma, int N,
+                                                          int gamma, int N, int mode,
+                                                          int m_cap,
                                                           int32_t* __restrict__ lengths,
                                                           int32_t* __restrict__ order,
                                                           dspark_schedule_info* info) {
@@ -302,7 +372,7 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int p = threadIdx.x * ITEMS + i;
-    spv[i] = p < N ? sps[R + p] : 0.0f;
+    spv[i] = (p < N && mode != 2) ? sps[R + p] : 0.0f;
   }
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 8 * pass;
@@ -345,7 +415,8 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
   }
   Best best;
   scan_theta<ITEMS>(
-      sh, N, R, sps, order, [&](int p, uint32_t& k, int& i) { k = skey[p]; i = sid[p]; },
+      sh, N, R, sps, mode, m_cap, order,
+      [&](int p, uint32_t& k, int& i) { k = skey[p]; i = sid[p]; },
       [&](int i, int p) { sid[i] = p; }, [&](int, int i) { return spv[i]; }, best);
   write_results(R, gamma, best, sid, lengths, info);
 }
@@ -671,6 +742,115 @@ __global__ __launch_bounds__(kGT) void sched_tscan_kernel(
   }
 }
 
+// Early stop / capacity over tiles: per tile, the carry, the prefix sums and
+// (early stop) the first position p whose Theta_{p+1} does not exceed
+// Theta_p; writes order.  tbrk[t] = that position or INT_MAX.
+__global__ __launch_bounds__(kGT) void sched_tbreak_kernel(
+    const uint32_t* __restrict__ sk, const int* __restrict__ si, const float* __restrict__ sps,
+    int R, int N, int mode, const unsigned long long* __restrict__ tsum,
+    int32_t* __restrict__ order, int* __restrict__ tbrk) {
+  __shared__ unsigned long long red[kGW];
+  __shared__ int bmin[kGW];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int p0 = t * kGTile + 4 * tid;
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  uint32_t ck[4];
+  int id[4];
+  load4_sorted(sk, si, N, p0, a16(sk) && a16(si), ck, id);
+  if (order) {
+    if (a16(order) && p0 + 3 < N) {
+      *reinterpret_cast<int4*>(order + p0) = make_int4(id[0], id[1], id[2], id[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (p0 + i < N) order[p0 + i] = id[i];
+    }
+  }
+  if (mode != 1) return;   // capacity: order only (uniform per workgroup)
+  unsigned long long c = 0;
+  for (int t2 = tid; t2 < t; t2 += kGT) c += tsum[t2];
+  const unsigned long long carry = block_sum_u64(red, c);
+  __syncthreads();
+  unsigned long long q[4];
+  unsigned long long s4 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[i] = p0 + i < N ? qfx(ck[i]) : 0ull;
+    s4 += q[i];
+  }
+  unsigned long long inc = s4;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  unsigned long long S = carry + inc - s4;
+#pragma unroll
+  for (int j = 0; j < kGW; ++j) S += j < w ? red[j] : 0ull;
+  int brk = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = p0 + i;
+    if (p < N) {
+      S += q[i];
+      const double th = theta_at(R, S, sps[R + p]);
+      const double th_prev = theta_at(R, S - q[i], sps[R + p - 1]);
+      if (!(th > th_prev)) brk = min(brk, p);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) brk = min(brk, __shfl_xor(brk, off));
+  if (lane == 0) bmin[w] = brk;
+  __syncthreads();
+  if (tid == 0) {
+    int b = bmin[0];
+#pragma unroll
+    for (int j = 1; j < kGW; ++j) b = min(b, bmin[j]);
+    tbrk[t] = b;
+  }
+}
+
+// Early stop / capacity: m* (the first break over the tiles, or m_cap), tau*
+// from the tile sums below m*'s tile plus that tile's keys below m*, info,
+// m*; clears lengths for the count.  One workgroup.
+__global__ __launch_bounds__(kT) void sched_pick_ex_kernel(
+    const uint32_t* __restrict__ sk, const unsigned long long* __restrict__ tsum,
+    const int* __restrict__ tbrk, int ntiles, int N, int R, int mode, int m_cap,
+    const float* __restrict__ sps, dspark_schedule_info* info, int* __restrict__ mstar,
+    int32_t* __restrict__ lengths) {
+  __shared__ SchedShared sh;
+  const int tid = threadIdx.x;
+  for (int r = tid; r < R; r += kT) lengths[r] = 0;
+  int m_star = m_cap;
+  if (mode == 1) {
+    int b = 0x7fffffff;
+    for (int t = tid; t < ntiles; t += kT) b = min(b, tbrk[t]);
+    m_star = block_min_int(sh, b);
+    if (m_star > N) m_star = N;
+  }
+  const int t_full = m_star / kGTile;
+  unsigned long long part = 0;
+  for (int t = tid; t < t_full; t += kT) part += tsum[t];
+  for (int p = t_full * kGTile + tid; p < m_star; p += kT) part += qfx(sk[p]);
+  const unsigned long long Sm = block_sum_sh(sh, part);
+  if (tid == 0) {
+    *mstar = m_star;
+    if (info) {
+      const unsigned long long tau_fx = ((unsigned long long)R << 40) + Sm;
+      info->B_star = R + m_star;
+      info->m_star = m_star;
+      info->tau_fx = tau_fx;
+      info->tau = __ull2double_rn(tau_fx) * kTauInv;
+      info->theta = theta_at(R, Sm, mode == 1 ? sps[R + m_star - 1] : 1.0f);
+    }
+  }
+}
+
 // First argmax over m = 0 (tau = R) and the tiles' bests; writes m*, info, and
 // clears lengths for the count.  One workgroup.
 __global__ __launch_bounds__(kT) void sched_pick_kernel(const TileBest* __restrict__ tbest,
@@ -708,8 +888,8 @@ __global__ __launch_bounds__(256) void sched_count_kernel(const int* __restrict_
 }
 
 template <int ITEMS>
-dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, int N,
-                         int32_t* lengths, int32_t* order, dspark_schedule_info* info,
+dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, int N, int mode,
+                         int m_cap, int32_t* lengths, int32_t* order, dspark_schedule_info* info,
                          hipStream_t stream) {
   const size_t lds = sizeof(SchedShared) + (size_t)kT * ITEMS * 8;
   static bool attr = false;
@@ -720,7 +900,7 @@ dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, 
     attr = true;
   }
   hipLaunchKernelGGL(schedule_lds_kernel<ITEMS>, dim3(1), dim3(kT), lds, stream, surv, sps, R,
-                     gamma, N, lengths, order, info);
+                     gamma, N, mode, m_cap, lengths, order, info);
   return check_launch("schedule_lds_kernel");
 }
 
@@ -747,15 +927,18 @@ void launch_scatter(int ntiles, hipStream_t stream, const float* surv, const uin
                      surv, sk, si, dk, di, N, shift, ntiles, hist);
 }
 
-dspark_status launch_schedule(const float* surv, const float* sps, int R, int gamma,
-                              int32_t* lengths, int32_t* order, dspark_schedule_info* info,
-                              void* workspace, hipStream_t stream) {
+dspark_status launch_schedule(const float* surv, const float* sps, int R, int gamma, int mode,
+                              int m_cap, int32_t* lengths, int32_t* order,
+                              dspark_schedule_info* info, void* workspace, hipStream_t stream) {
   const int N = R * gamma;
-  if (N <= kT * 1) return launch_lds<1>(surv, sps, R, gamma, N, lengths, order, info, stream);
-  if (N <= kT * 2) return launch_lds<2>(surv, sps, R, gamma, N, lengths, order, info, stream);
-  if (N <= kT * 4) return launch_lds<4>(surv, sps, R, gamma, N, lengths, order, info, stream);
+#define DSPARK_LDS(I) \
+  launch_lds<I>(surv, sps, R, gamma, N, mode, m_cap, lengths, order, info, stream)
+  if (N <= kT * 1) return DSPARK_LDS(1);
+  if (N <= kT * 2) return DSPARK_LDS(2);
+  if (N <= kT * 4) return DSPARK_LDS(4);
   static_assert(kLdsMaxN == kT * 8, "the largest LDS variant covers kLdsMaxN");
-  if (N <= kT * 8) return launch_lds<8>(surv, sps, R, gamma, N, lengths, order, info, stream);
+  if (N <= kT * 8) return DSPARK_LDS(8);
+#undef DSPARK_LDS
   // Workspace: keys and ids twice (Np each, so every array keeps the base's
   // 16-byte alignment), digit counts (256 x tiles), tile sums, tile bests, m*.
   const int ntiles = (N + kGTile - 1) / kGTile;
@@ -796,10 +979,18 @@ dspark_status launch_schedule(const float* surv, const float* sps, int R, int ga
     if (st != DSPARK_OK) return st;
   }
   hipLaunchKernelGGL(sched_tsum_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, N, tsum);
-  hipLaunchKernelGGL(sched_tscan_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, sps, R, N,
-                     tsum, order, tbest);
-  hipLaunchKernelGGL(sched_pick_kernel, dim3(1), dim3(kT), 0, stream, tbest, ntiles, sps, R, info,
-                     mstar, lengths);
+  if (mode == 0) {
+    hipLaunchKernelGGL(sched_tscan_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, sps, R, N,
+                       tsum, order, tbest);
+    hipLaunchKernelGGL(sched_pick_kernel, dim3(1), dim3(kT), 0, stream, tbest, ntiles, sps, R,
+                       info, mstar, lengths);
+  } else {
+    int* tbrk = reinterpret_cast<int*>(tbest);   // one int per tile in the tile-best area
+    hipLaunchKernelGGL(sched_tbreak_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, sps, R,
+                       N, mode, tsum, order, tbrk);
+    hipLaunchKernelGGL(sched_pick_ex_kernel, dim3(1), dim3(kT), 0, stream, k0, tsum, tbrk,
+                       ntiles, N, R, mode, m_cap, sps, info, mstar, lengths);
+  }
   hipLaunchKernelGGL(sched_count_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, i0, gamma,
                      mstar, lengths);
   return check_launch("schedule scan");

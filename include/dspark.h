@@ -211,6 +211,36 @@ dspark_status dspark_schedule(const float* surv, const float* sps, int R, int ga
                               int32_t* lengths, int32_t* order, dspark_schedule_info* info,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* Admission rules of dspark_schedule_ex. */
+typedef enum {
+  DSPARK_SCHED_GLOBAL = 0,      /* global search over every budget (= dspark_schedule) */
+  DSPARK_SCHED_EARLY_STOP = 1,  /* the greedy scan with its break */
+  DSPARK_SCHED_CAPACITY = 2     /* a predicted batch capacity, top candidates */
+} dspark_sched_mode;
+
+/*
+ * The scheduler with a choice of admission rule.  Candidates, their order,
+ * q, S_m, Theta_m, l_r and the info fields are those of dspark_schedule.
+ *   DSPARK_SCHED_GLOBAL: identical to dspark_schedule.
+ *   DSPARK_SCHED_EARLY_STOP ([P1] section 二 design 2, greedy steps 3-5, the
+ *     theoretical version that [P3] part 01 describes as non-anticipating):
+ *     candidates are admitted in order while Theta keeps rising; m* is the
+ *     smallest m with Theta_{m+1} <= Theta_m, or R*gamma if there is none.
+ *   DSPARK_SCHED_CAPACITY ([P1] section 三 challenge 1, [P3] part 01: the
+ *     asynchronous production form): `capacity` K is the predicted size of the
+ *     next verification batch in tokens, anchors included; m* = clamp(K - R,
+ *     0, R*gamma) (the dynamic top-K).  sps and B_max are not used (sps may be
+ *     NULL); info->theta reports tau*.
+ *   capacity  >= 0, used by DSPARK_SCHED_CAPACITY only.
+ * Other arguments as for dspark_schedule; the workspace size is the same.
+ * Errors: as dspark_schedule, plus EINVAL for an unknown mode or a negative
+ * capacity (sps and B_max are checked only when the mode uses them).
+ */
+dspark_status dspark_schedule_ex(const float* surv, const float* sps, int R, int gamma, int B_max,
+                                 int mode, int capacity, int32_t* lengths, int32_t* order,
+                                 dspark_schedule_info* info, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
 /* Static description of a status code. */
 const char* dspark_status_string(int status);
 

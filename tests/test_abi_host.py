@@ -138,6 +138,29 @@ def test_schedule_rejects(kw, want):
     assert st == want
 
 
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(mode=3), EINVAL), (dict(mode=-1), EINVAL),
+    (dict(mode=2, capacity=-1), EINVAL),
+    (dict(mode=1, sps=None), EINVAL), (dict(mode=0, sps=None), EINVAL),
+    (dict(mode=1, B_max=23), EINVAL),
+    (dict(mode=2, surv=None), EINVAL), (dict(mode=2, lengths=None), EINVAL),
+    (dict(mode=2, R=0), EINVAL),
+    (dict(mode=2, R=1 << 21, g=8), EUNSUPPORTED),
+    (dict(mode=2, ws=None), EWORKSPACE), (dict(mode=1, ws_bytes=1), EWORKSPACE),
+])
+def test_schedule_ex_rejects(kw, want):
+    a = dict(surv=P, sps=P, R=4, g=5, B_max=24, mode=0, capacity=10, lengths=P, ws=P,
+             ws_bytes=1 << 20)
+    a.update(kw)
+    L = D.lib()
+    st = L.dspark_schedule_ex(a["surv"], a["sps"], a["R"], a["g"], a["B_max"], a["mode"],
+                              a["capacity"], a["lengths"], None, None, a["ws"], a["ws_bytes"],
+                              None)
+    assert st == want
+    assert L.dspark_last_error() != b""
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("DSPARK_LIB", str(tmp_path / "missing.so"))
     monkeypatch.setattr(D, "_LIB", None)

@@ -224,6 +224,66 @@ def test_sched_stress_workload():
     _sched_case(wl["conf"], wl["sps"])
 
 
+def _sched_ex_case(a, sps, mode, K=0):
+    gs = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    gsps = None if sps is None else torch.from_numpy(sps).to(DEV)
+    lengths, order, info = D.dspark_schedule_ex(gs, gsps, mode=mode, capacity=K, want_order=True,
+                                                want_info=True)
+    torch.cuda.synchronize()
+    ref = O.schedule_early_stop(a, sps) if mode == D.SCHED_EARLY_STOP else O.schedule_capacity(a, K)
+    inf = D.schedule_info(info)
+    assert np.array_equal(order.cpu().numpy(), ref["order"]), "sort order differs"
+    assert np.array_equal(lengths.cpu().numpy(), ref["lengths"]), "lengths differ"
+    assert inf.m_star == ref["m_star"] and inf.B_star == ref["B_star"]
+    assert inf.tau_fx == ref["tau_fx"] and inf.tau == ref["tau"] and inf.theta == ref["theta"]
+    return ref
+
+
+@pytest.mark.parametrize("R,g,kind,slope", [(50, 5, "stair_lin", 0.002), (256, 7, "stair", 0.0),
+                                            (1000, 8, "stair", 0.0), (1100, 8, "stair", 0.0),
+                                            (1100, 8, "lin", 0.00004), (3000, 5, "lin", 0.00002),
+                                            (3000, 5, "lin", 0.00005)])
+def test_schedule_early_stop(R, g, kind, slope):
+    # "stair": the staircase alone (survivals near 1: the break is the first
+    # plateau edge inside the range); "stair_lin": the staircase times a linear
+    # decay; "lin": a linear decay alone, which puts the break thousands of
+    # candidates in (later tiles of the workspace path, which 1100 x 8 and
+    # 3000 x 5 take).
+    _say(f"case schedule early stop R={R} g={g} {kind} slope={slope}")
+    from draft_head_step_amd.inputs import sps_table
+    rng = np.random.default_rng(R + g)
+    lo = 0.97 if kind == "stair" else 0.3
+    a = O.survival(rng.uniform(lo, 1.0, size=(R, g)).astype(np.float32))
+    B = np.arange(1, R * (1 + g) + 1, dtype=np.float64)
+    lin = np.maximum(1.0 - slope * (B - 1), 0.01)
+    stair = sps_table("staircase", R * (1 + g)).astype(np.float64)
+    sps = (stair if kind == "stair" else lin if kind == "lin" else stair * lin).astype(np.float32)
+    ref = _sched_ex_case(a, sps, D.SCHED_EARLY_STOP)
+    assert 0 <= ref["m_star"] <= R * g
+
+
+@pytest.mark.parametrize("R,g,K", [(4, 5, 0), (4, 5, 4), (4, 5, 13), (4, 5, 24), (4, 5, 99),
+                                   (300, 5, 1000), (2000, 4, 9000), (2731, 3, 5000),
+                                   (5000, 7, 20000), (5000, 7, 40000)])
+def test_schedule_capacity(R, g, K):
+    _say(f"case schedule capacity R={R} g={g} K={K}")
+    rng = np.random.default_rng(K + R)
+    a = O.survival(rng.uniform(0.05, 1.0, size=(R, g)).astype(np.float32))
+    _sched_ex_case(a, None, D.SCHED_CAPACITY, K)
+
+
+@pytest.mark.parametrize("R,g", [(700, 6), (3000, 6)])
+def test_schedule_ex_ties_and_zeros(R, g):
+    _say(f"case schedule ex ties R={R} g={g}")
+    rng = np.random.default_rng(77)
+    c = rng.choice(np.array([1.0, 0.5, 0.0, 0.75], np.float32), size=(R, g))
+    a = O.survival(c)
+    B = np.arange(1, R * (1 + g) + 1)
+    sps = (0.999 ** (B / 64.0)).astype(np.float32)
+    _sched_ex_case(a, sps, D.SCHED_EARLY_STOP)
+    _sched_ex_case(a, None, D.SCHED_CAPACITY, R + (R * g) // 2)
+
+
 # --------------------------------------------------------------------------- full sizes
 
 def _sample_rows(R, n, seed):
