@@ -285,6 +285,77 @@ def schedule_capacity(surv: np.ndarray, capacity: int):
     return _result(a, order, m, tau)
 
 
+# ---------------------------------------------------------------------------
+# Verification side -- [P1] §三 挑战3 (every verified token is one flattened
+# element; a marker tensor carries the within-sequence dependencies); [P3]
+# Figure 1 (the target verifies anchor + kept prefix in parallel, accepts the
+# matching prefix and emits a corrected token); [P1] §二 设计二 (the acceptance
+# label 1 - TV(p^d, p^t)).
+# ---------------------------------------------------------------------------
+
+def verify_pack(anchors, tokens, lengths, pos0=None):
+    """Flatten the scheduled prefixes: request r contributes 1 + l_r elements,
+    its anchor then its first l_r drafts, at positions pos0[r] + j (pos0 = 0 if
+    not given), each marked with r.  cu_seqlens[r] is where request r starts;
+    cu_seqlens[R] = B = sum_r (1 + l_r)."""
+    anchors = np.asarray(anchors, dtype=np.int64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    R, g = tokens.shape
+    lengths = np.asarray(lengths, dtype=np.int64)
+    pos0 = np.zeros(R, np.int64) if pos0 is None else np.asarray(pos0, dtype=np.int64)
+    cu = np.zeros(R + 1, np.int64)
+    flat_tok, flat_pos, flat_req = [], [], []
+    for r in range(R):
+        n = 1 + int(lengths[r])
+        cu[r + 1] = cu[r] + n
+        for j in range(n):
+            flat_tok.append(int(anchors[r]) if j == 0 else int(tokens[r, j - 1]))
+            flat_pos.append(int(pos0[r]) + j)
+            flat_req.append(r)
+    return {"tokens": np.array(flat_tok, np.int32), "positions": np.array(flat_pos, np.int32),
+            "request": np.array(flat_req, np.int32), "cu_seqlens": cu.astype(np.int32),
+            "B": int(cu[R])}
+
+
+def verify_greedy(target_logits, cu_seqlens, tokens, lengths):
+    """Greedy verification of the flattened batch: t = argmax of each target row
+    (the target's next token after that element; ties -> smallest id).  For
+    request r starting at s = cu_seqlens[r], draft j (1-based) is accepted while
+    tokens[r, j-1] == t[s + j - 1] for every earlier j; a = the number accepted
+    (<= l_r); the next token is t[s + a] -- the correction of the first rejected
+    draft, or the bonus token when all l_r are accepted."""
+    t = np.argmax(np.asarray(target_logits, dtype=np.float32), axis=1).astype(np.int64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    R = tokens.shape[0]
+    accepted = np.zeros(R, np.int32)
+    nxt = np.zeros(R, np.int32)
+    for r in range(R):
+        s = int(cu_seqlens[r])
+        a = 0
+        while a < int(lengths[r]) and tokens[r, a] == t[s + a]:
+            a += 1
+        accepted[r] = a
+        nxt[r] = t[s + a]
+    return {"target_argmax": t.astype(np.int32), "accepted": accepted, "next_token": nxt}
+
+
+def softmax64(z: np.ndarray, temperature: float = 1.0) -> np.ndarray:
+    x = np.asarray(z, dtype=np.float64) / float(temperature)
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def accept_prob(draft_logits, target_logits, temperature: float = 1.0):
+    """Per row: sum_v min(p^d_v, p^t_v) with p = softmax(logits / T) -- the
+    probability that a token drawn from the draft distribution survives the
+    rejection test against the target, which equals 1 - TV(p^d, p^t), the
+    confidence head's training label."""
+    p = softmax64(draft_logits, temperature)
+    q = softmax64(target_logits, temperature)
+    return np.minimum(p, q).sum(axis=-1)
+
+
 def run_path(wl: dict, rows=None):
     """Draft -> confidence -> survival -> schedule for one workload (the whole hot path)."""
     dr = markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"], wl["mode"],
