@@ -425,6 +425,60 @@ def main():
                 "frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                 "data": "synthetic, drawn on the device (seeded torch generator)"}
 
+    def verify_side(vR=256, vg=5, vV=129280, calls=20):
+        """The verification side at the DeepSeek-V4 shape, every request keeping all
+        gamma drafts (B = R (1 + gamma) flattened elements): dspark_verify_pack,
+        dspark_verify_greedy over the B target rows, and dspark_accept_prob over
+        R * gamma draft / target row pairs.  Inputs drawn on the device."""
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(21)
+        anc = torch.randint(0, vV, (vR,), generator=gen, device=dev, dtype=torch.int32)
+        drafts = torch.randint(0, vV, (vR, vg), generator=gen, device=dev, dtype=torch.int32)
+        lens = torch.full((vR,), vg, dtype=torch.int32, device=dev)
+        nB = vR * (1 + vg)
+        tgt = torch.randn((nB, vV), generator=gen, device=dev).mul_(2.0)
+        dl = torch.randn((vR * vg, vV), generator=gen, device=dev).mul_(3.0)
+        tl = dl + torch.randn((vR * vg, vV), generator=gen, device=dev)
+        ft = torch.empty((nB,), dtype=torch.int32, device=dev)
+        fpos = torch.empty_like(ft)
+        freq = torch.empty_like(ft)
+        cu = torch.empty((vR + 1,), dtype=torch.int32, device=dev)
+        am = torch.empty((nB,), dtype=torch.int32, device=dev)
+        acc = torch.empty((vR,), dtype=torch.int32, device=dev)
+        nxt = torch.empty((vR,), dtype=torch.int32, device=dev)
+        ap = torch.empty((vR * vg,), dtype=torch.float32, device=dev)
+
+        def timed(fn):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(calls)]
+            warm(fn, 20.0)
+            for b, e in evs:
+                b.record(stream)
+                fn()
+                e.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([b.elapsed_time(e) for b, e in evs])) * 1e3
+
+        pack = lambda: D.dspark_verify_pack(anc, drafts, lens, flat_tokens=ft, flat_pos=fpos,
+                                            flat_req=freq, cu_seqlens=cu, stream=stream)
+        pack()
+        us_pack = timed(pack)
+        us_greedy = timed(lambda: D.dspark_verify_greedy(tgt, cu, drafts, target_argmax=am,
+                                                         accepted=acc, next_token=nxt,
+                                                         stream=stream))
+        us_acc = timed(lambda: D.dspark_accept_prob(dl, tl, 1.0, out=ap, stream=stream))
+        b_greedy = nB * vV * 4
+        b_acc = 2 * vR * vg * vV * 4
+        del tgt, dl, tl
+        return {"workload": f"R={vR}, gamma={vg}, V={vV}, every draft kept (B={nB})",
+                "pack_us": round(us_pack, 1),
+                "greedy_us": round(us_greedy, 1),
+                "greedy_frac_of_hbm": round(b_greedy / (us_greedy / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                "accept_prob_us": round(us_acc, 1),
+                "accept_prob_frac_of_hbm": round(b_acc / (us_acc / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "fractions use one read of the logits (the accept-prob kernel reads "
+                        "each row pair twice: max/sum, then the min-sum)"}
+
     def hbm_measured(nbytes=1 << 31, reps=5):
         """Large-copy bandwidth (read + write bytes over time) of torch's device copy:
         a measured reference beside the published peak."""
@@ -486,6 +540,7 @@ def main():
         out["gemm_only"] = [gemm_only(args.config), gemm_only("long_block")]
         out["scheduler"] = scheduler_only()
         out["other_configs"] = [whole_step_config("qwen3_8b"), whole_step_config("long_block")]
+        out["verify"] = verify_side()
         out["hbm_measured"] = hbm_measured()
     if not args.no_row_major and not args.no_extras and args.layout != "rgv":
         ms2, d2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1), ev_steps=20)

@@ -9,7 +9,8 @@ raises: there is no fallback path.
 
 Entry points (same names as the C ABI):
   dspark_markov_draft, dspark_confidence, dspark_survival, dspark_schedule,
-  dspark_schedule_ex, dspark_markov_draft_workspace, dspark_schedule_workspace.
+  dspark_schedule_ex, dspark_verify_pack, dspark_verify_greedy, dspark_accept_prob,
+  dspark_markov_draft_workspace, dspark_schedule_workspace.
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ from typing import Optional
 __all__ = [
     "DsparkError", "GREEDY", "SAMPLE", "LAYOUT_RGV", "LAYOUT_TILED", "lib", "lib_path",
     "dspark_markov_draft", "dspark_confidence", "dspark_survival", "dspark_schedule",
-    "dspark_schedule_ex", "dspark_markov_draft_workspace", "dspark_schedule_workspace",
+    "dspark_schedule_ex", "dspark_verify_pack", "dspark_verify_greedy", "dspark_accept_prob",
+    "dspark_markov_draft_workspace", "dspark_schedule_workspace",
     "ScheduleInfo", "SCHED_GLOBAL", "SCHED_EARLY_STOP", "SCHED_CAPACITY",
 ]
 
@@ -94,6 +96,12 @@ def lib() -> ctypes.CDLL:
     L.dspark_schedule.restype = i32
     L.dspark_schedule_ex.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     L.dspark_schedule_ex.restype = i32
+    L.dspark_verify_pack.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    L.dspark_verify_pack.restype = i32
+    L.dspark_verify_greedy.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    L.dspark_verify_greedy.restype = i32
+    L.dspark_accept_prob.argtypes = [vp, vp, i32, i32, f32, vp, vp]
+    L.dspark_accept_prob.restype = i32
     _LIB = L
     return L
 
@@ -303,3 +311,88 @@ def schedule_info(info_tensor) -> ScheduleInfo:
     """Copy a device dspark_schedule_info to the host (synchronises)."""
     raw = bytes(info_tensor.cpu().numpy().tobytes())
     return ScheduleInfo.from_buffer_copy(raw)
+
+
+def dspark_verify_pack(anchors, tokens, lengths, pos0=None, flat_tokens=None, flat_pos=None,
+                       flat_req=None, cu_seqlens=None, want_pos: bool = True,
+                       want_req: bool = True, stream=None):
+    """Flattened verification batch.  Returns (flat_tokens, flat_pos or None,
+    flat_req or None, cu_seqlens); arrays have room for R * (1 + gamma) elements,
+    the first cu_seqlens[R] are written."""
+    torch = _torch()
+    L = lib()
+    R, gamma = tokens.shape
+    dev = tokens.device
+    _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
+    _need(anchors, "anchors", (torch.int32,), (R,), dev)
+    _need(lengths, "lengths", (torch.int32,), (R,), dev)
+    if pos0 is not None:
+        _need(pos0, "pos0", (torch.int32,), (R,), dev)
+    n = R * (1 + gamma)
+    if flat_tokens is None:
+        flat_tokens = torch.empty((n,), dtype=torch.int32, device=dev)
+    _need(flat_tokens, "flat_tokens", (torch.int32,), (n,), dev)
+    if flat_pos is None and want_pos:
+        flat_pos = torch.empty((n,), dtype=torch.int32, device=dev)
+    if flat_req is None and want_req:
+        flat_req = torch.empty((n,), dtype=torch.int32, device=dev)
+    for t, name in ((flat_pos, "flat_pos"), (flat_req, "flat_req")):
+        if t is not None:
+            _need(t, name, (torch.int32,), (n,), dev)
+    if cu_seqlens is None:
+        cu_seqlens = torch.empty((R + 1,), dtype=torch.int32, device=dev)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), (R + 1,), dev)
+    _check(L.dspark_verify_pack(_ptr(anchors), _ptr(tokens), _ptr(lengths), _ptr(pos0), R, gamma,
+                                _ptr(flat_tokens), _ptr(flat_pos), _ptr(flat_req),
+                                _ptr(cu_seqlens), _stream(stream)), "dspark_verify_pack")
+    return flat_tokens, flat_pos, flat_req, cu_seqlens
+
+
+def dspark_verify_greedy(target_logits, cu_seqlens, tokens, target_argmax=None, accepted=None,
+                         next_token=None, stream=None):
+    """Greedy accept / correct over a flattened batch.  Returns (accepted [R],
+    next_token [R], target_argmax [R*(1+gamma)])."""
+    torch = _torch()
+    L = lib()
+    R, gamma = tokens.shape
+    dev = tokens.device
+    _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), (R + 1,), dev)
+    if target_logits.dim() != 2 or target_logits.dtype != torch.float32 or \
+            target_logits.device != dev or not target_logits.is_contiguous():
+        raise ValueError("target_logits must be a contiguous [rows, V] float32 device tensor")
+    V = target_logits.shape[1]
+    n = R * (1 + gamma)
+    if target_argmax is None:
+        target_argmax = torch.empty((n,), dtype=torch.int32, device=dev)
+    if accepted is None:
+        accepted = torch.empty((R,), dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty((R,), dtype=torch.int32, device=dev)
+    _need(target_argmax, "target_argmax", (torch.int32,), (n,), dev)
+    _need(accepted, "accepted", (torch.int32,), (R,), dev)
+    _need(next_token, "next_token", (torch.int32,), (R,), dev)
+    _check(L.dspark_verify_greedy(_ptr(target_logits), _ptr(cu_seqlens), _ptr(tokens), R, gamma,
+                                  V, _ptr(target_argmax), _ptr(accepted), _ptr(next_token),
+                                  _stream(stream)), "dspark_verify_greedy")
+    return accepted, next_token, target_argmax
+
+
+def dspark_accept_prob(draft_logits, target_logits, temperature: float = 1.0, out=None,
+                       stream=None):
+    """sum_v min(softmax(draft/T), softmax(target/T)) per row of two [n, V] tensors."""
+    torch = _torch()
+    L = lib()
+    for t, name in ((draft_logits, "draft_logits"), (target_logits, "target_logits")):
+        if t.dim() != 2 or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [n, V] float32 tensor")
+    if draft_logits.shape != target_logits.shape or draft_logits.device != target_logits.device:
+        raise ValueError("draft_logits and target_logits must match in shape and device")
+    n, V = draft_logits.shape
+    if out is None:
+        out = torch.empty((n,), dtype=torch.float32, device=draft_logits.device)
+    _need(out, "out", (torch.float32,), (n,), draft_logits.device)
+    _check(L.dspark_accept_prob(_ptr(draft_logits), _ptr(target_logits), n, V,
+                                float(temperature), _ptr(out), _stream(stream)),
+           "dspark_accept_prob")
+    return out

@@ -182,4 +182,47 @@ dspark_status dspark_schedule_ex(const float* surv, const float* sps, int R, int
                                  reinterpret_cast<hipStream_t>(stream));
 }
 
+dspark_status dspark_verify_pack(const int32_t* anchors, const int32_t* tokens,
+                                 const int32_t* lengths, const int32_t* pos0, int R, int gamma,
+                                 int32_t* flat_tokens, int32_t* flat_pos, int32_t* flat_req,
+                                 int32_t* cu_seqlens, void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!anchors || !tokens || !lengths || !flat_tokens || !cu_seqlens)
+    return fail(DSPARK_EINVAL, "verify_pack: NULL required pointer");
+  if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "verify_pack: sizes must be positive");
+  if ((long long)R * (1LL + gamma) > 0x7fffffffLL)
+    return fail(DSPARK_EUNSUPPORTED, "verify_pack: R * (1 + gamma) above 2^31 - 1");
+  return dspark::launch_verify_pack(anchors, tokens, lengths, pos0, R, gamma, flat_tokens,
+                                    flat_pos, flat_req, cu_seqlens,
+                                    reinterpret_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_verify_greedy(const float* target_logits, const int32_t* cu_seqlens,
+                                   const int32_t* tokens, int R, int gamma, int V,
+                                   int32_t* target_argmax, int32_t* accepted,
+                                   int32_t* next_token, void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!target_logits || !cu_seqlens || !tokens || !target_argmax || !accepted || !next_token)
+    return fail(DSPARK_EINVAL, "verify_greedy: NULL required pointer");
+  if (R <= 0 || gamma <= 0 || V < 1)
+    return fail(DSPARK_EINVAL, "verify_greedy: sizes must be positive");
+  if ((long long)R * (1LL + gamma) > 0x7fffffffLL)
+    return fail(DSPARK_EUNSUPPORTED, "verify_greedy: R * (1 + gamma) above 2^31 - 1");
+  return dspark::launch_verify_greedy(target_logits, cu_seqlens, tokens, R, gamma, V,
+                                      target_argmax, accepted, next_token,
+                                      reinterpret_cast<hipStream_t>(stream));
+}
+
+dspark_status dspark_accept_prob(const float* draft_logits, const float* target_logits, int n,
+                                 int V, float temperature, float* out, void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!draft_logits || !target_logits || !out)
+    return fail(DSPARK_EINVAL, "accept_prob: NULL required pointer");
+  if (n <= 0 || V < 1) return fail(DSPARK_EINVAL, "accept_prob: sizes must be positive");
+  if (!(temperature > 0.0f) || !isfinite(temperature))
+    return fail(DSPARK_EINVAL, "accept_prob: temperature must be positive and finite");
+  return dspark::launch_accept_prob(draft_logits, target_logits, n, V, temperature, out,
+                                    reinterpret_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -46,6 +46,18 @@ dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int
                                 hipStream_t stream);
 dspark_status launch_survival(const float* conf, int R, int gamma, float* surv, hipStream_t stream);
 
+// ---- verification side ----
+dspark_status launch_verify_pack(const int32_t* anchors, const int32_t* tokens,
+                                 const int32_t* lengths, const int32_t* pos0, int R, int gamma,
+                                 int32_t* flat_tokens, int32_t* flat_pos, int32_t* flat_req,
+                                 int32_t* cu_seqlens, hipStream_t stream);
+dspark_status launch_verify_greedy(const float* target_logits, const int32_t* cu_seqlens,
+                                   const int32_t* tokens, int R, int gamma, int V,
+                                   int32_t* target_argmax, int32_t* accepted,
+                                   int32_t* next_token, hipStream_t stream);
+dspark_status launch_accept_prob(const float* draft_logits, const float* target_logits, int n,
+                                 int V, float temperature, float* out, hipStream_t stream);
+
 // ---- prefix scheduler ----
 size_t schedule_workspace_bytes(int R, int gamma);
 // mode: 0 global search, 1 early stop, 2 capacity (m_cap = clamp(K - R, 0, R * gamma)).

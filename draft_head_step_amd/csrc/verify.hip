@@ -1,0 +1,282 @@
+// Verification side for CDNA4 (gfx950).
+//
+// [P1] section 三 challenge 3: every verified token is one flattened element,
+// the within-sequence dependencies travel in a marker tensor; [P3] Figure 1:
+// the target verifies anchor + kept prefix in parallel, accepts the prefix its
+// own predictions match and emits a corrected token; [P1] section 二 design 2:
+// the acceptance label 1 - TV(p_draft, p_target).
+//
+//   verify_pack:   cu_seqlens = exclusive scan of (1 + l_r) (one workgroup,
+//                  chunks of 1024 with a carry), then one thread per (r, j)
+//                  writes token (anchor or draft j), position pos0[r] + j and
+//                  the request id r;
+//   verify_greedy: one workgroup per flattened row takes the target's argmax
+//                  (16-byte loads, per-thread running max in increasing v,
+//                  smallest id on ties), then one thread per request walks
+//                  its drafts against those argmaxes;
+//   accept_prob:   one workgroup per row pair, two passes over V: online
+//                  (max, sum of exp) of both rows, then sum_v min(p, q).
+//                  Reductions use a fixed tree, so results are deterministic.
+#include <math.h>
+
+#include "dspark_internal.h"
+
+namespace dspark {
+namespace {
+
+constexpr int kPackT = 1024;
+constexpr int kRowT = 256;
+constexpr int kRowW = kRowT / 64;
+
+__device__ __forceinline__ int clamp_len(int l, int gamma) { return min(max(l, 0), gamma); }
+
+__global__ __launch_bounds__(kPackT) void verify_scan_kernel(const int32_t* __restrict__ lengths,
+                                                             int R, int gamma,
+                                                             int32_t* __restrict__ cu) {
+  __shared__ int wtot[kPackT / 64];
+  __shared__ int carry;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < R; c0 += kPackT) {
+    const int r = c0 + t;
+    const int v = r < R ? 1 + clamp_len(lengths[r], gamma) : 0;
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    int pre = carry, total = 0;
+#pragma unroll
+    for (int j = 0; j < kPackT / 64; ++j) {
+      pre += j < w ? wtot[j] : 0;
+      total += wtot[j];
+    }
+    if (r < R) cu[r] = pre + inc - v;
+    __syncthreads();
+    if (t == 0) carry += total;
+    __syncthreads();
+  }
+  if (t == 0) cu[R] = carry;
+}
+
+__global__ __launch_bounds__(256) void verify_scatter_kernel(
+    const int32_t* __restrict__ anchors, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ lengths, const int32_t* __restrict__ pos0,
+    const int32_t* __restrict__ cu, int R, int gamma, int32_t* __restrict__ flat_tokens,
+    int32_t* __restrict__ flat_pos, int32_t* __restrict__ flat_req) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int per = 1 + gamma;
+  if (e >= (long long)R * per) return;
+  const int r = (int)(e / per);
+  const int j = (int)(e % per);
+  if (j > clamp_len(lengths[r], gamma)) return;
+  const int dst = cu[r] + j;
+  flat_tokens[dst] = j == 0 ? anchors[r] : tokens[(size_t)r * gamma + j - 1];
+  if (flat_pos) flat_pos[dst] = (pos0 ? pos0[r] : 0) + j;
+  if (flat_req) flat_req[dst] = r;
+}
+
+// Running (max, smallest index) of one thread, merged in a fixed tree.
+__device__ __forceinline__ void take(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__global__ __launch_bounds__(kRowT) void verify_argmax_kernel(const float* __restrict__ logits,
+                                                              const int32_t* __restrict__ cu,
+                                                              int R, int V, int vec,
+                                                              int32_t* __restrict__ amax) {
+  __shared__ float sv[kRowW];
+  __shared__ int si[kRowW];
+  const int row = blockIdx.x;
+  if (row >= cu[R]) return;   // rows past the batch are not read
+  const int t = threadIdx.x;
+  const float* z = logits + (size_t)row * V;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  if (vec) {
+    const float4* z4 = reinterpret_cast<const float4*>(z);
+    const int n4 = V >> 2;
+    for (int p = t; p < n4; p += kRowT) {
+      const float4 q = z4[p];
+      take(bv, bi, q.x, 4 * p);
+      take(bv, bi, q.y, 4 * p + 1);
+      take(bv, bi, q.z, 4 * p + 2);
+      take(bv, bi, q.w, 4 * p + 3);
+    }
+  } else {
+    for (int v = t; v < V; v += kRowT) take(bv, bi, z[v], v);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    take(bv, bi, ov, oi);
+  }
+  if ((t & 63) == 0) {
+    sv[t >> 6] = bv;
+    si[t >> 6] = bi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int j = 1; j < kRowW; ++j) take(bv, bi, sv[j], si[j]);
+    amax[row] = bi < V ? bi : 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void verify_accept_kernel(const int32_t* __restrict__ amax,
+                                                            const int32_t* __restrict__ cu,
+                                                            const int32_t* __restrict__ tokens,
+                                                            int R, int gamma,
+                                                            int32_t* __restrict__ accepted,
+                                                            int32_t* __restrict__ next_token) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  const int s = cu[r];
+  const int l = clamp_len(cu[r + 1] - s - 1, gamma);
+  int a = 0;
+  while (a < l && tokens[(size_t)r * gamma + a] == amax[s + a]) ++a;
+  accepted[r] = a;
+  next_token[r] = amax[s + a];
+}
+
+// (max, sum of exp(x - max)) pairs, merged without losing the smaller one.
+struct MaxSum {
+  float m;
+  float s;
+};
+
+__device__ __forceinline__ MaxSum merge_ms(MaxSum a, MaxSum b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -INFINITY) return {m, 0.0f};
+  return {m, a.s * expf(a.m - m) + b.s * expf(b.m - m)};
+}
+
+__device__ __forceinline__ void add_ms(MaxSum& a, float x) {
+  if (x > a.m) {
+    a.s = a.s * expf(a.m - x) + 1.0f;   // exp(-inf) = 0 on the first finite element
+    a.m = x;
+  } else if (x != -INFINITY) {          // -inf adds nothing (and -inf - -inf is NaN)
+    a.s += expf(x - a.m);
+  }
+}
+
+__device__ __forceinline__ MaxSum block_ms(MaxSum v, MaxSum* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    MaxSum o{__shfl_xor(v.m, off), __shfl_xor(v.s, off)};
+    v = merge_ms(v, o);
+  }
+  const int t = threadIdx.x;
+  if ((t & 63) == 0) sh[t >> 6] = v;
+  __syncthreads();
+  MaxSum r = sh[0];
+#pragma unroll
+  for (int j = 1; j < kRowW; ++j) r = merge_ms(r, sh[j]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kRowT) void accept_prob_kernel(const float* __restrict__ zd,
+                                                            const float* __restrict__ zt, int V,
+                                                            float inv_t, int vec,
+                                                            float* __restrict__ out) {
+  __shared__ MaxSum shd[kRowW];
+  __shared__ MaxSum sht[kRowW];
+  __shared__ float ssum[kRowW];
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const float* a = zd + (size_t)row * V;
+  const float* b = zt + (size_t)row * V;
+  MaxSum md{-INFINITY, 0.0f}, mt{-INFINITY, 0.0f};
+  if (vec) {
+    const float4* a4 = reinterpret_cast<const float4*>(a);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+    for (int p = t; p < (V >> 2); p += kRowT) {
+      const float4 x = a4[p];
+      const float4 y = b4[p];
+      add_ms(md, x.x * inv_t); add_ms(md, x.y * inv_t); add_ms(md, x.z * inv_t); add_ms(md, x.w * inv_t);
+      add_ms(mt, y.x * inv_t); add_ms(mt, y.y * inv_t); add_ms(mt, y.z * inv_t); add_ms(mt, y.w * inv_t);
+    }
+  } else {
+    for (int v = t; v < V; v += kRowT) {
+      add_ms(md, a[v] * inv_t);
+      add_ms(mt, b[v] * inv_t);
+    }
+  }
+  md = block_ms(md, shd);
+  mt = block_ms(mt, sht);
+  const float id_ = 1.0f / md.s;
+  const float it_ = 1.0f / mt.s;
+  float acc = 0.0f;
+  auto term = [&](float x, float y) {
+    return fminf(expf(x * inv_t - md.m) * id_, expf(y * inv_t - mt.m) * it_);
+  };
+  if (vec) {
+    const float4* a4 = reinterpret_cast<const float4*>(a);
+    const float4* b4 = reinterpret_cast<const float4*>(b);
+    for (int p = t; p < (V >> 2); p += kRowT) {
+      const float4 x = a4[p];
+      const float4 y = b4[p];
+      acc += (term(x.x, y.x) + term(x.y, y.y)) + (term(x.z, y.z) + term(x.w, y.w));
+    }
+  } else {
+    for (int v = t; v < V; v += kRowT) acc += term(a[v], b[v]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((t & 63) == 0) ssum[t >> 6] = acc;
+  __syncthreads();
+  if (t == 0) {
+    float s = 0.0f;
+    for (int j = 0; j < kRowW; ++j) s += ssum[j];
+    out[row] = s;
+  }
+}
+
+}  // namespace
+
+dspark_status launch_verify_pack(const int32_t* anchors, const int32_t* tokens,
+                                 const int32_t* lengths, const int32_t* pos0, int R, int gamma,
+                                 int32_t* flat_tokens, int32_t* flat_pos, int32_t* flat_req,
+                                 int32_t* cu_seqlens, hipStream_t stream) {
+  hipLaunchKernelGGL(verify_scan_kernel, dim3(1), dim3(kPackT), 0, stream, lengths, R, gamma,
+                     cu_seqlens);
+  const long long n = (long long)R * (1 + gamma);
+  hipLaunchKernelGGL(verify_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     stream, anchors, tokens, lengths, pos0, cu_seqlens, R, gamma, flat_tokens,
+                     flat_pos, flat_req);
+  return check_launch("verify_pack");
+}
+
+dspark_status launch_verify_greedy(const float* target_logits, const int32_t* cu_seqlens,
+                                   const int32_t* tokens, int R, int gamma, int V,
+                                   int32_t* target_argmax, int32_t* accepted,
+                                   int32_t* next_token, hipStream_t stream) {
+  const int rows = R * (1 + gamma);
+  const int vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target_logits) & 15u) == 0);
+  hipLaunchKernelGGL(verify_argmax_kernel, dim3(rows), dim3(kRowT), 0, stream, target_logits,
+                     cu_seqlens, R, V, vec, target_argmax);
+  hipLaunchKernelGGL(verify_accept_kernel, dim3((R + 255) / 256), dim3(256), 0, stream,
+                     target_argmax, cu_seqlens, tokens, R, gamma, accepted, next_token);
+  return check_launch("verify_greedy");
+}
+
+dspark_status launch_accept_prob(const float* draft_logits, const float* target_logits, int n,
+                                 int V, float temperature, float* out, hipStream_t stream) {
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const int vec = (V % 4 == 0) && a16(draft_logits) && a16(target_logits);
+  hipLaunchKernelGGL(accept_prob_kernel, dim3(n), dim3(kRowT), 0, stream, draft_logits,
+                     target_logits, V, 1.0f / temperature, vec, out);
+  return check_launch("accept_prob_kernel");
+}
+
+}  // namespace dspark

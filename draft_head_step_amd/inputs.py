@@ -104,7 +104,8 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 CHUNK = 1 << 22
 TAGS = {"W1": 1, "W2": 2, "base": 3, "boost": 4, "h": 5, "w_conf": 6, "anchors": 7,
-        "uniforms": 8, "conf": 9}
+        "uniforms": 8, "conf": 9, "v_tokens": 10, "v_target": 11, "v_match": 12,
+        "v_draft_logits": 13, "v_noise": 14}
 
 
 def _gen(seed: int, tag: str, idx: int = 0) -> np.random.Generator:
@@ -252,3 +253,34 @@ def make_head(cfg: Config, seed: Optional[int] = None, *, w_std: Optional[float]
     return {"W1": _normal_bf16(seed, "W1", (V, r), ws), "W2": _normal_bf16(seed, "W2", (V, r), ws),
             "anchors": _gen(seed, "anchors").integers(0, V, size=(cfg.R,), dtype=np.int32),
             "R": cfg.R, "gamma": cfg.gamma, "V": V, "r": r}
+
+
+def make_verify_workload(R: int, gamma: int, V: int, seed: int = 11, match_rate: float = 0.7,
+                         logit_std: float = 2.0) -> dict:
+    """Inputs of the verification side: anchors, drafts, kept lengths, anchor
+    positions, and target logits laid out per request and element,
+    target[r, j] (j = 0..gamma) being the target's logits after element j of
+    request r (its anchor, then draft j).  With probability match_rate the
+    target's top token after element j is draft j + 1 (so drafts get accepted),
+    else a random row.  The caller flattens target[r, :1 + l_r] in request order."""
+    g = _gen(seed, "v_tokens")
+    anchors = g.integers(0, V, size=R, dtype=np.int32)
+    drafts = g.integers(0, V, size=(R, gamma), dtype=np.int32)
+    lengths = g.integers(0, gamma + 1, size=R, dtype=np.int32)
+    pos0 = g.integers(0, 4096, size=R, dtype=np.int32)
+    target = _fill((R, 1 + gamma, V), np.float32, seed, "v_target", _normal_f32(logit_std))
+    m = _gen(seed, "v_match").random(size=(R, gamma)) < match_rate
+    for r in range(R):
+        for j in range(gamma):
+            if m[r, j]:
+                target[r, j, drafts[r, j]] = target[r, j].max() + np.float32(1.0)
+    return {"anchors": anchors, "tokens": drafts, "lengths": lengths, "pos0": pos0,
+            "target": target, "R": R, "gamma": gamma, "V": V}
+
+
+def make_accept_workload(n: int, V: int, seed: int = 12, draft_std: float = 3.0,
+                         noise_std: float = 1.0) -> dict:
+    """Paired draft / target logit rows [n, V]: target = draft + independent noise."""
+    d = _fill((n, V), np.float32, seed, "v_draft_logits", _normal_f32(draft_std))
+    t = d + _fill((n, V), np.float32, seed, "v_noise", _normal_f32(noise_std))
+    return {"draft": d, "target": t}

@@ -241,6 +241,62 @@ dspark_status dspark_schedule_ex(const float* surv, const float* sps, int R, int
                                  dspark_schedule_info* info, void* workspace, size_t ws_bytes,
                                  void* stream);
 
+/*
+ * Verification side, [P1] section 三 challenge 3 (every verified token is one
+ * flattened element; a marker tensor carries the within-sequence
+ * dependencies) and [P3] Figure 1 (the target verifies anchor + kept prefix
+ * in parallel).  Request r contributes 1 + l_r elements: its anchor, then its
+ * first l_r drafts, at positions pos0[r] + j, each marked with r.
+ *   anchors      [R] int32;  tokens [R, gamma] int32 drafts (row r, draft j at
+ *                r*gamma + j - 1);  lengths [R] int32 l_r (values outside
+ *                [0, gamma] are clamped into it).
+ *   pos0         optional [R] int32 position of each anchor (0 if NULL).
+ *   flat_tokens  [R*(1+gamma)] int32 output (the first B entries are written).
+ *   flat_pos, flat_req  optional outputs of the same size: positions, request ids.
+ *   cu_seqlens   [R+1] int32 output: segment starts, cu_seqlens[R] = B.
+ * Errors: EINVAL for NULL required pointers or non-positive sizes;
+ * EUNSUPPORTED if R*(1+gamma) exceeds 2^31 - 1; EDEVICE.
+ */
+dspark_status dspark_verify_pack(const int32_t* anchors, const int32_t* tokens,
+                                 const int32_t* lengths, const int32_t* pos0, int R, int gamma,
+                                 int32_t* flat_tokens, int32_t* flat_pos, int32_t* flat_req,
+                                 int32_t* cu_seqlens, void* stream);
+
+/*
+ * Greedy verification of a flattened batch ([P3] Figure 1): t_e = argmax_v of
+ * target_logits row e (the target's next token after element e; ties resolve to
+ * the smallest id; rows must be free of NaN).  For request r with segment
+ * start s = cu_seqlens[r] and l_r = cu_seqlens[r+1] - s - 1 drafts, drafts are
+ * accepted while tokens[r, j] == t_{s+j}; accepted[r] = their number and
+ * next_token[r] = t_{s + accepted[r]} (the correction of the first rejected
+ * draft, or the bonus token when all are accepted).
+ *   target_logits  [rows, V] fp32, row e for flattened element e (rows >= B;
+ *                  rows from B on are not read).
+ *   cu_seqlens     [R+1] as written by dspark_verify_pack.
+ *   target_argmax  [R*(1+gamma)] int32 output (the first B entries are written).
+ *   accepted, next_token  [R] int32 outputs.
+ * Errors: EINVAL for NULL pointers or non-positive sizes; EUNSUPPORTED if
+ * R*(1+gamma) exceeds 2^31 - 1; EDEVICE.
+ */
+dspark_status dspark_verify_greedy(const float* target_logits, const int32_t* cu_seqlens,
+                                   const int32_t* tokens, int R, int gamma, int V,
+                                   int32_t* target_argmax, int32_t* accepted,
+                                   int32_t* next_token, void* stream);
+
+/*
+ * Acceptance probability of paired rows ([P1] section 二 design 2, the
+ * confidence head's label 1 - TV(p_draft, p_target)):
+ *   out[i] = sum_v min(softmax(draft_logits[i] / T)_v, softmax(target_logits[i] / T)_v).
+ *   draft_logits, target_logits  [n, V] fp32 (each row needs a finite value;
+ *                                -inf entries are allowed).
+ *   temperature  T > 0 and finite.
+ *   out          [n] fp32 output.
+ * Errors: EINVAL for NULL pointers, non-positive sizes or a bad temperature;
+ * EDEVICE.
+ */
+dspark_status dspark_accept_prob(const float* draft_logits, const float* target_logits, int n,
+                                 int V, float temperature, float* out, void* stream);
+
 /* Static description of a status code. */
 const char* dspark_status_string(int status);
 

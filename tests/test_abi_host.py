@@ -161,6 +161,40 @@ def test_schedule_ex_rejects(kw, want):
     assert L.dspark_last_error() != b""
 
 
+@no_gpu
+@pytest.mark.parametrize("idx", range(5))
+def test_verify_pack_rejects_null(idx):
+    args = [P] * 5   # anchors, tokens, lengths, flat_tokens, cu_seqlens (pos0 / pos / req optional)
+    args[idx] = None
+    an, tk, ln, ft, cu = args
+    assert D.lib().dspark_verify_pack(an, tk, ln, None, 4, 5, ft, None, None, cu, None) == EINVAL
+
+
+@no_gpu
+def test_verify_rejects_sizes_and_nulls():
+    L = D.lib()
+    assert L.dspark_verify_pack(P, P, P, None, 0, 5, P, None, None, P, None) == EINVAL
+    assert L.dspark_verify_pack(P, P, P, None, 1 << 30, 4, P, None, None, P, None) == EUNSUPPORTED
+    assert L.dspark_verify_greedy(P, P, P, 4, 5, 0, P, P, P, None) == EINVAL
+    for i in range(6):
+        a = [P] * 6
+        a[i] = None
+        assert L.dspark_verify_greedy(a[0], a[1], a[2], 4, 5, 100, a[3], a[4], a[5], None) == EINVAL
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=None), EINVAL), (dict(t=None), EINVAL), (dict(o=None), EINVAL),
+    (dict(n=0), EINVAL), (dict(V=0), EINVAL),
+    (dict(T=0.0), EINVAL), (dict(T=-1.0), EINVAL), (dict(T=float("inf")), EINVAL),
+    (dict(T=float("nan")), EINVAL),
+])
+def test_accept_prob_rejects(kw, want):
+    a = dict(d=P, t=P, n=4, V=100, T=1.0, o=P)
+    a.update(kw)
+    assert D.lib().dspark_accept_prob(a["d"], a["t"], a["n"], a["V"], a["T"], a["o"], None) == want
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("DSPARK_LIB", str(tmp_path / "missing.so"))
     monkeypatch.setattr(D, "_LIB", None)
