@@ -14,8 +14,9 @@
 //                  (16-byte loads, per-thread running max in increasing v,
 //                  smallest id on ties), then one thread per request walks
 //                  its drafts against those argmaxes;
-//   accept_prob:   one workgroup per row pair, two passes over V: online
-//                  (max, sum of exp) of both rows, then sum_v min(p, q).
+//   accept_prob:   one 1024-thread workgroup per row pair, two passes over V
+//                  in base 2: online (max, sum of 2^x) of both rows, four
+//                  values per rescale, then sum_v min(p, q).
 //                  Reductions use a fixed tree, so results are deterministic.
 #include <math.h>
 
@@ -148,25 +149,31 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(const int32_t* __res
   next_token[r] = amax[s + a];
 }
 
-// (max, sum of exp(x - max)) pairs, merged without losing the smaller one.
+// Acceptance probability in base 2: with k = log2(e) / T and x' = k x, p_v =
+// 2^(x'_v - L) where L = m + log2(sum 2^(x' - m)), so the kernel keeps (max,
+// sum of 2^(x' - max)) pairs and uses the hardware 2^x.
+constexpr int kAccT = 1024;
+constexpr int kAccW = kAccT / 64;
+
 struct MaxSum {
   float m;
   float s;
 };
 
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ MaxSum merge_ms(MaxSum a, MaxSum b) {
   const float m = fmaxf(a.m, b.m);
   if (m == -INFINITY) return {m, 0.0f};
-  return {m, a.s * expf(a.m - m) + b.s * expf(b.m - m)};
+  return {m, a.s * exp2_(a.m - m) + b.s * exp2_(b.m - m)};
 }
 
-__device__ __forceinline__ void add_ms(MaxSum& a, float x) {
-  if (x > a.m) {
-    a.s = a.s * expf(a.m - x) + 1.0f;   // exp(-inf) = 0 on the first finite element
-    a.m = x;
-  } else if (x != -INFINITY) {          // -inf adds nothing (and -inf - -inf is NaN)
-    a.s += expf(x - a.m);
-  }
+// Fold four scaled values into a running pair (one rescale per four).
+__device__ __forceinline__ void add4(MaxSum& a, float x0, float x1, float x2, float x3) {
+  const float nm = fmaxf(fmaxf(a.m, fmaxf(x0, x1)), fmaxf(x2, x3));
+  if (nm == -INFINITY) return;   // nothing finite yet
+  a.s = a.s * exp2_(a.m - nm) + ((exp2_(x0 - nm) + exp2_(x1 - nm)) + (exp2_(x2 - nm) + exp2_(x3 - nm)));
+  a.m = nm;
 }
 
 __device__ __forceinline__ MaxSum block_ms(MaxSum v, MaxSum* sh) {
@@ -180,65 +187,67 @@ __device__ __forceinline__ MaxSum block_ms(MaxSum v, MaxSum* sh) {
   __syncthreads();
   MaxSum r = sh[0];
 #pragma unroll
-  for (int j = 1; j < kRowW; ++j) r = merge_ms(r, sh[j]);
+  for (int j = 1; j < kAccW; ++j) r = merge_ms(r, sh[j]);
   __syncthreads();
   return r;
 }
 
-__global__ __launch_bounds__(kRowT) void accept_prob_kernel(const float* __restrict__ zd,
+__global__ __launch_bounds__(kAccT) void accept_prob_kernel(const float* __restrict__ zd,
                                                             const float* __restrict__ zt, int V,
-                                                            float inv_t, int vec,
+                                                            float k2, int vec,
                                                             float* __restrict__ out) {
-  __shared__ MaxSum shd[kRowW];
-  __shared__ MaxSum sht[kRowW];
-  __shared__ float ssum[kRowW];
-  const int row = blockIdx.x;
+  __shared__ MaxSum shd[kAccW];
+  __shared__ MaxSum sht[kAccW];
+  __shared__ float ssum[kAccW];
   const int t = threadIdx.x;
-  const float* a = zd + (size_t)row * V;
-  const float* b = zt + (size_t)row * V;
-  MaxSum md{-INFINITY, 0.0f}, mt{-INFINITY, 0.0f};
-  if (vec) {
-    const float4* a4 = reinterpret_cast<const float4*>(a);
-    const float4* b4 = reinterpret_cast<const float4*>(b);
-    for (int p = t; p < (V >> 2); p += kRowT) {
-      const float4 x = a4[p];
-      const float4 y = b4[p];
-      add_ms(md, x.x * inv_t); add_ms(md, x.y * inv_t); add_ms(md, x.z * inv_t); add_ms(md, x.w * inv_t);
-      add_ms(mt, y.x * inv_t); add_ms(mt, y.y * inv_t); add_ms(mt, y.z * inv_t); add_ms(mt, y.w * inv_t);
+  {
+    const int row = blockIdx.x;
+    const float* a = zd + (size_t)row * V;
+    const float* b = zt + (size_t)row * V;
+    MaxSum md{-INFINITY, 0.0f}, mt{-INFINITY, 0.0f};
+    if (vec) {
+      const float4* a4 = reinterpret_cast<const float4*>(a);
+      const float4* b4 = reinterpret_cast<const float4*>(b);
+      for (int p = t; p < (V >> 2); p += kAccT) {
+        const float4 x = a4[p];
+        const float4 y = b4[p];
+        add4(md, x.x * k2, x.y * k2, x.z * k2, x.w * k2);
+        add4(mt, y.x * k2, y.y * k2, y.z * k2, y.w * k2);
+      }
+    } else {
+      for (int v = t; v < V; v += kAccT) {
+        add4(md, a[v] * k2, -INFINITY, -INFINITY, -INFINITY);
+        add4(mt, b[v] * k2, -INFINITY, -INFINITY, -INFINITY);
+      }
     }
-  } else {
-    for (int v = t; v < V; v += kRowT) {
-      add_ms(md, a[v] * inv_t);
-      add_ms(mt, b[v] * inv_t);
+    md = block_ms(md, shd);
+    mt = block_ms(mt, sht);
+    const float Ld = md.m + __log2f(md.s);
+    const float Lt = mt.m + __log2f(mt.s);
+    float acc = 0.0f;
+    auto term = [&](float x, float y) {
+      return fminf(exp2_(fmaf(x, k2, -Ld)), exp2_(fmaf(y, k2, -Lt)));
+    };
+    if (vec) {
+      const float4* a4 = reinterpret_cast<const float4*>(a);
+      const float4* b4 = reinterpret_cast<const float4*>(b);
+      for (int p = t; p < (V >> 2); p += kAccT) {
+        const float4 x = a4[p];
+        const float4 y = b4[p];
+        acc += (term(x.x, y.x) + term(x.y, y.y)) + (term(x.z, y.z) + term(x.w, y.w));
+      }
+    } else {
+      for (int v = t; v < V; v += kAccT) acc += term(a[v], b[v]);
     }
-  }
-  md = block_ms(md, shd);
-  mt = block_ms(mt, sht);
-  const float id_ = 1.0f / md.s;
-  const float it_ = 1.0f / mt.s;
-  float acc = 0.0f;
-  auto term = [&](float x, float y) {
-    return fminf(expf(x * inv_t - md.m) * id_, expf(y * inv_t - mt.m) * it_);
-  };
-  if (vec) {
-    const float4* a4 = reinterpret_cast<const float4*>(a);
-    const float4* b4 = reinterpret_cast<const float4*>(b);
-    for (int p = t; p < (V >> 2); p += kRowT) {
-      const float4 x = a4[p];
-      const float4 y = b4[p];
-      acc += (term(x.x, y.x) + term(x.y, y.y)) + (term(x.z, y.z) + term(x.w, y.w));
-    }
-  } else {
-    for (int v = t; v < V; v += kRowT) acc += term(a[v], b[v]);
-  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if ((t & 63) == 0) ssum[t >> 6] = acc;
-  __syncthreads();
-  if (t == 0) {
-    float s = 0.0f;
-    for (int j = 0; j < kRowW; ++j) s += ssum[j];
-    out[row] = s;
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((t & 63) == 0) ssum[t >> 6] = acc;
+    __syncthreads();
+    if (t == 0) {
+      float s = 0.0f;
+      for (int j = 0; j < kAccW; ++j) s += ssum[j];
+      out[row] = s;
+    }
   }
 }
 
@@ -274,8 +283,12 @@ dspark_status launch_accept_prob(const float* draft_logits, const float* target_
                                  int V, float temperature, float* out, hipStream_t stream) {
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const int vec = (V % 4 == 0) && a16(draft_logits) && a16(target_logits);
-  hipLaunchKernelGGL(accept_prob_kernel, dim3(n), dim3(kRowT), 0, stream, draft_logits,
-                     target_logits, V, 1.0f / temperature, vec, out);
+  // One 1024-thread workgroup per row pair.  (Measured: capping the grid so
+  // that workgroups loop over rows, or limiting workgroups per CU, was slower
+  // or no faster.)
+  const float k2 = 1.44269504088896341f / temperature;   // log2(e) / T
+  hipLaunchKernelGGL(accept_prob_kernel, dim3(n), dim3(kAccT), 0, stream, draft_logits,
+                     target_logits, V, k2, vec, out);
   return check_launch("accept_prob_kernel");
 }
 
