@@ -99,19 +99,21 @@ __device__ __forceinline__ void rank_items(SchedShared& sh, const uint32_t (&ck)
   }
 }
 
-// Turn per-wave counters into scatter offsets: cnt[w][d] = base[d] + sum_{w'<w} cnt[w'][d];
-// then advance base[d] by the tile's total of digit d.  Threads 0..255.
-__device__ __forceinline__ void offsets_from_base(SchedShared& sh) {
+// Single tile: per digit d (threads 0..255), cnt[w][d] becomes the count of
+// digit d in waves before w, and tot[d] the digit's total.
+__device__ __forceinline__ void wave_prefix_and_totals(SchedShared& sh) {
   if (threadIdx.x < kDig) {
     const int d = threadIdx.x;
-    int run = sh.base[d];
+    int c[kW];
+#pragma unroll
+    for (int w = 0; w < kW; ++w) c[w] = sh.cnt[w * kDig + d];
+    int run = 0;
 #pragma unroll
     for (int w = 0; w < kW; ++w) {
-      const int c = sh.cnt[w * kDig + d];
       sh.cnt[w * kDig + d] = run;
-      run += c;
+      run += c[w];
     }
-    sh.base[d] = run;
+    sh.tot[d] = run;
   }
 }
 
@@ -232,15 +234,15 @@ __device__ __forceinline__ double theta_at(int R, unsigned long long S, float sp
 // Modes 1 and 2 then sum the survivals below m* (tau*) from the sorted keys.
 template <int ITEMS, typename Load, typename SetRank, typename SpsAt>
 __device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restrict__ sps,
-                           int mode, int m_cap, int32_t* __restrict__ order, Load load,
-                           SetRank set_rank, SpsAt sps_at, Best& best) {
+                           float sps0, int mode, int m_cap, int32_t* __restrict__ order,
+                           Load load, SetRank set_rank, SpsAt sps_at, Best& best) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.carry = 0ull;
   best.theta = -1.0;
   best.m = 0x7fffffff;
   best.S = 0ull;
   if (tid == 0 && mode == 0) {
-    best.theta = (double)R * (double)sps[R - 1];  // m = 0: tau = R
+    best.theta = (double)R * (double)sps0;  // m = 0: tau = R, sps0 = sps[R - 1]
     best.m = 0;
   }
   int brk = 0x7fffffff;
@@ -374,28 +376,26 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
     const int p = threadIdx.x * ITEMS + i;
     spv[i] = (p < N && mode != 2) ? sps[R + p] : 0.0f;
   }
+  const float sps0 = (mode == 0 && threadIdx.x == 0) ? sps[R - 1] : 0.0f;
+  // Per pass four barriers: after the ranking, after the per-digit wave
+  // prefixes, after the digit scan, after the scatter.  The reload of the next
+  // pass's keys needs none after it: every wave's next scatter waits behind
+  // that pass's first barrier, and each wave only touches its own counter row
+  // between barriers.
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 8 * pass;
     zero_my_counters(sh);
     rank_items<ITEMS>(sh, ck, ok, shift, rk);
     __syncthreads();
-    // digit totals -> exclusive digit bases (single tile: the tile is the array)
-    if (threadIdx.x < kDig) {
-      int t = 0;
-#pragma unroll
-      for (int ww = 0; ww < kW; ++ww) t += sh.cnt[ww * kDig + threadIdx.x];
-      sh.tot[threadIdx.x] = t;
-    }
+    wave_prefix_and_totals(sh);
     __syncthreads();
-    scan_digits(sh, sh.tot);
-    __syncthreads();
-    offsets_from_base(sh);
+    scan_digits(sh, sh.tot);   // base[d]: items with a smaller digit
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       if (ok[i]) {
         const int d = (ck[i] >> shift) & 0xff;
-        const int dst = sh.cnt[w * kDig + d] + rk[i];
+        const int dst = sh.base[d] + sh.cnt[w * kDig + d] + rk[i];
         skey[dst] = ck[i];
         sid[dst] = id[i];
       }
@@ -410,12 +410,11 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
           id[i] = sid[e];
         }
       }
-      __syncthreads();
     }
   }
   Best best;
   scan_theta<ITEMS>(
-      sh, N, R, sps, mode, m_cap, order,
+      sh, N, R, sps, sps0, mode, m_cap, order,
       [&](int p, uint32_t& k, int& i) { k = skey[p]; i = sid[p]; },
       [&](int i, int p) { sid[i] = p; }, [&](int, int i) { return spv[i]; }, best);
   write_results(R, gamma, best, sid, lengths, info);
