@@ -624,9 +624,14 @@ constexpr int kSplitUnroll = lcm_small(kSplitWD, kSplitPD + 1);
 
 constexpr int kSplitBufs = kSplitWD + 1;   // LDS stage buffers (direct loads run WD ahead)
 
+// W1 staging per wave: 32 rows x 256 bf16 (its K half of rank 512).
+constexpr int kGatherWave = 32 * 256;
+
 template <int NP>
 constexpr size_t ksplit_lds_bytes() {
-  return (size_t)kSplitBufs * kChunk * kPitch512 * 2 + (size_t)2 * (2 * NP) * 64 * 8 * 4;
+  const size_t loop = (size_t)kSplitBufs * kChunk * kPitch512 * 2 + (size_t)2 * (2 * NP) * 64 * 8 * 4;
+  const size_t gather = (size_t)(2 * NP) * kGatherWave * 2;
+  return loop > gather ? loop : gather;
 }
 
 // One K-split workgroup (its LDS stages and exchange buffer) fills a CU's LDS:
@@ -683,16 +688,38 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   const int m_loc = pair * 32 + col;
   const int m = rb * ROWS + m_loc;
   const bool m_ok = m < R;
+  // W1 rows, staged through LDS before anything else uses it: each wave copies
+  // its 32 rows' K half (32 x 512 B) with direct loads that each move two
+  // contiguous row halves (a row-major gather straight into registers touches
+  // 32 lines per instruction).  Piece c of row q is stored in slot c ^ q, so
+  // the reads below, one row per lane, spread over the banks.  The W2
+  // prologue waits behind this (the staging area covers the stage buffers).
   bf16x8 e[KH];
   {
     int x = step_input(io, m, m_ok, vg == 0 && kh == 0 && half == 0, V);
     x = min(max(x, 0), V - 1);
-    const uint16_t* er = W1 + (size_t)x * r + half * 8;
+    const u32x4 dw1 = raw_desc(W1, (uint32_t)V * (uint32_t)r * 2u);
+    uint16_t* greg = lds + wave * kGatherWave;
+    const int c = lane & 31;
 #pragma unroll
-    for (int s = 0; s < KH; ++s) {
-      const int ks = kh * KH + s;
-      e[s] = (ks * 16 < r && m_ok) ? ld_bf16x8(er + ks * 16) : bf16x8{};
+    for (int i = 0; i < 16; ++i) {
+      const int q = 2 * i + (lane >> 5);
+      const int xq = __shfl(x, q);
+      const bool okq = rb * ROWS + pair * 32 + q < R;
+      const int piece = c ^ q;
+      const uint32_t voff = (okq && kh * 256 + piece * 8 < r)
+                                ? (uint32_t)xq * (uint32_t)r * 2u + (uint32_t)(kh * 512 + piece * 16)
+                                : kOutOfRange;
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(voff), "s"(dw1), "{m0}"(lds_addr(greg + 2 * i * 256))
+                   : "memory");
     }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int s = 0; s < KH; ++s)
+      e[s] = *reinterpret_cast<const bf16x8*>(greg + col * 256 + (((2 * s + half) ^ col) & 31) * 8);
+    lds_barrier();   // every wave has its rows before the stage buffers are reused
   }
 
   const u32x4 dw2 = raw_desc(W2, (uint32_t)V * (uint32_t)r * 2u);
