@@ -317,6 +317,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // VMEM instructions one epi_load issues (they count in vmcnt with the DMA).
+// Exact for the 16-byte path; the scalar path's consecutive four-byte loads
+// may be merged by the compiler, so waits never rely on that count.
 template <int MODE, bool VEC4, int NJ>
 constexpr int epi_load_count() {
   return MODE == kBiasOnly ? 0 : (VEC4 ? NJ : 4 * NJ) * (MODE == DSPARK_SAMPLE ? 2 : 1);
@@ -387,6 +389,16 @@ __device__ __forceinline__ int n_whole(int c0, int cstep, int n_valid, int V) {
 // ---------------------------------------------------------------------------
 template <int RK, int NW>
 constexpr bool plain_deep() { return RK == 512 && NW == 4; }
+// W1 rows of all the workgroup's tiles staged through LDS (register-staged W2
+// ranks only, and only if they fit in the CU's LDS).
+template <int RK, int NW, int TW>
+constexpr bool plain_lds_gather() { return RK < 512 && NW * TW * 32 * RK * 2 <= 160 * 1024; }
+template <int RK, int NW, int TW>
+constexpr size_t plain_lds_bytes() {
+  const size_t stage = (size_t)(RK == 512 ? (plain_deep<RK, NW>() ? 3 : 2) : 2) * 32 * (RK + 8) * 2;
+  const size_t gather = plain_lds_gather<RK, NW, TW>() ? (size_t)NW * TW * 32 * RK * 2 : 0;
+  return stage > gather ? stage : gather;
+}
 template <int RK, int NW>
 constexpr int plain_wd() { return plain_deep<RK, NW>() ? 2 : 1; }   // W2 chunks staged ahead
 template <int RK, int NW>
@@ -422,10 +434,14 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   constexpr bool DMA = RK == 512;                  // W2 staged by direct loads into LDS
   constexpr int NBUF = DMA ? WD + 1 : 2;           // LDS stage buffers
   static_assert(TW == 1 || !DMA, "two tiles per wave only with register staging");
+  // W1 rows staged through LDS (see plain_lds_gather) when they fit.
+  constexpr bool LDSG = plain_lds_gather<RK, NW, TW>();
   // vmcnt at the top of an iteration that leaves only the loads issued after
   // the DMA of its own chunk outstanding (0 with bias stores in flight).
   constexpr int EL = epi_load_count<MODE, VEC4, 4>();
-  constexpr int DMA_WAIT = BIAS ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
+  // The scalar epilogue's four-byte loads may be merged by the compiler into
+  // fewer instructions, so only the 16-byte path has a count to rely on.
+  constexpr int DMA_WAIT = (BIAS || !VEC4) ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -451,6 +467,7 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   // Tile t of this wave holds requests (wave * TW + t) * 32 + col of the R block.
   int m[TW];
   bool m_ok[TW];
+  int xt[TW];
   uint32_t e_off[TW];
   bf16x8 e[TW][KS];
 #pragma unroll
@@ -460,11 +477,13 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
     m_ok[t] = m[t] < R;
     e_off[t] = (uint32_t)(m_loc * ad.row_stride + 4 * half) * 4u;
     int x = step_input(io, m[t], m_ok[t], vg == 0 && half == 0, V);
-    x = min(max(x, 0), V - 1);                          // out-of-range ids never fault
-    const uint16_t* er = W1 + (size_t)x * r + half * 8;
+    xt[t] = min(max(x, 0), V - 1);                      // out-of-range ids never fault
+    if constexpr (!LDSG) {
+      const uint16_t* er = W1 + (size_t)xt[t] * r + half * 8;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      e[t][s] = (s * 16 < r && m_ok[t]) ? ld_bf16x8(er + s * 16) : bf16x8{};
+      for (int s = 0; s < KS; ++s)
+        e[t][s] = (s * 16 < r && m_ok[t]) ? ld_bf16x8(er + s * 16) : bf16x8{};
+    }
   }
 
   const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
@@ -556,6 +575,38 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // W1 rows through LDS: each wave copies its tiles' rows (32 x RK bf16 each)
+  // with direct loads that move whole rows (1 KB per instruction: 512 / RK
+  // rows); piece c of row q sits in slot c ^ (q mod pieces per row), so the
+  // one-row-per-lane reads spread over the banks.  The register staging of W2
+  // and the epilogue prefetch below are issued before the wait, which counts
+  // them from the back.
+  constexpr int PPR = RK / 8;       // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;     // rows per direct load
+  if constexpr (LDSG) {
+    const u32x4 dw1 = raw_desc(W1, (uint32_t)V * (uint32_t)r * 2u);
+    const int c = lane % PPR;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      uint16_t* greg = lds + (wave * TW + t) * 32 * RK;
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int q = i * RPI + lane / PPR;
+        const int xq = __shfl(xt[t], q);
+        const bool okq = rb * ROWS + (wave * TW + t) * 32 + q < R;
+        const int piece = c ^ (q & (PPR - 1));
+        const uint32_t voff = (okq && piece * 8 < r)
+                                  ? (uint32_t)xq * (uint32_t)r * 2u + (uint32_t)(piece * 16)
+                                  : kOutOfRange;
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(voff), "s"(dw1), "{m0}"(lds_addr(greg + i * RPI * RK))
+                     : "memory");
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
   // Prologue loads in the order they are consumed (oldest first), so that the
   // waits at the top of the loop can count them from the back.
 #pragma unroll
@@ -571,6 +622,21 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
                                 e_off[u] + (uint32_t)chunk(t) * e_cb);
     }
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (LDSG) {
+    // Everything is waited for: the prologue loads were issued right behind
+    // the staging and land at about the same time (and the compiler may merge
+    // the scalar epilogue loads, so a count of them is not reliable).
+    wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const uint16_t* greg = lds + (wave * TW + t) * 32 * RK + col * RK;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        e[t][s] = *reinterpret_cast<const bf16x8*>(greg + (((2 * s + half) ^ (col & (PPR - 1))) * 8));
+    }
+    lds_barrier();   // every wave has its rows before the stage buffers are written
   }
   // The first UNR iterations (the first has nothing to finish) and those from
   // n_main on use the masked select; in between every finished chunk lies
@@ -659,10 +725,11 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   constexpr int NBUF = kSplitBufs;
   constexpr int EL = epi_load_count<MODE, VEC4, 2>();
   // vmcnt at the top of an iteration that leaves only the loads issued after
-  // the DMA of its own chunk outstanding (0 with bias stores in flight).  With
-  // WD = 1 those are the previous iteration's epilogue loads, which also
-  // retires the epilogue inputs this iteration uses.
-  constexpr int DMA_WAIT = BIAS ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
+  // the DMA of its own chunk outstanding (0 with bias stores in flight, and 0
+  // with the scalar epilogue, whose four-byte loads the compiler may merge
+  // into fewer instructions).  With WD = 1 those are the previous iteration's
+  // epilogue loads, which also retires the epilogue inputs this iteration uses.
+  constexpr int DMA_WAIT = (BIAS || !VEC4) ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
   static_assert(PITCH == kPitch512, "rank-512 pitch");
 
   const int tid = threadIdx.x;
@@ -716,6 +783,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
                    : "memory");
     }
     wait_vmcnt<0>();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KH; ++s)
       e[s] = *reinterpret_cast<const bf16x8*>(greg + col * 256 + (((2 * s + half) ^ col) & 31) * 8);
@@ -877,9 +945,8 @@ struct StepVariant {
 
 template <int RK, int NW, int MODE, bool VEC4, bool BIAS, int TW = 1>
 StepVariant plain_variant() {
-  return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS, TW>, NW * 64,
-          (size_t)(RK == 512 ? plain_wd<RK, NW>() + 1 : 2) * kChunk * (RK + 8) * 2, NW * 32 * TW,
-          plain_unroll<RK, NW>()};
+  return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS, TW>, NW * 64, plain_lds_bytes<RK, NW, TW>(),
+          NW * 32 * TW, plain_unroll<RK, NW>()};
 }
 template <int NP, int MODE, bool VEC4, bool BIAS>
 StepVariant ksplit_variant() {

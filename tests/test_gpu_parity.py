@@ -105,6 +105,9 @@ EDGE = [
     (70, 4, 3000, 256, 100, SAMPLE),    # partial R blocks, d % 8 != 0
     (3, 6, 64, 512, 16, GREEDY),        # V smaller than a chunk group, r = 512
     (300, 2, 777, 64, 64, GREEDY),      # two 256-request blocks, last one partial
+    (40, 3, 1001, 512, 16, SAMPLE),     # rank 512 (K-split) with the scalar epilogue
+    (40, 3, 1001, 512, 16, GREEDY),     # rank 512 (plain, direct-to-LDS W2), scalar epilogue
+    (130, 2, 999, 256, 16, GREEDY),     # rank 256, 4-wave blocks, scalar epilogue
 ]
 
 
@@ -118,16 +121,18 @@ def test_edge_shapes(R, g, V, r, d, mode, layout):
     _full_path_check(wl, layout=layout)
 
 
-def test_unaligned_base_uses_scalar_path():
-    _say("case unaligned base")
-    cfg = Config("edge", R=6, gamma=3, V=4096, r=64, d=32, w_std=0.2, seed=7)
+@pytest.mark.parametrize("r,mode", [(64, GREEDY), (512, GREEDY), (512, SAMPLE)])
+def test_unaligned_base_uses_scalar_path(r, mode):
+    _say(f"case unaligned base r={r} mode={mode}")
+    cfg = Config("edge", R=6, gamma=3, V=4096, r=r, d=32, w_std=0.2, mode=mode, seed=7)
     wl = make_workload(cfg)
     g = H.to_device(wl, DEV)
     R, gm, V = wl["base"].shape
     big = torch.empty(R * gm * V + 1, dtype=torch.float32, device=DEV)
     base = big[1:].view(R, gm, V)
     base.copy_(g["base"])
-    tok = D.dspark_markov_draft(g["W1"], g["W2"], base, g["anchors"], GREEDY)
+    tok = D.dspark_markov_draft(g["W1"], g["W2"], base, g["anchors"], mode, wl["temperature"],
+                                g.get("uniforms"))
     toks = tok.cpu().numpy()
     H.check_draft(wl, toks)
 
