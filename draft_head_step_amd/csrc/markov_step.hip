@@ -43,6 +43,7 @@
 //     of chunk c).
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -998,24 +999,30 @@ StepVariant pick_variant(const MarkovPlan& p, int mode, bool vec4, bool bias) {
                                : pick2<DSPARK_GREEDY>(p, vec4, bias);
 }
 
-// Per-kernel launch attributes and occupancy, resolved once per variant.
+// Per-kernel launch attributes and occupancy, resolved once per variant and
+// device (host threads may call concurrently).
 struct VariantState {
   StepKernel fn;
+  int device;
   int blocks_per_cu;
 };
-VariantState g_states[256];
+VariantState g_states[512];
 int g_nstates = 0;
+std::mutex g_states_mu;
 
 int prepare_variant(const StepVariant& v) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(g_states_mu);
   for (int i = 0; i < g_nstates; ++i)
-    if (g_states[i].fn == v.fn) return g_states[i].blocks_per_cu;
+    if (g_states[i].fn == v.fn && g_states[i].device == dev) return g_states[i].blocks_per_cu;
   const void* f = reinterpret_cast<const void*>(v.fn);
   if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)v.lds) != hipSuccess)
     return -1;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, v.threads, v.lds) != hipSuccess || nb < 1)
     nb = 1;
-  if (g_nstates < 256) g_states[g_nstates++] = {v.fn, nb};
+  if (g_nstates < 512) g_states[g_nstates++] = {v.fn, dev, nb};
   return nb;
 }
 

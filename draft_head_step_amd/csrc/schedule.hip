@@ -18,6 +18,8 @@
 // all in LDS in a single launch.  Beyond that the sort and the scan are spread
 // over tiles of 1024 candidates on the whole device through workspace buffers
 // (a dozen short launches, no host sync).
+#include <atomic>
+
 #include "dspark_internal.h"
 
 namespace dspark {
@@ -891,12 +893,16 @@ dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, 
                          int m_cap, int32_t* lengths, int32_t* order, dspark_schedule_info* info,
                          hipStream_t stream) {
   const size_t lds = sizeof(SchedShared) + (size_t)kT * ITEMS * 8;
-  static bool attr = false;
-  if (!attr) {
+  // The dynamic-LDS attribute, set once per device (bit d of `done`).
+  static std::atomic<unsigned long long> done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DSPARK_EDEVICE, "hipGetDevice failed");
+  const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+  if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_lds_kernel<ITEMS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the schedule kernel");
-    attr = true;
+    done.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL(schedule_lds_kernel<ITEMS>, dim3(1), dim3(kT), lds, stream, surv, sps, R,
                      gamma, N, mode, m_cap, lengths, order, info);

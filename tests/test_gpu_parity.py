@@ -75,6 +75,38 @@ def test_deterministic_repeat():
     assert np.array_equal(a, b) and np.array_equal(ba.view(np.uint32), bb.view(np.uint32))
 
 
+def test_concurrent_host_threads_on_separate_streams():
+    # Two host threads, each with its own stream, outputs and workspace (the
+    # documented condition for concurrent calls), draft the same batch: every
+    # result equals the single-threaded one.
+    _say("case concurrent host threads")
+    import threading
+    wl = make_workload(CONFIGS["tiny"], w_std=0.3)
+    g = H.to_device(wl, DEV)
+    ref = D.dspark_markov_draft(g["W1"], g["W2"], g["base"], g["anchors"], GREEDY).cpu().numpy()
+    results, errors = [], []
+
+    def worker():
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(5):
+                    t = D.dspark_markov_draft(g["W1"], g["W2"], g["base"], g["anchors"], GREEDY,
+                                              stream=st)
+                    st.synchronize()
+                    results.append(t.cpu().numpy())
+        except Exception as exc:  # noqa: BLE001
+            errors.append(exc)
+
+    th = [threading.Thread(target=worker) for _ in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    assert len(results) == 10 and all(np.array_equal(r, ref) for r in results)
+
+
 def test_workspace_contents_do_not_matter():
     # The call clears the words it combines into: a workspace full of 0xff, and
     # the same workspace again after a call on other inputs, give the same tokens.
