@@ -153,6 +153,17 @@ def test_edge_shapes(R, g, V, r, d, mode, layout):
     _full_path_check(wl, layout=layout)
 
 
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
+def test_largest_row_major_vocabulary(layout):
+    # gamma * V just below 2^22, the row-major limit of 32-bit element offsets
+    # per request block (the tiled layout takes the same V).
+    V = (1 << 22) - 32
+    _say(f"case V={V} layout={layout}")
+    cfg = Config("edge", R=5, gamma=1, V=V, r=64, d=16, w_std=0.2, base_std=1.0, seed=31)
+    wl = make_workload(cfg)
+    _full_path_check(wl, layout=layout)
+
+
 @pytest.mark.parametrize("r,mode", [(64, GREEDY), (512, GREEDY), (512, SAMPLE)])
 def test_unaligned_base_uses_scalar_path(r, mode):
     _say(f"case unaligned base r={r} mode={mode}")
@@ -253,6 +264,16 @@ def test_schedule_capacity_step_is_top_k(K):
     sps = (np.arange(1, R * (1 + g) + 1) <= K).astype(np.float32)
     ref = _sched_case(c, sps)
     assert ref["B_star"] == K
+
+
+def test_schedule_at_the_candidate_limit():
+    # R * gamma = DSPARK_MAX_CANDIDATES = 2^23: 8192 tiles on the tiled path.
+    _say("case schedule at 2^23 candidates")
+    R, g = 1 << 20, 8
+    rng = np.random.default_rng(23)
+    c = rng.uniform(0.05, 1.0, size=(R, g)).astype(np.float32)
+    from draft_head_step_amd.inputs import sps_table
+    _sched_case(c, sps_table("staircase", R * (1 + g)))
 
 
 def test_sched_stress_workload():
