@@ -7,9 +7,9 @@ dspark_confidence (confidence head, STS, survival), then dspark_schedule
 DeepSeek-V4-shaped drafter: R = 256 requests, gamma = 5, V = 129280,
 Markov rank r = 512, hidden d = 7168, Gumbel-max sampling at T = 1.
 
-The base logits and uniforms are handed over in the chunk-tiled layout
-([gamma][ceil(V/32)][R][32], what a producer that writes them tile by tile
-emits) by default; the row-major [R][gamma][V] layout is timed in the same run
+The base logits and uniforms are handed over in the column-tiled layout
+([gamma][ceil(V/32)][32][R], what an LM-head GEMM that writes its logits
+transposed, or a random-number fill, emits) by default; the row-major [R][gamma][V] layout is timed in the same run
 and reported beside it (``row_major``).
 
 Prints one JSON line with the throughput, the roofline position of the
@@ -110,13 +110,13 @@ def device_workload(cfg, dev, seed=None):
 
 
 def tiled_on_device(x):
-    """[R, gamma, V] -> [gamma, ceil(V/32), R, 32] on the device (tail columns zero)."""
+    """[R, gamma, V] -> column-tiled [gamma, ceil(V/32), 32, R] on the device (tail entries zero)."""
     import torch
     R, g, V = x.shape
     C = (V + 31) // 32
     if C * 32 != V:
         x = torch.nn.functional.pad(x, (0, C * 32 - V))
-    return x.view(R, g, C, 32).permute(1, 2, 0, 3).contiguous()
+    return x.view(R, g, C, 32).permute(1, 2, 3, 0).contiguous()
 
 
 def cpu_baseline(wl):

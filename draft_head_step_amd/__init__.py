@@ -29,7 +29,7 @@ __all__ = [
 GREEDY = 0
 SAMPLE = 1
 LAYOUT_RGV = 0     # base / uniforms / bias_out as [R, gamma, V]
-LAYOUT_TILED = 1   # [gamma, ceil(V/32), R, 32]
+LAYOUT_TILED = 1   # [gamma, ceil(V/32), 32, R]
 SCHED_GLOBAL = 0       # dspark_schedule_ex admission rules
 SCHED_EARLY_STOP = 1
 SCHED_CAPACITY = 2
@@ -155,7 +155,7 @@ def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: 
                         events=None, stream=None, layout: int = LAYOUT_RGV, gamma=None):
     """gamma-step Markov-head draft.  W1, W2 [V, r] bf16; anchors [R] int32; base (and
     uniforms, SAMPLE only; bias_out, optional) fp32 as [R, gamma, V] (LAYOUT_RGV) or
-    [gamma, ceil(V/32), R, 32] (LAYOUT_TILED).  Returns tokens [R, gamma] int32.
+    [gamma, ceil(V/32), 32, R] (LAYOUT_TILED).  Returns tokens [R, gamma] int32.
     ``base=None`` (GREEDY only, ``gamma`` given) drafts from the Markov bias alone.
 
     ``events`` is an optional pair (begin, end) of sequences of hipEvent_t handles (ints)
@@ -170,7 +170,7 @@ def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: 
             raise ValueError("gamma must be given when base is None")
         gamma = base.shape[0] if layout == LAYOUT_TILED else base.shape[1]
     if layout == LAYOUT_TILED:
-        shape = (gamma, (V + 31) // 32, R, 32)
+        shape = (gamma, (V + 31) // 32, 32, R)
     else:
         shape = (R, gamma, V)
     _need(W1, "W1", _bf16_types(), (V, r), dev)

@@ -91,8 +91,10 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
       return fail(DSPARK_EUNSUPPORTED, "markov_draft: ceil(V/32)*32*r above 2^30");
     if (layout == DSPARK_LAYOUT_RGV && (uint64_t)gamma * (uint64_t)V >= (1ull << 22))
       return fail(DSPARK_EUNSUPPORTED, "markov_draft: gamma*V must be below 2^22 in the RGV layout");
-    if (layout == DSPARK_LAYOUT_TILED && C * (uint64_t)R + 256 > (1ull << 25))
-      return fail(DSPARK_EUNSUPPORTED, "markov_draft: ceil(V/32)*R + 256 above 2^25 in the tiled layout");
+    // Tiled: one step (C * 32 * R floats) stays below 2^31 bytes, so an offset
+    // pushed out of range by 2^31 is never back in range.
+    if (layout == DSPARK_LAYOUT_TILED && C * (uint64_t)R >= (1ull << 24))
+      return fail(DSPARK_EUNSUPPORTED, "markov_draft: ceil(V/32)*R must be below 2^24 in the tiled layout");
   }
   if (events && (events->count < gamma))
     return fail(DSPARK_EINVAL, "markov_draft: events->count < gamma");

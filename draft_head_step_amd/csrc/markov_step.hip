@@ -217,13 +217,19 @@ __device__ __forceinline__ u32x4 buf_load16(Rsrc r, uint32_t off) {
 __device__ __forceinline__ float buf_load4(Rsrc r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// Four-byte load of a stream read once (non-temporal: the line is not kept in
+// the caches).  The uniform part of the offset rides in soffset, which the
+// range check does not cover: an out-of-range lane must carry it in `off`.
+__device__ __forceinline__ float buf_load4_nt(Rsrc r, uint32_t off, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 2));
+}
 
 // Element (m, k, v) of base / uniforms / bias_out is at float offset
-// k_off + m * row_stride + (v / 32) * cstride + v % 32 in either layout; total
-// is the array's length in floats.  Byte offsets inside one R block of one
-// step fit in 32 bits (checked on the host).
+// k_off + m * row_stride + (v / 32) * cstride + (v % 32) * vstride in either
+// layout; block_rsrc covers [block start, total).  Byte offsets inside one R
+// block of one step fit in 32 bits (checked on the host).
 struct Addr {
-  size_t k_off, row_stride, cstride, total;
+  size_t k_off, row_stride, cstride, vstride, total;
 };
 
 // Buffer resource over the rows of R block `rb` (first row rb * rows) at step k.
@@ -317,20 +323,33 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
 }
 
+// How the epilogue reads the logits and uniforms of a chunk.
+//   kEpiScalar  row-major, four-byte loads (any alignment);
+//   kEpiVec4    row-major, 16-byte loads (each row's 128-byte slice of a chunk
+//               takes four instructions per half-wave);
+//   kEpiCol     column-tiled: for one vocabulary entry the 32 requests of a
+//               tile are 128 contiguous bytes, so every four-byte load
+//               instruction reads whole lines, which go non-temporal.
+constexpr int kEpiScalar = 0;
+constexpr int kEpiVec4 = 1;
+constexpr int kEpiCol = 2;
+
 // VMEM instructions one epi_load issues (they count in vmcnt with the DMA).
-// Exact for the 16-byte path; the scalar path's consecutive four-byte loads
-// may be merged by the compiler, so waits never rely on that count.
-template <int MODE, bool VEC4, int NJ>
+// Exact for the 16-byte and column paths (the column loads differ in soffset
+// only, which no merge combines); the scalar path's consecutive four-byte
+// loads may be merged by the compiler, so waits never rely on that count.
+template <int MODE, int EPI, int NJ>
 constexpr int epi_load_count() {
-  return MODE == kBiasOnly ? 0 : (VEC4 ? NJ : 4 * NJ) * (MODE == DSPARK_SAMPLE ? 2 : 1);
+  return MODE == kBiasOnly ? 0 : (EPI == kEpiVec4 ? NJ : 4 * NJ) * (MODE == DSPARK_SAMPLE ? 2 : 1);
 }
 
 // Epilogue inputs of NJ accumulator groups (jq = j0 .. j0+NJ-1) of one chunk for
 // one lane: element 4*j + i is vocabulary entry v0 + 8*(j0+j) + 4*half + i; `off`
-// is the lane's byte offset of entry v0 + 8*j0 + 4*half.
-template <int MODE, bool VEC4, int NJ>
+// is the lane's byte offset of entry v0 + 8*j0 + 4*half and `vs` the byte
+// distance between consecutive entries of the column layout.
+template <int MODE, int EPI, int NJ>
 __device__ __forceinline__ void epi_load(float (&bv)[4 * NJ], float (&uv)[4 * NJ], Rsrc rbase,
-                                         Rsrc runif, uint32_t off) {
+                                         Rsrc runif, uint32_t off, int vs) {
   if (MODE == kBiasOnly) {
 #pragma unroll
     for (int j = 0; j < 4 * NJ; ++j) bv[j] = 0.0f;
@@ -338,7 +357,14 @@ __device__ __forceinline__ void epi_load(float (&bv)[4 * NJ], float (&uv)[4 * NJ
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    if (VEC4) {
+    if (EPI == kEpiCol) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int so = (8 * j + i) * vs;
+        bv[4 * j + i] = buf_load4_nt(rbase, off, so);
+        if (MODE == DSPARK_SAMPLE) uv[4 * j + i] = buf_load4_nt(runif, off, so);
+      }
+    } else if (EPI == kEpiVec4) {
       const float4 t = __builtin_bit_cast(float4, buf_load16(rbase, off + 32u * j));
       bv[4 * j + 0] = t.x; bv[4 * j + 1] = t.y; bv[4 * j + 2] = t.z; bv[4 * j + 3] = t.w;
       if (MODE == DSPARK_SAMPLE) {
@@ -414,7 +440,7 @@ constexpr int plain_unroll() { return lcm_small(plain_wd<RK, NW>(), plain_pd<RK,
 template <int RK>
 constexpr int plain_max_waves() { return RK == 512 ? 2 : 8; }
 
-template <int RK, int NW, int MODE, bool VEC4, bool BIAS, int TW>
+template <int RK, int NW, int MODE, int EPI, bool BIAS, int TW>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
@@ -439,10 +465,11 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   constexpr bool LDSG = plain_lds_gather<RK, NW, TW>();
   // vmcnt at the top of an iteration that leaves only the loads issued after
   // the DMA of its own chunk outstanding (0 with bias stores in flight).
-  constexpr int EL = epi_load_count<MODE, VEC4, 4>();
+  constexpr int EL = epi_load_count<MODE, EPI, 4>();
   // The scalar epilogue's four-byte loads may be merged by the compiler into
-  // fewer instructions, so only the 16-byte path has a count to rely on.
-  constexpr int DMA_WAIT = (BIAS || !VEC4) ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
+  // fewer instructions, so only the 16-byte and column paths have a count to
+  // rely on.
+  constexpr int DMA_WAIT = (BIAS || EPI == kEpiScalar) ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -476,7 +503,11 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
     const int m_loc = (wave * TW + t) * 32 + col;
     m[t] = rb * ROWS + m_loc;
     m_ok[t] = m[t] < R;
-    e_off[t] = (uint32_t)(m_loc * ad.row_stride + 4 * half) * 4u;
+    // Row-major rows past R lie past the block's range; column-layout rows
+    // past R would alias the next entries, so they are sent out of range.
+    e_off[t] = (EPI == kEpiCol && !m_ok[t])
+                   ? kOutOfRange
+                   : (uint32_t)(m_loc * ad.row_stride + 4 * half * ad.vstride) * 4u;
     int x = step_input(io, m[t], m_ok[t], vg == 0 && half == 0, V);
     xt[t] = min(max(x, 0), V - 1);                      // out-of-range ids never fault
     if constexpr (!LDSG) {
@@ -493,6 +524,8 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   const Rsrc rbase = MODE == kBiasOnly ? make_rsrc(W2, 0u) : block_rsrc(base, ad, rb, ROWS);
   const Rsrc runif = MODE == DSPARK_SAMPLE ? block_rsrc(unif, ad, rb, ROWS) : rbase;
   const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
+  const size_t vstride = EPI == kEpiCol ? ad.vstride : 1;
+  const int e_vs = (int)vstride * 4;
 
   u32x4 stage[DMA ? 1 : WD][DMA ? 1 : PMAX];
   float eb[NS][TW][16];
@@ -520,7 +553,7 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
 #pragma unroll
         for (int qq = 0; qq < 16; ++qq) {
           const int o = 8 * (qq >> 2) + 4 * half + (qq & 3);
-          if (cv + o < vlim) oc[o] = acc[t][qq];
+          if (cv + o < vlim) oc[o * vstride] = acc[t][qq];
         }
       }
     }
@@ -570,7 +603,8 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
     if constexpr (RK == 512) mfma_pipeline<KS>();
 #pragma unroll
     for (int t = 0; t < TW; ++t)
-      epi_load<MODE, VEC4, 4>(pb[t], pu[t], rbase, runif, e_off[t] + (uint32_t)chunk(i + PD) * e_cb);
+      epi_load<MODE, EPI, 4>(pb[t], pu[t], rbase, runif, e_off[t] + (uint32_t)chunk(i + PD) * e_cb,
+                             e_vs);
     // Keep each chunk's arithmetic in its own iteration: hoisting the noise of
     // a prefetched chunk next to its load would wait for that load.
     __builtin_amdgcn_sched_barrier(0);
@@ -619,8 +653,8 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
     if (t < PD) {
 #pragma unroll
       for (int u = 0; u < TW; ++u)
-        epi_load<MODE, VEC4, 4>(eb[t][u], eu[t][u], rbase, runif,
-                                e_off[u] + (uint32_t)chunk(t) * e_cb);
+        epi_load<MODE, EPI, 4>(eb[t][u], eu[t][u], rbase, runif,
+                               e_off[u] + (uint32_t)chunk(t) * e_cb, e_vs);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -703,7 +737,7 @@ constexpr size_t ksplit_lds_bytes() {
 
 // One K-split workgroup (its LDS stages and exchange buffer) fills a CU's LDS:
 // at most two waves per SIMD.
-template <int NP, int MODE, bool VEC4, bool BIAS>
+template <int NP, int MODE, int EPI, bool BIAS>
 __global__ __launch_bounds__(NP * 128)
 __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
@@ -724,13 +758,13 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   constexpr int NS = PD + 1;
   constexpr int UNR = kSplitUnroll;
   constexpr int NBUF = kSplitBufs;
-  constexpr int EL = epi_load_count<MODE, VEC4, 2>();
+  constexpr int EL = epi_load_count<MODE, EPI, 2>();
   // vmcnt at the top of an iteration that leaves only the loads issued after
   // the DMA of its own chunk outstanding (0 with bias stores in flight, and 0
   // with the scalar epilogue, whose four-byte loads the compiler may merge
   // into fewer instructions).  With WD = 1 those are the previous iteration's
   // epilogue loads, which also retires the epilogue inputs this iteration uses.
-  constexpr int DMA_WAIT = (BIAS || !VEC4) ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
+  constexpr int DMA_WAIT = (BIAS || EPI == kEpiScalar) ? 0 : EL + (WD - 1) * (kChunk / NW + EL);
   static_assert(PITCH == kPitch512, "rank-512 pitch");
 
   const int tid = threadIdx.x;
@@ -795,8 +829,13 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   const uint32_t w2_off = w2_dma_lane_offset(lane, r);
   const Rsrc rbase = MODE == kBiasOnly ? make_rsrc(W2, 0u) : block_rsrc(base, ad, rb, ROWS);
   const Rsrc runif = MODE == DSPARK_SAMPLE ? block_rsrc(unif, ad, rb, ROWS) : rbase;
-  const uint32_t e_off = (uint32_t)(m_loc * ad.row_stride + 16 * kh + 4 * half) * 4u;
+  const uint32_t e_off =
+      (EPI == kEpiCol && !m_ok)
+          ? kOutOfRange
+          : (uint32_t)(m_loc * ad.row_stride + (16 * kh + 4 * half) * ad.vstride) * 4u;
   const uint32_t e_cb = (uint32_t)ad.cstride * 4u;
+  const size_t vstride = EPI == kEpiCol ? ad.vstride : 1;
+  const int e_vs = (int)vstride * 4;
 
   float eb[NS][8];
   float eu[NS][8];
@@ -821,7 +860,7 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
 #pragma unroll
       for (int qq = 0; qq < 8; ++qq) {
         const int o = 16 * kh + 8 * (qq >> 2) + 4 * half + (qq & 3);
-        if (cv + o < vlim) oc[o] = z[qq];
+        if (cv + o < vlim) oc[o * vstride] = z[qq];
       }
     }
   };
@@ -861,14 +900,15 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) own[qq] = acc[qq];
     // The slot of iteration t-1 is free now: refill it with iteration t + PD.
-    epi_load<MODE, VEC4, 2>(nb, nu, rbase, runif, e_off + (uint32_t)chunk(t + PD) * e_cb);
+    epi_load<MODE, EPI, 2>(nb, nu, rbase, runif, e_off + (uint32_t)chunk(t + PD) * e_cb, e_vs);
     __builtin_amdgcn_sched_barrier(0);
   };
 
 #pragma unroll
   for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
     if (t < WD) w2_dma<NW>(lds + t * BUF, dw2, w2_off, chunk(t), r, wave);
-    if (t < PD) epi_load<MODE, VEC4, 2>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb);
+    if (t < PD)
+      epi_load<MODE, EPI, 2>(eb[t], eu[t], rbase, runif, e_off + (uint32_t)chunk(t) * e_cb, e_vs);
     __builtin_amdgcn_sched_barrier(0);
   }
   // Iteration t's epilogue inputs live in slot t % NS; iteration t finishes
@@ -944,59 +984,65 @@ struct StepVariant {
   int unroll;   // chunks per group must be a multiple of this
 };
 
-template <int RK, int NW, int MODE, bool VEC4, bool BIAS, int TW = 1>
+template <int RK, int NW, int MODE, int EPI, bool BIAS, int TW = 1>
 StepVariant plain_variant() {
-  return {&markov_step_kernel<RK, NW, MODE, VEC4, BIAS, TW>, NW * 64, plain_lds_bytes<RK, NW, TW>(),
+  return {&markov_step_kernel<RK, NW, MODE, EPI, BIAS, TW>, NW * 64, plain_lds_bytes<RK, NW, TW>(),
           NW * 32 * TW, plain_unroll<RK, NW>()};
 }
-template <int NP, int MODE, bool VEC4, bool BIAS>
+template <int NP, int MODE, int EPI, bool BIAS>
 StepVariant ksplit_variant() {
-  return {&markov_step_ksplit_kernel<NP, MODE, VEC4, BIAS>, NP * 128, ksplit_lds_bytes<NP>(),
+  return {&markov_step_ksplit_kernel<NP, MODE, EPI, BIAS>, NP * 128, ksplit_lds_bytes<NP>(),
           NP * 32, kSplitUnroll};
 }
 
-template <int RK, int MODE, bool VEC4, bool BIAS>
+template <int RK, int MODE, int EPI, bool BIAS>
 StepVariant plain_by_nw(int nw, int tw) {
   // Two tiles per wave: bias-only GEMM at ranks 128 and 256, 4 or 8 waves, no
   // bias output (the only combinations built; with the logits streams as well
   // the registers spill).
   if constexpr ((RK == 128 || RK == 256) && !BIAS && MODE == kBiasOnly) {
-    if (tw == 2) return nw == 8 ? plain_variant<RK, 8, MODE, VEC4, BIAS, 2>()
-                                : plain_variant<RK, 4, MODE, VEC4, BIAS, 2>();
+    if (tw == 2) return nw == 8 ? plain_variant<RK, 8, MODE, EPI, BIAS, 2>()
+                                : plain_variant<RK, 4, MODE, EPI, BIAS, 2>();
   }
   switch (nw) {
-    case 1: return plain_variant<RK, 1, MODE, VEC4, BIAS>();
-    case 2: return plain_variant<RK, 2, MODE, VEC4, BIAS>();
-    case 4: return plain_variant<RK, 4, MODE, VEC4, BIAS>();
-    default: return plain_variant<RK, 8, MODE, VEC4, BIAS>();
+    case 1: return plain_variant<RK, 1, MODE, EPI, BIAS>();
+    case 2: return plain_variant<RK, 2, MODE, EPI, BIAS>();
+    case 4: return plain_variant<RK, 4, MODE, EPI, BIAS>();
+    default: return plain_variant<RK, 8, MODE, EPI, BIAS>();
   }
 }
-template <int MODE, bool VEC4, bool BIAS>
+template <int MODE, int EPI, bool BIAS>
 StepVariant pick3(const MarkovPlan& p) {
   if (p.ksplit) {
     switch (p.nw / 2) {
-      case 1: return ksplit_variant<1, MODE, VEC4, BIAS>();
-      case 2: return ksplit_variant<2, MODE, VEC4, BIAS>();
-      default: return ksplit_variant<4, MODE, VEC4, BIAS>();
+      case 1: return ksplit_variant<1, MODE, EPI, BIAS>();
+      case 2: return ksplit_variant<2, MODE, EPI, BIAS>();
+      default: return ksplit_variant<4, MODE, EPI, BIAS>();
     }
   }
   switch (p.rk) {
-    case 64: return plain_by_nw<64, MODE, VEC4, BIAS>(p.nw, p.tw);
-    case 128: return plain_by_nw<128, MODE, VEC4, BIAS>(p.nw, p.tw);
-    case 256: return plain_by_nw<256, MODE, VEC4, BIAS>(p.nw, p.tw);
-    default: return plain_by_nw<512, MODE, VEC4, BIAS>(p.nw, p.tw);
+    case 64: return plain_by_nw<64, MODE, EPI, BIAS>(p.nw, p.tw);
+    case 128: return plain_by_nw<128, MODE, EPI, BIAS>(p.nw, p.tw);
+    case 256: return plain_by_nw<256, MODE, EPI, BIAS>(p.nw, p.tw);
+    default: return plain_by_nw<512, MODE, EPI, BIAS>(p.nw, p.tw);
   }
 }
 template <int MODE>
-StepVariant pick2(const MarkovPlan& p, bool vec4, bool bias) {
-  if (vec4) return bias ? pick3<MODE, true, true>(p) : pick3<MODE, true, false>(p);
-  return bias ? pick3<MODE, false, true>(p) : pick3<MODE, false, false>(p);
+StepVariant pick2(const MarkovPlan& p, int epi, bool bias) {
+  switch (epi) {
+    case kEpiCol: return bias ? pick3<MODE, kEpiCol, true>(p) : pick3<MODE, kEpiCol, false>(p);
+    case kEpiVec4: return bias ? pick3<MODE, kEpiVec4, true>(p) : pick3<MODE, kEpiVec4, false>(p);
+    default: return bias ? pick3<MODE, kEpiScalar, true>(p) : pick3<MODE, kEpiScalar, false>(p);
+  }
 }
-StepVariant pick_variant(const MarkovPlan& p, int mode, bool vec4, bool bias) {
-  if (mode == kBiasOnly)   // no logits stream: the vector-width choice does not arise
-    return bias ? pick3<kBiasOnly, true, true>(p) : pick3<kBiasOnly, true, false>(p);
-  return mode == DSPARK_SAMPLE ? pick2<DSPARK_SAMPLE>(p, vec4, bias)
-                               : pick2<DSPARK_GREEDY>(p, vec4, bias);
+StepVariant pick_variant(const MarkovPlan& p, int mode, int epi, bool bias) {
+  // No logits stream: the epilogue mode only decides where the bias goes.
+  if (mode == kBiasOnly) {
+    if (!bias) return pick3<kBiasOnly, kEpiVec4, false>(p);
+    return epi == kEpiCol ? pick3<kBiasOnly, kEpiCol, true>(p) : pick3<kBiasOnly, kEpiVec4, true>(p);
+  }
+  return mode == DSPARK_SAMPLE ? pick2<DSPARK_SAMPLE>(p, epi, bias)
+                               : pick2<DSPARK_GREEDY>(p, epi, bias);
 }
 
 // Per-kernel launch attributes and occupancy, resolved once per variant and
@@ -1086,9 +1132,10 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   MarkovPlan p = plan_markov(R, gamma, V, r, kmode, true);
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const bool tiled = layout == DSPARK_LAYOUT_TILED;
-  const bool vec4 = (tiled || V % 4 == 0) && V >= 4 && a16(base) &&
-                    (!uniforms || a16(uniforms)) && (!bias_out || a16(bias_out));
-  const StepVariant var = pick_variant(p, kmode, vec4, bias_out != nullptr);
+  const bool vec4 = V % 4 == 0 && a16(base) && (!uniforms || a16(uniforms)) &&
+                    (!bias_out || a16(bias_out));
+  const int epi = tiled ? kEpiCol : vec4 ? kEpiVec4 : kEpiScalar;
+  const StepVariant var = pick_variant(p, kmode, epi, bias_out != nullptr);
   p.n_rblocks = (R + var.rows - 1) / var.rows;   // the variant's requests per workgroup
   const int bpc = prepare_variant(var);
   if (bpc < 0) return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the Markov step kernel");
@@ -1128,14 +1175,19 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   const int padded_groups = (p.n_vgroups + 7) / 8 * 8;
   const dim3 grid(padded_groups * p.n_rblocks);
   const float inv_t = mode == DSPARK_SAMPLE ? 1.0f / temperature : 1.0f;
+  // Column-tiled [gamma][C][32][R]: one step is C * 32 * R floats, and each
+  // launch's range ends with its own step (rows past R are sent past it).
+  const size_t step_floats = (size_t)p.n_chunks * kChunk * R;
   Addr ad;
-  ad.row_stride = tiled ? (size_t)kChunk : (size_t)gamma * V;
-  ad.cstride = tiled ? (size_t)R * kChunk : (size_t)kChunk;
-  ad.total = tiled ? (size_t)gamma * p.n_chunks * R * kChunk : (size_t)R * gamma * V;
+  ad.row_stride = tiled ? 1 : (size_t)gamma * V;
+  ad.cstride = tiled ? (size_t)kChunk * R : (size_t)kChunk;
+  ad.vstride = tiled ? (size_t)R : 1;
+  ad.total = (size_t)R * gamma * V;
   for (int k = 0; k < gamma; ++k) {
     const StepIO io{anchors, k == 0 ? nullptr : packed + (size_t)(k - 1) * words,
                     packed + (size_t)k * words, tokens, gamma, k, sub};
-    ad.k_off = tiled ? (size_t)k * p.n_chunks * R * kChunk : (size_t)k * V;
+    ad.k_off = tiled ? (size_t)k * step_floats : (size_t)k * V;
+    if (tiled) ad.total = ad.k_off + step_floats;
     // Timing hooks ride on the dispatch itself (start / stop timestamps of the
     // kernel's packet), so they add no marker packets between kernels.
     hipEvent_t ev_begin = nullptr, ev_end = nullptr;

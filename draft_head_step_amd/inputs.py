@@ -169,18 +169,18 @@ def open_uniforms(rng: np.random.Generator, shape) -> np.ndarray:
 
 
 def to_tiled(x: np.ndarray) -> np.ndarray:
-    """[R, gamma, V] -> chunk-tiled [gamma, ceil(V/32), R, 32] (tail columns zero)."""
+    """[R, gamma, V] -> column-tiled [gamma, ceil(V/32), 32, R] (tail entries zero)."""
     R, g, V = x.shape
     C = (V + 31) // 32
     pad = np.zeros((R, g, C * 32), dtype=x.dtype)
     pad[:, :, :V] = x
-    return np.ascontiguousarray(pad.reshape(R, g, C, 32).transpose(1, 2, 0, 3))
+    return np.ascontiguousarray(pad.reshape(R, g, C, 32).transpose(1, 2, 3, 0))
 
 
 def from_tiled(t: np.ndarray, V: int) -> np.ndarray:
-    """Chunk-tiled [gamma, C, R, 32] -> [R, gamma, V]."""
-    g, C, R, _ = t.shape
-    return np.ascontiguousarray(t.transpose(2, 0, 1, 3).reshape(R, g, C * 32)[:, :, :V])
+    """Column-tiled [gamma, C, 32, R] -> [R, gamma, V]."""
+    g, C, _, R = t.shape
+    return np.ascontiguousarray(t.transpose(3, 0, 1, 2).reshape(R, g, C * 32)[:, :, :V])
 
 
 def sps_table(kind: str, b_max: int) -> np.ndarray:

@@ -64,12 +64,14 @@ typedef enum {
  * uniforms, bias_out).  Element (m, k, v) -- request m, position k (0-based),
  * vocabulary entry v -- sits at
  *   DSPARK_LAYOUT_RGV:   (m * gamma + k) * V + v                     (row-major [R][gamma][V])
- *   DSPARK_LAYOUT_TILED: ((k * C + v / 32) * R + m) * 32 + v % 32,  C = ceil(V / 32)
- * The tiled order ([gamma][C][R][32], tail columns of the last chunk padding)
- * puts the 32-column slice of every request that one step reads together in
- * one contiguous block, which the HBM streams at full burst length; a backbone
- * LM-head epilogue or a random-number fill can write it at no extra cost.
- * Row-major arrays are read in 128-byte pieces per request row instead. */
+ *   DSPARK_LAYOUT_TILED: ((k * C + v / 32) * 32 + v % 32) * R + m,  C = ceil(V / 32)
+ * The tiled order ([gamma][C][32][R], the tail entries of the last chunk
+ * padding) is column-major inside each 32-entry chunk: for one vocabulary
+ * entry the requests are contiguous, so every load of a 32-request tile reads
+ * whole 128-byte lines and a chunk of all requests is one contiguous block
+ * (the logits-transposed output of a backbone LM-head GEMM, or a random-number
+ * fill, produces it at no extra cost).  Row-major arrays are read in 128-byte
+ * pieces per request row instead. */
 typedef enum {
   DSPARK_LAYOUT_RGV = 0,
   DSPARK_LAYOUT_TILED = 1
@@ -120,7 +122,7 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *   layout    DSPARK_LAYOUT_RGV or DSPARK_LAYOUT_TILED: storage order of base,
  *             uniforms and bias_out (see dspark_layout).
  *   base      [R, gamma, V] fp32 backbone base logits (in `layout` order; the
- *             tiled order holds gamma * C * R * 32 floats).  NULL in GREEDY mode
+ *             tiled order holds gamma * C * 32 * R floats).  NULL in GREEDY mode
  *             drafts from the Markov bias alone (base taken as zero; no logits
  *             are read, so a call costs the gather + bias GEMM + argmax only).
  *   anchors   [R] int32     anchor token of each request (x_0), in [0, V).
@@ -141,7 +143,7 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  * non-finite temperature in SAMPLE mode, or uniforms given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or r % 16 != 0, and
  * where one step of one block of requests would not fit 32-bit byte offsets:
  * ceil(V/32)*32*r > 2^30, gamma*V >= 2^22 (DSPARK_LAYOUT_RGV) or
- * ceil(V/32)*R + 256 > 2^25 (DSPARK_LAYOUT_TILED); EWORKSPACE if the workspace
+ * ceil(V/32)*R >= 2^24 (DSPARK_LAYOUT_TILED); EWORKSPACE if the workspace
  * is NULL or too small, EINVAL if it is not 16-byte aligned; EDEVICE on a
  * launch failure.
  */

@@ -82,7 +82,7 @@ def _draft(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, layout=0, mode
     # 32-bit byte offsets of one step of one request block
     (dict(g=1, V=1 << 22), EUNSUPPORTED),                       # gamma*V = 2^22, RGV
     (dict(V=(1 << 21) + 32, r=512, layout=1), EUNSUPPORTED),   # ceil(V/32)*32*r > 2^30
-    (dict(R=1 << 20, V=4096, layout=1), EUNSUPPORTED),         # ceil(V/32)*R > 2^25
+    (dict(R=1 << 17, V=4096, layout=1), EUNSUPPORTED),         # ceil(V/32)*R = 2^24, tiled
     (dict(ws=None), EWORKSPACE), (dict(ws_bytes=8), EWORKSPACE), (dict(ws=P + 8), EINVAL),
 ])
 def test_markov_draft_rejects(kw, want):
@@ -207,10 +207,10 @@ def test_tiled_layout_roundtrip():
     from draft_head_step_amd.inputs import from_tiled, to_tiled
     x = np.random.default_rng(0).standard_normal((5, 3, 70)).astype(np.float32)
     t = to_tiled(x)
-    assert t.shape == (3, 3, 5, 32)
-    # element (m, k, v) at ((k * C + v // 32) * R + m) * 32 + v % 32
+    assert t.shape == (3, 3, 32, 5)
+    # element (m, k, v) at ((k * C + v // 32) * 32 + v % 32) * R + m
     flat = t.reshape(-1)
     for (m, k, v) in [(0, 0, 0), (4, 2, 69), (2, 1, 33), (3, 0, 31)]:
-        assert flat[((k * 3 + v // 32) * 5 + m) * 32 + v % 32] == x[m, k, v]
+        assert flat[((k * 3 + v // 32) * 32 + v % 32) * 5 + m] == x[m, k, v]
     assert np.array_equal(from_tiled(t, 70), x)
-    assert np.all(t[:, 2, :, 6:] == 0)
+    assert np.all(t[:, 2, 6:, :] == 0)

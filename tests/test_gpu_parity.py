@@ -400,25 +400,33 @@ def test_step_events_time_each_fused_launch():
 
 # --------------------------------------------------------------------------- bias only
 
-def _bias_only_case(wl, rows=None, bias=True):
+def _bias_only_case(wl, rows=None, bias=True, layout=D.LAYOUT_RGV):
     """base = NULL (greedy on the Markov bias alone) against the oracle with base = 0."""
+    from draft_head_step_amd.inputs import from_tiled
     g = H.to_device(wl, DEV)
     R, gm, V = wl["base"].shape
-    bias_out = torch.full((R, gm, V), float("nan"), dtype=torch.float32, device=DEV) if bias else None
+    shape = (gm, (V + 31) // 32, 32, R) if layout == D.LAYOUT_TILED else (R, gm, V)
+    bias_out = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV) if bias else None
     tok = D.dspark_markov_draft(g["W1"], g["W2"], None, g["anchors"], GREEDY, gamma=gm,
-                                bias_out=bias_out)
+                                bias_out=bias_out, layout=layout)
     torch.cuda.synchronize()
     ref = dict(wl, base=np.zeros_like(wl["base"]), mode=GREEDY, uniforms=None)
-    H.check_draft(ref, tok.cpu().numpy(), rows, None if bias_out is None else bias_out.cpu().numpy())
+    b = None
+    if bias:
+        b = bias_out.cpu().numpy()
+        if layout == D.LAYOUT_TILED:
+            b = from_tiled(b, V)
+    H.check_draft(ref, tok.cpu().numpy(), rows, b)
 
 
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
 @pytest.mark.parametrize("R,g,V,r", [(4, 5, 4096, 64), (70, 4, 3000, 256), (3, 6, 64, 512),
                                      (300, 2, 777, 64)])
-def test_bias_only_small(R, g, V, r):
-    _say(f"case bias-only R={R} g={g} V={V} r={r}")
+def test_bias_only_small(R, g, V, r, layout):
+    _say(f"case bias-only R={R} g={g} V={V} r={r} layout={layout}")
     cfg = Config("edge", R=R, gamma=g, V=V, r=r, d=16, mode=GREEDY, temperature=1.0, w_std=0.3,
                  base_std=1.0, wconf_std=0.1, seed=500 + R)
-    _bias_only_case(make_workload(cfg))
+    _bias_only_case(make_workload(cfg), layout=layout)
 
 
 @pytest.mark.parametrize("R,g,V,r", [(130, 3, 3000, 256), (600, 2, 5000, 128),

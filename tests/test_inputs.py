@@ -20,6 +20,6 @@ def test_workload_is_reproducible():
 def test_tiled_roundtrip_ragged_tail():
     x = np.random.default_rng(0).standard_normal((3, 2, 70)).astype(np.float32)
     t = to_tiled(x)
-    assert t.shape == (2, 3, 3, 32)
+    assert t.shape == (2, 3, 32, 3)
     assert np.array_equal(from_tiled(t, 70), x)
-    assert np.all(t[:, 2, :, 6:] == 0)      # columns past V are zero
+    assert np.all(t[:, 2, 6:, :] == 0)      # entries past V are zero
