@@ -416,14 +416,17 @@ __device__ __forceinline__ int n_whole(int c0, int cstep, int n_valid, int V) {
 // ---------------------------------------------------------------------------
 template <int RK, int NW>
 constexpr bool plain_deep() { return RK == 512 && NW == 4; }
-// W1 rows of all the workgroup's tiles staged through LDS (register-staged W2
-// ranks only, and only if they fit in the CU's LDS).
+// W1 rows of all the workgroup's tiles are staged through LDS, in one round if
+// they fit in the CU's LDS, else in two (the first half of the waves, then the
+// second half, through the same area).
 template <int RK, int NW, int TW>
-constexpr bool plain_lds_gather() { return RK < 512 && NW * TW * 32 * RK * 2 <= 160 * 1024; }
+constexpr int plain_gather_rounds() {
+  return (size_t)NW * TW * 32 * RK * 2 <= 160 * 1024 ? 1 : 2;
+}
 template <int RK, int NW, int TW>
 constexpr size_t plain_lds_bytes() {
   const size_t stage = (size_t)(RK == 512 ? (plain_deep<RK, NW>() ? 3 : 2) : 2) * 32 * (RK + 8) * 2;
-  const size_t gather = plain_lds_gather<RK, NW, TW>() ? (size_t)NW * TW * 32 * RK * 2 : 0;
+  const size_t gather = (size_t)NW / plain_gather_rounds<RK, NW, TW>() * TW * 32 * RK * 2;
   return stage > gather ? stage : gather;
 }
 template <int RK, int NW>
@@ -461,8 +464,11 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   constexpr bool DMA = RK == 512;                  // W2 staged by direct loads into LDS
   constexpr int NBUF = DMA ? WD + 1 : 2;           // LDS stage buffers
   static_assert(TW == 1 || !DMA, "two tiles per wave only with register staging");
-  // W1 rows staged through LDS (see plain_lds_gather) when they fit.
-  constexpr bool LDSG = plain_lds_gather<RK, NW, TW>();
+  // W1 rows staged through LDS (see plain_gather_rounds).
+  constexpr int GROUNDS = plain_gather_rounds<RK, NW, TW>();
+  constexpr int GWPR = NW / GROUNDS;                 // waves staging per round
+  static_assert(NW % GROUNDS == 0 && (size_t)GWPR * TW * 32 * RK * 2 <= 160 * 1024,
+                "W1 staging must fit the CU's LDS");
   // vmcnt at the top of an iteration that leaves only the loads issued after
   // the DMA of its own chunk outstanding (0 with bias stores in flight).
   constexpr int EL = epi_load_count<MODE, EPI, 4>();
@@ -510,12 +516,6 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
                    : (uint32_t)(m_loc * ad.row_stride + 4 * half * ad.vstride) * 4u;
     int x = step_input(io, m[t], m_ok[t], vg == 0 && half == 0, V);
     xt[t] = min(max(x, 0), V - 1);                      // out-of-range ids never fault
-    if constexpr (!LDSG) {
-      const uint16_t* er = W1 + (size_t)xt[t] * r + half * 8;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        e[t][s] = (s * 16 < r && m_ok[t]) ? ld_bf16x8(er + s * 16) : bf16x8{};
-    }
   }
 
   const Rsrc rw2 = make_rsrc(W2, (uint32_t)V * (uint32_t)r * 2u);
@@ -613,17 +613,17 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   // W1 rows through LDS: each wave copies its tiles' rows (32 x RK bf16 each)
   // with direct loads that move whole rows (1 KB per instruction: 512 / RK
   // rows); piece c of row q sits in slot c ^ (q mod pieces per row), so the
-  // one-row-per-lane reads spread over the banks.  The register staging of W2
-  // and the epilogue prefetch below are issued before the wait, which counts
-  // them from the back.
+  // one-row-per-lane reads spread over the banks.  Wave w stages in round
+  // w / GWPR into slot w % GWPR of the area.
   constexpr int PPR = RK / 8;       // 16-byte pieces per row
   constexpr int RPI = 64 / PPR;     // rows per direct load
-  if constexpr (LDSG) {
+  const int gslot = wave % GWPR;
+  auto gather_issue = [&]() {
     const u32x4 dw1 = raw_desc(W1, (uint32_t)V * (uint32_t)r * 2u);
     const int c = lane % PPR;
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
-      uint16_t* greg = lds + (wave * TW + t) * 32 * RK;
+      uint16_t* greg = lds + (gslot * TW + t) * 32 * RK;
 #pragma unroll
       for (int i = 0; i < 32 / RPI; ++i) {
         const int q = i * RPI + lane / PPR;
@@ -639,40 +639,52 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
                      : "memory");
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // Prologue loads in the order they are consumed (oldest first), so that the
-  // waits at the top of the loop can count them from the back.
-#pragma unroll
-  for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
-    if (t < WD) {
-      if constexpr (DMA) w2_dma<NW>(lds + t * BUF, dw2, w2_off, chunk(t), r, wave);
-      else w2_load<RK, NT, PMAX>(stage[t % (DMA ? 1 : WD)], rw2, w2_off, chunk(t), r);
-    }
-    if (t < PD) {
-#pragma unroll
-      for (int u = 0; u < TW; ++u)
-        epi_load<MODE, EPI, 4>(eb[t][u], eu[t][u], rbase, runif,
-                               e_off[u] + (uint32_t)chunk(t) * e_cb, e_vs);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if constexpr (LDSG) {
-    // Everything is waited for: the prologue loads were issued right behind
-    // the staging and land at about the same time (and the compiler may merge
-    // the scalar epilogue loads, so a count of them is not reliable).
+  };
+  // Waits for everything this wave issued (the compiler may merge the scalar
+  // epilogue loads, so a count of them is not reliable), then reads the rows.
+  auto gather_read = [&]() {
     wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
-      const uint16_t* greg = lds + (wave * TW + t) * 32 * RK + col * RK;
+      const uint16_t* greg = lds + (gslot * TW + t) * 32 * RK + col * RK;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         e[t][s] = *reinterpret_cast<const bf16x8*>(greg + (((2 * s + half) ^ (col & (PPR - 1))) * 8));
     }
-    lds_barrier();   // every wave has its rows before the stage buffers are written
+  };
+  // Prologue loads in the order they are consumed (oldest first), so that the
+  // waits at the top of the loop can count them from the back.
+  auto prologue = [&]() {
+#pragma unroll
+    for (int t = 0; t < (WD > PD ? WD : PD); ++t) {
+      if (t < WD) {
+        if constexpr (DMA) w2_dma<NW>(lds + t * BUF, dw2, w2_off, chunk(t), r, wave);
+        else w2_load<RK, NT, PMAX>(stage[t % (DMA ? 1 : WD)], rw2, w2_off, chunk(t), r);
+      }
+      if (t < PD) {
+#pragma unroll
+        for (int u = 0; u < TW; ++u)
+          epi_load<MODE, EPI, 4>(eb[t][u], eu[t][u], rbase, runif,
+                                 e_off[u] + (uint32_t)chunk(t) * e_cb, e_vs);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Register-staged W2: the prologue goes first and lands while the rows are
+  // staged.  Direct-to-LDS W2 writes the area the rows pass through, so it
+  // starts after the last round.  The barrier after each round frees the area
+  // for the next round or for the stage buffers.
+  if constexpr (!DMA) prologue();
+#pragma unroll
+  for (int rd = 0; rd < GROUNDS; ++rd) {
+    if (wave / GWPR == rd) {
+      gather_issue();
+      gather_read();
+    }
+    lds_barrier();
   }
+  if constexpr (DMA) prologue();
   // The first UNR iterations (the first has nothing to finish) and those from
   // n_main on use the masked select; in between every finished chunk lies
   // wholly inside V.

@@ -140,6 +140,7 @@ EDGE = [
     (40, 3, 1001, 512, 16, SAMPLE),     # rank 512 (K-split) with the scalar epilogue
     (40, 3, 1001, 512, 16, GREEDY),     # rank 512 (plain, direct-to-LDS W2), scalar epilogue
     (130, 2, 999, 256, 16, GREEDY),     # rank 256, 4-wave blocks, scalar epilogue
+    (300, 2, 3000, 512, 16, GREEDY),    # rank 512, 8 waves: W1 rows staged in two rounds
 ]
 
 
