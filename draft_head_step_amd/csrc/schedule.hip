@@ -37,10 +37,66 @@ struct SchedShared {
   int base[kDig];            // running global digit offsets
   int tot[kDig];             // digit totals
   unsigned long long wsum[kW];
-  double bval[kW];
-  int bidx[kW];
-  unsigned long long bsum[kW];
+  unsigned long long wpre[kW];   // exclusive prefix of the wave totals
+  double bval[kW + 1];       // per-wave results, then the block's (slot kW)
+  int bidx[kW + 1];
+  unsigned long long bsum[kW + 1];
   unsigned long long carry;
+  unsigned long long cin;    // carry before the current chunk
+};
+
+// ---- wavefront scans through DPP ----
+// One step of a 64-lane inclusive scan: lanes read the value `CTRL` names (row
+// shifts inside each 16-lane row, then the broadcasts of lane 15 and lane 31
+// into the following rows, restricted to rows ROWS); a lane with no source, or
+// outside ROWS, reads `ident`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_read(uint32_t v, uint32_t ident) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_read(unsigned long long v,
+                                                       unsigned long long ident) {
+  const uint32_t lo = dpp_read<CTRL, ROWS>((uint32_t)v, (uint32_t)ident);
+  const uint32_t hi = dpp_read<CTRL, ROWS>((uint32_t)(v >> 32), (uint32_t)(ident >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Inclusive scan of v over the wavefront under an associative op with
+// identity ident (Hillis-Steele inside rows, then two row broadcasts).
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_iscan(T v, T ident, Op op) {
+  v = op(v, dpp_read<0x111, 0xf>(v, ident));   // row_shr:1
+  v = op(v, dpp_read<0x112, 0xf>(v, ident));   // row_shr:2
+  v = op(v, dpp_read<0x114, 0xf>(v, ident));   // row_shr:4
+  v = op(v, dpp_read<0x118, 0xf>(v, ident));   // row_shr:8
+  v = op(v, dpp_read<0x142, 0xa>(v, ident));   // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_read<0x143, 0xc>(v, ident));   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int lane) {
+  return ((unsigned long long)lane_u32((uint32_t)(v >> 32), lane) << 32) | lane_u32((uint32_t)v, lane);
+}
+
+struct AddU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct AddU64 {
+  __device__ unsigned long long operator()(unsigned long long a, unsigned long long b) const {
+    return a + b;
+  }
+};
+struct MaxU64 {
+  __device__ unsigned long long operator()(unsigned long long a, unsigned long long b) const {
+    return a > b ? a : b;
+  }
+};
+struct MinI32 {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+    return (uint32_t)min((int)a, (int)b);
+  }
 };
 
 __device__ __forceinline__ uint32_t key_of(float a) {
@@ -62,12 +118,7 @@ __device__ void scan_digits(SchedShared& sh, const int* tot) {
       s += tot[lane * 4 + j];
     }
     // inclusive scan of s across the wave
-    int inc = s;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(inc, off);
-      if (lane >= off) inc += o;
-    }
+    const int inc = (int)wave_iscan((uint32_t)s, 0u, AddU32{});
     const int ex = inc - s;
 #pragma unroll
     for (int j = 0; j < 4; ++j) sh.base[lane * 4 + j] = ex + v[j];
@@ -134,26 +185,24 @@ __device__ __forceinline__ unsigned long long block_exscan_u64(SchedShared& sh,
                                                                unsigned long long& carry_in) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  unsigned long long inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
-  }
+  const unsigned long long inc = wave_iscan(v, 0ull, AddU64{});
   if (lane == 63) sh.wsum[w] = inc;
   __syncthreads();
-  unsigned long long before = 0;
-  unsigned long long total = 0;
-#pragma unroll
-  for (int j = 0; j < kW; ++j) {
-    const unsigned long long s = sh.wsum[j];
-    if (j < w) before += s;
-    total += s;
+  // Wave 0 scans the wave totals and moves the carry on.
+  if (w == 0) {
+    const unsigned long long t = lane < kW ? sh.wsum[lane] : 0ull;
+    const unsigned long long ti = wave_iscan(t, 0ull, AddU64{});
+    if (lane < kW) sh.wpre[lane] = ti - t;
+    const unsigned long long total = lane_u64(ti, 63);
+    if (lane == 0) {
+      const unsigned long long c = sh.carry;
+      sh.cin = c;
+      sh.carry = c + total;
+    }
   }
-  carry_in = sh.carry;
   __syncthreads();
-  if (threadIdx.x == 0) sh.carry = carry_in + total;
-  return before + inc - v;
+  carry_in = sh.cin;
+  return sh.wpre[w] + inc - v;
 }
 
 struct Best {
@@ -166,27 +215,52 @@ __device__ __forceinline__ void better(Best& b, const Best& o) {
   if (o.theta > b.theta || (o.theta == b.theta && o.m < b.m)) b = o;
 }
 
-// Block argmax of Theta (largest Theta, smallest m); every thread gets the result.
+// Order-preserving 64-bit key of a double (larger value, larger key).
+__device__ __forceinline__ unsigned long long theta_key(double x) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Argmax over the wavefront: the largest Theta, then the smallest m among the
+// lanes holding it; every lane gets the winner.
+__device__ __forceinline__ Best wave_best(const Best& b) {
+  const unsigned long long key = theta_key(b.theta);
+  const unsigned long long kmax = lane_u64(wave_iscan(key, 0ull, MaxU64{}), 63);
+  const uint32_t mine = key == kmax ? (uint32_t)b.m : 0x7fffffffu;
+  const int mmin = (int)lane_u32(wave_iscan(mine, 0x7fffffffu, MinI32{}), 63);
+  const unsigned long long sel = __ballot(key == kmax && b.m == mmin);
+  const int src = (int)__builtin_ctzll(sel);
+  Best r;
+  r.theta = __longlong_as_double((long long)lane_u64((unsigned long long)__double_as_longlong(b.theta), src));
+  r.m = mmin;
+  r.S = lane_u64(b.S, src);
+  return r;
+}
+
+// Block argmax of Theta (largest Theta, smallest m); every thread gets the
+// result.  Each wave reduces its lanes, wave 0 the per-wave winners.
 __device__ __forceinline__ void block_best(SchedShared& sh, Best& best) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    Best o;
-    o.theta = __shfl_xor(best.theta, off);
-    o.m = __shfl_xor(best.m, off);
-    o.S = __shfl_xor(best.S, off);
-    better(best, o);
-  }
+  const Best wb = wave_best(best);
   if (lane == 0) {
-    sh.bval[w] = best.theta;
-    sh.bidx[w] = best.m;
-    sh.bsum[w] = best.S;
+    sh.bval[w] = wb.theta;
+    sh.bidx[w] = wb.m;
+    sh.bsum[w] = wb.S;
   }
   __syncthreads();
-  best = Best{sh.bval[0], sh.bidx[0], sh.bsum[0]};
-#pragma unroll
-  for (int j = 1; j < kW; ++j) better(best, Best{sh.bval[j], sh.bidx[j], sh.bsum[j]});
+  if (w == 0) {
+    Best e{-1.0, 0x7fffffff, 0ull};
+    if (lane < kW) e = Best{sh.bval[lane], sh.bidx[lane], sh.bsum[lane]};
+    const Best bb = wave_best(e);
+    if (lane == 0) {
+      sh.bval[kW] = bb.theta;
+      sh.bidx[kW] = bb.m;
+      sh.bsum[kW] = bb.S;
+    }
+  }
+  __syncthreads();
+  best = Best{sh.bval[kW], sh.bidx[kW], sh.bsum[kW]};
 }
 
 // Block minimum / sum (every thread gets the result; sh's per-wave slots are
@@ -194,13 +268,16 @@ __device__ __forceinline__ void block_best(SchedShared& sh, Best& best) {
 __device__ __forceinline__ int block_min_int(SchedShared& sh, int v) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  v = (int)lane_u32(wave_iscan((uint32_t)v, 0x7fffffffu, MinI32{}), 63);
   if (lane == 0) sh.bidx[w] = v;
   __syncthreads();
-  int r = sh.bidx[0];
-#pragma unroll
-  for (int j = 1; j < kW; ++j) r = min(r, sh.bidx[j]);
+  if (w == 0) {
+    const uint32_t t = lane < kW ? (uint32_t)sh.bidx[lane] : 0x7fffffffu;
+    const int r = (int)lane_u32(wave_iscan(t, 0x7fffffffu, MinI32{}), 63);
+    if (lane == 0) sh.bidx[kW] = r;
+  }
+  __syncthreads();
+  const int r = sh.bidx[kW];
   __syncthreads();
   return r;
 }
@@ -209,13 +286,16 @@ __device__ __forceinline__ unsigned long long block_sum_sh(SchedShared& sh,
                                                            unsigned long long v) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v = lane_u64(wave_iscan(v, 0ull, AddU64{}), 63);
   if (lane == 0) sh.wsum[w] = v;
   __syncthreads();
-  unsigned long long r = 0;
-#pragma unroll
-  for (int j = 0; j < kW; ++j) r += sh.wsum[j];
+  if (w == 0) {
+    const unsigned long long t = lane < kW ? sh.wsum[lane] : 0ull;
+    const unsigned long long r = lane_u64(wave_iscan(t, 0ull, AddU64{}), 63);
+    if (lane == 0) sh.bsum[kW] = r;
+  }
+  __syncthreads();
+  const unsigned long long r = sh.bsum[kW];
   __syncthreads();
   return r;
 }
