@@ -63,7 +63,8 @@ __device__ __forceinline__ unsigned long long dpp_read(unsigned long long v,
 }
 
 // Inclusive scan of v over the wavefront under an associative op with
-// identity ident (Hillis-Steele inside rows, then two row broadcasts).
+// identity ident (Hillis-Steele inside rows, then two row broadcasts).  All 64
+// lanes must be active.
 template <typename T, typename Op>
 __device__ __forceinline__ T wave_iscan(T v, T ident, Op op) {
   v = op(v, dpp_read<0x111, 0xf>(v, ident));   // row_shr:1
@@ -215,9 +216,10 @@ __device__ __forceinline__ void better(Best& b, const Best& o) {
   if (o.theta > b.theta || (o.theta == b.theta && o.m < b.m)) b = o;
 }
 
-// Order-preserving 64-bit key of a double (larger value, larger key).
+// Order-preserving 64-bit key of a double (larger value, larger key; -0 and
+// +0 share one key, as they compare equal).
 __device__ __forceinline__ unsigned long long theta_key(double x) {
-  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x == 0.0 ? 0.0 : x);
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 

@@ -255,6 +255,19 @@ def test_schedule_ties_and_saturation():
     _sched_case(c, (0.999 ** (B / 64.0)).astype(np.float32))
 
 
+@pytest.mark.parametrize("R,g", [(40, 5), (3000, 4)])
+def test_schedule_signed_zero_sps_ties(R, g):
+    # SPS entries of -0.0 and +0.0 alternate, so every Theta is a signed zero; they
+    # compare equal, and the first argmax (m* = 0) must win on both paths.
+    _say(f"case schedule signed-zero SPS R={R} g={g}")
+    rng = np.random.default_rng(R)
+    c = rng.uniform(0.2, 1.0, size=(R, g)).astype(np.float32)
+    sps = np.zeros(R * (1 + g), np.float32)
+    sps[R - 1::2] = np.float32(-0.0)
+    assert O.schedule(O.survival(c), sps)["m_star"] == 0
+    _sched_case(c, sps)
+
+
 @pytest.mark.parametrize("K", [1, 100, 777])
 def test_schedule_capacity_step_is_top_k(K):
     _say(f"case schedule top-K K={K}")
