@@ -479,6 +479,30 @@ def main():
                 "note": "fractions use one read of the logits (the accept-prob kernel reads "
                         "each row pair twice: max/sum, then the min-sum)"}
 
+    def confidence_side(calls=50):
+        """dspark_confidence (with survival) on the default workload's tokens, timed
+        alone with HIP events around each call: us per call and the fraction of the
+        HBM peak on its algorithmic bytes (h, the gathered W1 rows, w, the outputs)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(calls)]
+        fn = lambda: D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv,
+                                         stream=stream)
+        warm(fn, 20.0)
+        for b, e in evs:
+            b.record(stream)
+            fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        us = [b.elapsed_time(e) * 1e3 for b, e in evs]
+        p50 = float(np.median(us))
+        nb = R * g * d * 2 + R * g * r * 2 + (d + r) * 4 + 2 * R * g * 4
+        return {"workload": f"{cfg.name}: R={R}, gamma={g}, d={d}, r={r}",
+                "us_per_call_p10_p50_p90": [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])],
+                "algorithmic_bytes": int(nb),
+                "achieved_GBps_at_p50": round(nb / (p50 / 1e6) / 1e9, 1),
+                "frac_of_hbm": round(nb / (p50 / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                "note": "one call per event pair: includes the launch"}
+
     def hbm_measured(nbytes=1 << 31, reps=5):
         """Large-copy bandwidth (read + write bytes over time) of torch's device copy:
         a measured reference beside the published peak."""
@@ -540,6 +564,7 @@ def main():
         out["gemm_only"] = [gemm_only(args.config), gemm_only("long_block")]
         out["scheduler"] = scheduler_only()
         out["other_configs"] = [whole_step_config("qwen3_8b"), whole_step_config("long_block")]
+        out["confidence"] = confidence_side()
         out["verify"] = verify_side()
         out["hbm_measured"] = hbm_measured()
     if not args.no_row_major and not args.no_extras and args.layout != "rgv":
