@@ -139,11 +139,12 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *             it uses in its first launch).
  *   events    optional timing hooks (NULL on the hot path).
  * Errors: EINVAL for NULL required pointers (base is optional only in GREEDY
- * mode), R/gamma/V/r <= 0, V < 2, a bad layout or mode, a non-positive or
- * non-finite temperature in SAMPLE mode, or uniforms given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or r % 16 != 0, and
- * where one step of one block of requests would not fit 32-bit byte offsets:
- * ceil(V/32)*32*r > 2^30, gamma*V >= 2^22 (DSPARK_LAYOUT_RGV) or
- * ceil(V/32)*R >= 2^24 (DSPARK_LAYOUT_TILED); EWORKSPACE if the workspace
+ * mode), W1 or W2 not 16-byte aligned, R/gamma/V/r <= 0, V < 2, a bad layout
+ * or mode, a non-positive or non-finite temperature in SAMPLE mode, or
+ * uniforms given in GREEDY mode; EUNSUPPORTED for r > DSPARK_MAX_RANK or
+ * r % 16 != 0, and where the 32-bit byte offsets of one step would overflow:
+ * ceil(V/32)*32*r > 2^30, gamma*V >= 2^22 (DSPARK_LAYOUT_RGV, per block of
+ * requests) or ceil(V/32)*R >= 2^24 (DSPARK_LAYOUT_TILED, all requests); EWORKSPACE if the workspace
  * is NULL or too small, EINVAL if it is not 16-byte aligned; EDEVICE on a
  * launch failure.
  */
