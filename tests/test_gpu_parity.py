@@ -165,6 +165,35 @@ def test_largest_row_major_vocabulary(layout):
     _full_path_check(wl, layout=layout)
 
 
+def test_tiled_layout_at_its_size_limit():
+    # ceil(V/32) * R = 2^24 - 128: one step of the column-tiled logits is just below
+    # 2^31 bytes, and the last 256-request block holds one row past R, which the
+    # kernel sends out of range.  The logits (2 GiB) are drawn on the device; the
+    # tokens are checked on sampled rows, the first and last included.
+    from draft_head_step_amd.inputs import make_head
+    R, V, g, r = (1 << 17) - 1, 4096, 1, 64
+    _say(f"case tiled size limit R={R} V={V} r={r}")
+    cfg = Config("edge", R=R, gamma=g, V=V, r=r, d=16, mode=GREEDY, temperature=1.0, w_std=0.3,
+                 base_std=1.0, wconf_std=0.1, seed=77)
+    hd = make_head(cfg)
+    gw = H.to_device({"W1": hd["W1"], "W2": hd["W2"], "anchors": hd["anchors"]}, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(77)
+    C = (V + 31) // 32
+    assert C * R < (1 << 24)
+    tiled = torch.randn((g, C, 32, R), generator=gen, device=DEV)
+    tok = D.dspark_markov_draft(gw["W1"], gw["W2"], tiled, gw["anchors"], GREEDY, 1.0, None,
+                                layout=D.LAYOUT_TILED)
+    torch.cuda.synchronize()
+    rows = _sample_rows(R, 12, 5)
+    sel = tiled.index_select(3, torch.from_numpy(rows).to(DEV))
+    base_rows = sel.permute(3, 0, 1, 2).reshape(len(rows), g, C * 32)[:, :, :V].cpu().numpy()
+    del tiled, sel
+    wl = {"W1": hd["W1"], "W2": hd["W2"], "anchors": hd["anchors"][rows], "base": base_rows,
+          "mode": GREEDY, "temperature": 1.0, "uniforms": None}
+    H.check_draft(wl, tok.cpu().numpy()[rows])
+
+
 @pytest.mark.parametrize("r,mode", [(64, GREEDY), (512, GREEDY), (512, SAMPLE)])
 def test_unaligned_base_uses_scalar_path(r, mode):
     _say(f"case unaligned base r={r} mode={mode}")
