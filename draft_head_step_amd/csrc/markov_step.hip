@@ -109,14 +109,25 @@ __device__ __forceinline__ int unpack_token(unsigned long long w, int V) {
   return i < (uint32_t)V ? (int)i : 0;
 }
 
-// Token of request m from its S packed words (S a power of two).
+// Token of request m from its S packed words (S a power of two).  The two
+// sizes the launch picks load all their words before combining them (one
+// memory round trip); other sizes (tuning overrides) take the plain loop.
 __device__ __forceinline__ int read_token(const unsigned long long* w, int m, int S, int V) {
-  unsigned long long b;
+  unsigned long long b = 0;
   if (S == 1) {
     b = w[m];
+  } else if (S == kMaxSubWords) {   // 16-byte loads, all issued first
+    const ulonglong2* p = reinterpret_cast<const ulonglong2*>(w + (size_t)m * S);
+    ulonglong2 v[kMaxSubWords / 2];
+#pragma unroll
+    for (int j = 0; j < kMaxSubWords / 2; ++j) v[j] = p[j];
+#pragma unroll
+    for (int j = 0; j < kMaxSubWords / 2; ++j) {
+      b = v[j].x > b ? v[j].x : b;
+      b = v[j].y > b ? v[j].y : b;
+    }
   } else {   // S even: 16-byte loads
     const ulonglong2* p = reinterpret_cast<const ulonglong2*>(w + (size_t)m * S);
-    b = 0;
     for (int j = 0; j < S / 2; ++j) {
       const ulonglong2 v = p[j];
       b = v.x > b ? v.x : b;
