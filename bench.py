@@ -54,6 +54,18 @@ def step_bytes(wl) -> int:
     return b
 
 
+def whole_step_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one whole step: gamma fused Markov steps, the
+    confidence head (h, the gathered W1 rows, w, conf and surv written), and the
+    schedule (survivals read, the SPS entries B = R .. R(1+gamma), lengths)."""
+    R, g, V = wl["base"].shape
+    r = wl["W1"].shape[1]
+    d = wl["h"].shape[2]
+    conf = R * g * d * 2 + R * g * r * 2 + (d + r) * 4 + 2 * R * g * 4
+    sched = R * g * 4 + (R * g + 1) * 4 + R * 4
+    return g * step_bytes(wl) + conf + sched
+
+
 def read_traffic(cfg, layout):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
     if the counters were taken on a different version of the kernel source."""
@@ -149,6 +161,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prewarm-ms", type=float, default=60.0,
+                    help="time-based warm-up before the counted warm-up steps (the GPU "
+                         "reaches its sustained clocks only after ~20 ms of work)")
     ap.add_argument("--config", default="dsv4")
     ap.add_argument("--layout", choices=["tiled", "rgv"], default="tiled",
                     help="storage order of base / uniforms handed to the draft")
@@ -278,6 +293,8 @@ def main():
     ws_d = torch.empty(D.dspark_markov_draft_workspace(R, g, V, r), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(D.dspark_schedule_workspace(R, g), dtype=torch.uint8, device=dev)
 
+    prewarm_ms = max(float(args.prewarm_ms), 0.0)
+
     def run(layout, steps, warmup, ev_steps=50):
         """Time `steps` whole steps; return (ms per step, fused-step launch durations in ms).
 
@@ -307,6 +324,7 @@ def main():
                for i in range(ev_steps)]
         torch.cuda.synchronize()
 
+        warm(one_step, prewarm_ms)
         for _ in range(warmup):
             one_step()
         torch.cuda.synchronize()
@@ -325,20 +343,30 @@ def main():
 
     def cold_steps(layout, n):
         """Per-step time with the caches flushed first (a 512 MB fill outside the
-        bracketed step): median over n steps, in ms."""
+        bracketed step): median over n steps, in ms, and the median duration of the
+        fused launch at each position (position 1 reads W2 cold; later positions
+        may find it in the 256 MB Infinity Cache)."""
         base, unif = inputs(layout)
         lay = layouts[layout]
         scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n + 1)]
+
+        def mk():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            return e
+        evs = [(mk(), mk()) for _ in range(n + 1)]
+        kb = [[mk() for _ in range(g)] for _ in range(n + 1)]
+        ke = [[mk() for _ in range(g)] for _ in range(n + 1)]
         warm(lambda: scratch.fill_(0.0))
-        times = []
+        times, per_pos = [], []
         for i in range(n + 1):
             scratch.fill_(float(i))
             b, e = evs[i]
             b.record(stream)
             D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
-                                  tokens=tokens, workspace=ws_d, stream=stream, layout=lay)
+                                  tokens=tokens, workspace=ws_d, stream=stream, layout=lay,
+                                  events=([x.cuda_event for x in kb[i]],
+                                          [x.cuda_event for x in ke[i]]))
             D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv,
                                 stream=stream)
             D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
@@ -346,8 +374,10 @@ def main():
             torch.cuda.synchronize()
             if i:
                 times.append(b.elapsed_time(e))
+                per_pos.append([kb[i][k].elapsed_time(ke[i][k]) for k in range(g)])
         del base, unif, scratch
-        return float(np.median(times))
+        pos_us = [round(float(x) * 1e3, 2) for x in np.median(np.asarray(per_pos), axis=0)]
+        return float(np.median(times)), pos_us
 
     def gemm_only(name, steps=10):
         """Greedy on the Markov bias alone (no logits stream): the gather + bias GEMM +
@@ -538,6 +568,7 @@ def main():
     # The library runs rank-512 sampling on the K-split kernel, everything else
     # on the plain one.
     kernel = "markov_step_ksplit_kernel" if (r > 256 and wl["mode"]) else "markov_step_kernel"
+    whole = whole_step_bytes(wl)
 
     out = {
         "metric": METRIC,
@@ -563,11 +594,22 @@ def main():
                      "launch_ms_p10_p50_p90": [round(float(x), 5)
                                                for x in np.percentile(durs, [10, 50, 90])],
                      "mfma_frac": round(2.0 * R * r * V / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "whole_step": {"algorithmic_bytes": whole,
+                       "achieved_GBps": round(whole / (ms_per_step / 1e3) / 1e9, 1),
+                       "frac_of_hbm": round(whole / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "note": "gamma fused steps + confidence (h, W1 rows, w) + schedule "
+                               "(survivals, SPS entries read, lengths) per step, over the "
+                               "whole step's time"},
+        "prewarm_ms": prewarm_ms,
         "cpu_baseline": None,
     }
     if not args.no_extras:
-        cold = cold_steps(args.layout, 10)
+        cold, cold_pos = cold_steps(args.layout, 10)
         out["cold"] = {"ms_per_step_median": round(cold, 4), "value": round(R * g / (cold / 1e3), 1),
+                       "whole_step_frac_of_hbm": round(whole / (cold / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "fused_launch_us_by_position": cold_pos,
+                       "frac_by_position": [round(nbytes / (u / 1e6) / 1e9 / HBM_PEAK_GBS, 4)
+                                            for u in cold_pos],
                        "note": "512 MB cache flush before each step, outside its events"}
         out["gemm_only"] = [gemm_only(args.config), gemm_only("long_block")]
         out["scheduler"] = scheduler_only()

@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -66,8 +67,17 @@ def _status_name(s: int) -> str:
         return "?"
 
 
+def _tree_hash() -> Optional[str]:
+    """Source hash of the tree this package sits in (None where the sources are not
+    shipped next to it, e.g. an installed copy)."""
+    from . import build as _build
+    if not os.path.isdir(_build.CSRC):
+        return None
+    return _build.source_hash()
+
+
 def lib() -> ctypes.CDLL:
-    """Load libdspark.so once; raise if it is not built."""
+    """Load libdspark.so once; raise if it is not built, or built from other sources."""
     global _LIB
     if _LIB is not None:
         return _LIB
@@ -76,6 +86,13 @@ def lib() -> ctypes.CDLL:
         raise ImportError(f"libdspark.so not found at {path}; build it with "
                           "`python -m draft_head_step_amd.build`")
     L = ctypes.CDLL(path)
+    L.dspark_source_hash.argtypes = []
+    L.dspark_source_hash.restype = ctypes.c_char_p
+    built = L.dspark_source_hash().decode()
+    want = _tree_hash()
+    if want is not None and built != want:
+        raise ImportError(f"{path} was built from other sources (hash {built}, tree {want}); "
+                          "rebuild it with `python -m draft_head_step_amd.build`")
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.dspark_status_string.argtypes = [i32]
     L.dspark_status_string.restype = ctypes.c_char_p
@@ -124,6 +141,15 @@ def _stream(stream) -> int:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _on(stream):
+    """Context for the binding's own allocations (default outputs, workspaces):
+    they are made on the stream the call enqueues on, so the caching allocator
+    only hands their memory to later work on that stream once it is released."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
 
 
 def _need(t, name, dtypes, shape, device):
@@ -180,14 +206,15 @@ def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: 
     _need(anchors, "anchors", (torch.int32,), (R,), dev)
     if uniforms is not None:
         _need(uniforms, "uniforms", (torch.float32,), shape, dev)
-    if tokens is None:
-        tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+    need = int(L.dspark_markov_draft_workspace(R, gamma, V, r))
+    with _on(stream):
+        if tokens is None:
+            tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
     if bias_out is not None:
         _need(bias_out, "bias_out", (torch.float32,), shape, dev)
-    need = int(L.dspark_markov_draft_workspace(R, gamma, V, r))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     ev = None
     if events is not None:
         b, e = events
@@ -216,11 +243,12 @@ def dspark_confidence(h, W1, anchors, tokens, w_conf, sts_temp=None, conf=None, 
     _need(w_conf, "w_conf", (torch.float32,), (d + r,), dev)
     if sts_temp is not None:
         _need(sts_temp, "sts_temp", (torch.float32,), (gamma,), dev)
-    if conf is None:
-        conf = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    with _on(stream):
+        if conf is None:
+            conf = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+        if surv is None and want_surv:
+            surv = torch.empty((R, gamma), dtype=torch.float32, device=dev)
     _need(conf, "conf", (torch.float32,), (R, gamma), dev)
-    if surv is None and want_surv:
-        surv = torch.empty((R, gamma), dtype=torch.float32, device=dev)
     if surv is not None:
         _need(surv, "surv", (torch.float32,), (R, gamma), dev)
     st = L.dspark_confidence(_ptr(h), _ptr(W1), _ptr(anchors), _ptr(tokens), _ptr(w_conf),
@@ -235,7 +263,8 @@ def dspark_survival(conf, surv=None, stream=None):
     R, gamma = conf.shape
     _need(conf, "conf", (torch.float32,), (R, gamma), conf.device)
     if surv is None:
-        surv = torch.empty_like(conf)
+        with _on(stream):
+            surv = torch.empty_like(conf)
     _need(surv, "surv", (torch.float32,), (R, gamma), conf.device)
     _check(lib().dspark_survival(_ptr(conf), R, gamma, _ptr(surv), _stream(stream)),
            "dspark_survival")
@@ -253,18 +282,21 @@ def dspark_schedule(surv, sps, lengths=None, order=None, want_order: bool = Fals
     _need(surv, "surv", (torch.float32,), (R, gamma), dev)
     if sps.dim() != 1 or sps.dtype != torch.float32 or sps.device != dev or not sps.is_contiguous():
         raise ValueError("sps must be a contiguous 1-D float32 tensor on the same device")
-    if lengths is None:
-        lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+    need = int(L.dspark_schedule_workspace(R, gamma))
+    with _on(stream):
+        if lengths is None:
+            lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+        if order is None and want_order:
+            order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
+        if info is None and want_info:   # every field is written by the call
+            info = torch.empty((32,), dtype=torch.uint8, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(lengths, "lengths", (torch.int32,), (R,), dev)
-    if order is None and want_order:
-        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
     if order is not None:
         _need(order, "order", (torch.int32,), (R * gamma,), dev)
-    if info is None and want_info:
-        info = torch.zeros((32,), dtype=torch.uint8, device=dev)
-    need = int(L.dspark_schedule_workspace(R, gamma))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if info is not None:
+        _need(info, "info", (torch.uint8,), (32,), dev)
     st = L.dspark_schedule(_ptr(surv), _ptr(sps), R, gamma, sps.numel(), _ptr(lengths),
                            _ptr(order), _ptr(info), _ptr(workspace), workspace.numel(),
                            _stream(stream))
@@ -287,18 +319,21 @@ def dspark_schedule_ex(surv, sps=None, mode: int = SCHED_GLOBAL, capacity: int =
     if sps is not None and (sps.dim() != 1 or sps.dtype != torch.float32 or sps.device != dev
                             or not sps.is_contiguous()):
         raise ValueError("sps must be a contiguous 1-D float32 tensor on the same device")
-    if lengths is None:
-        lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+    need = int(L.dspark_schedule_workspace(R, gamma))
+    with _on(stream):
+        if lengths is None:
+            lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+        if order is None and want_order:
+            order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
+        if info is None and want_info:   # every field is written by the call
+            info = torch.empty((32,), dtype=torch.uint8, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(lengths, "lengths", (torch.int32,), (R,), dev)
-    if order is None and want_order:
-        order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
     if order is not None:
         _need(order, "order", (torch.int32,), (R * gamma,), dev)
-    if info is None and want_info:
-        info = torch.zeros((32,), dtype=torch.uint8, device=dev)
-    need = int(L.dspark_schedule_workspace(R, gamma))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if info is not None:
+        _need(info, "info", (torch.uint8,), (32,), dev)
     st = L.dspark_schedule_ex(_ptr(surv), _ptr(sps), R, gamma,
                               0 if sps is None else sps.numel(), int(mode), int(capacity),
                               _ptr(lengths), _ptr(order), _ptr(info), _ptr(workspace),
@@ -329,18 +364,19 @@ def dspark_verify_pack(anchors, tokens, lengths, pos0=None, flat_tokens=None, fl
     if pos0 is not None:
         _need(pos0, "pos0", (torch.int32,), (R,), dev)
     n = R * (1 + gamma)
-    if flat_tokens is None:
-        flat_tokens = torch.empty((n,), dtype=torch.int32, device=dev)
+    with _on(stream):
+        if flat_tokens is None:
+            flat_tokens = torch.empty((n,), dtype=torch.int32, device=dev)
+        if flat_pos is None and want_pos:
+            flat_pos = torch.empty((n,), dtype=torch.int32, device=dev)
+        if flat_req is None and want_req:
+            flat_req = torch.empty((n,), dtype=torch.int32, device=dev)
+        if cu_seqlens is None:
+            cu_seqlens = torch.empty((R + 1,), dtype=torch.int32, device=dev)
     _need(flat_tokens, "flat_tokens", (torch.int32,), (n,), dev)
-    if flat_pos is None and want_pos:
-        flat_pos = torch.empty((n,), dtype=torch.int32, device=dev)
-    if flat_req is None and want_req:
-        flat_req = torch.empty((n,), dtype=torch.int32, device=dev)
     for t, name in ((flat_pos, "flat_pos"), (flat_req, "flat_req")):
         if t is not None:
             _need(t, name, (torch.int32,), (n,), dev)
-    if cu_seqlens is None:
-        cu_seqlens = torch.empty((R + 1,), dtype=torch.int32, device=dev)
     _need(cu_seqlens, "cu_seqlens", (torch.int32,), (R + 1,), dev)
     _check(L.dspark_verify_pack(_ptr(anchors), _ptr(tokens), _ptr(lengths), _ptr(pos0), R, gamma,
                                 _ptr(flat_tokens), _ptr(flat_pos), _ptr(flat_req),
@@ -363,12 +399,13 @@ def dspark_verify_greedy(target_logits, cu_seqlens, tokens, target_argmax=None, 
         raise ValueError("target_logits must be a contiguous [rows, V] float32 device tensor")
     V = target_logits.shape[1]
     n = R * (1 + gamma)
-    if target_argmax is None:
-        target_argmax = torch.empty((n,), dtype=torch.int32, device=dev)
-    if accepted is None:
-        accepted = torch.empty((R,), dtype=torch.int32, device=dev)
-    if next_token is None:
-        next_token = torch.empty((R,), dtype=torch.int32, device=dev)
+    with _on(stream):
+        if target_argmax is None:
+            target_argmax = torch.empty((n,), dtype=torch.int32, device=dev)
+        if accepted is None:
+            accepted = torch.empty((R,), dtype=torch.int32, device=dev)
+        if next_token is None:
+            next_token = torch.empty((R,), dtype=torch.int32, device=dev)
     _need(target_argmax, "target_argmax", (torch.int32,), (n,), dev)
     _need(accepted, "accepted", (torch.int32,), (R,), dev)
     _need(next_token, "next_token", (torch.int32,), (R,), dev)
@@ -390,7 +427,8 @@ def dspark_accept_prob(draft_logits, target_logits, temperature: float = 1.0, ou
         raise ValueError("draft_logits and target_logits must match in shape and device")
     n, V = draft_logits.shape
     if out is None:
-        out = torch.empty((n,), dtype=torch.float32, device=draft_logits.device)
+        with _on(stream):
+            out = torch.empty((n,), dtype=torch.float32, device=draft_logits.device)
     _need(out, "out", (torch.float32,), (n,), draft_logits.device)
     _check(L.dspark_accept_prob(_ptr(draft_logits), _ptr(target_logits), n, V,
                                 float(temperature), _ptr(out), _stream(stream)),

@@ -2,9 +2,16 @@
 
 Usage: python -m draft_head_step_amd.build   (or call build()).
 Objects go to <repo>/_build/, the library to draft_head_step_amd/libdspark.so.
+
+The library carries a hash of the sources and flags it was built from
+(dspark_source_hash()); the binding refuses to load a library whose hash
+differs from the tree's, so a stale build can never stand in for the
+committed source.
 """
 from __future__ import annotations
 
+import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -27,6 +34,26 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_files() -> list:
+    """Every file whose content goes into the library, in a fixed order."""
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")) +
+                   glob.glob(os.path.join(INCLUDE, "*.h")))
+    return files
+
+
+def source_hash() -> str:
+    """sha256 (first 32 hex digits) over the source files' names and contents and the
+    compile flags."""
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.relpath(f, ROOT).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(" ".join(HIPCC_FLAGS + SOURCES).encode())
+    return h.hexdigest()[:32]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -39,10 +66,12 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     procs = []
     objs = []
+    tag = f'-DDSPARK_SOURCE_HASH="{source_hash()}"'
     for s in SOURCES:
         obj = os.path.join(OUT_DIR, s.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, tag, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, s),
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((s, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

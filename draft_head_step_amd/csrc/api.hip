@@ -48,6 +48,11 @@ const char* dspark_status_string(int status) {
 
 const char* dspark_last_error(void) { return dspark::g_last_error; }
 
+#ifndef DSPARK_SOURCE_HASH
+#define DSPARK_SOURCE_HASH "unknown"
+#endif
+const char* dspark_source_hash(void) { return DSPARK_SOURCE_HASH; }
+
 size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r) {
   if (R <= 0 || gamma <= 0 || V < 2 || r <= 0) return 0;
   return dspark::plan_markov(R, gamma, V, r, DSPARK_GREEDY, false).ws_bytes;

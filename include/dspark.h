@@ -306,6 +306,11 @@ const char* dspark_status_string(int status);
 /* Thread-local description of the last failure on this thread ("" if none). */
 const char* dspark_last_error(void);
 
+/* Hash of the source files and compile flags this library was built from (32 hex
+ * digits; "unknown" for a build outside the package's build script).  Loaders
+ * compare it with the sources they ship to detect a stale library. */
+const char* dspark_source_hash(void);
+
 #ifdef __cplusplus
 }
 #endif

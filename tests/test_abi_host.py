@@ -214,3 +214,39 @@ def test_tiled_layout_roundtrip():
         assert flat[((k * 3 + v // 32) * 32 + v % 32) * 5 + m] == x[m, k, v]
     assert np.array_equal(from_tiled(t, 70), x)
     assert np.all(t[:, 2, 6:, :] == 0)
+
+
+def test_library_matches_the_tree_sources():
+    from draft_head_step_amd import build as B
+    assert D.lib().dspark_source_hash().decode() == B.source_hash()
+
+
+def test_stale_library_is_refused(monkeypatch):
+    # A library built from other sources (its embedded hash differs from the
+    # tree's) must not load.
+    monkeypatch.setattr(D, "_LIB", None)
+    monkeypatch.setattr(D, "_tree_hash", lambda: "0" * 32)
+    with pytest.raises(ImportError, match="other sources"):
+        D.lib()
+    monkeypatch.setattr(D, "_LIB", None)
+
+
+def test_source_hash_follows_every_source_file(tmp_path, monkeypatch):
+    # Changing any kernel source, internal header or the public header changes the hash.
+    from draft_head_step_amd import build as B
+    h0 = B.source_hash()
+    files = B.source_files()
+    assert any(f.endswith("dspark.h") for f in files)
+    assert any(f.endswith("markov_step.hip") for f in files)
+    real_open = open
+
+    def fake_open(path, mode="r", *a, **k):
+        fh = real_open(path, mode, *a, **k)
+        if path == files[0] and "b" in mode:
+            data = fh.read() + b"// changed"
+            fh.close()
+            import io
+            return io.BytesIO(data)
+        return fh
+    monkeypatch.setattr("builtins.open", fake_open)
+    assert B.source_hash() != h0

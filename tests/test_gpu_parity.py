@@ -144,14 +144,37 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("bias", [True, False])
 @pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
 @pytest.mark.parametrize("R,g,V,r,d,mode", EDGE)
-def test_edge_shapes(R, g, V, r, d, mode, layout):
-    _say(f"case edge R={R} g={g} V={V} r={r} d={d} mode={mode} layout={layout}")
+def test_edge_shapes(R, g, V, r, d, mode, layout, bias):
+    # With and without the bias output: the two select different kernel
+    # instances (the hot path never writes the bias).
+    _say(f"case edge R={R} g={g} V={V} r={r} d={d} mode={mode} layout={layout} bias={bias}")
     cfg = Config("edge", R=R, gamma=g, V=V, r=r, d=d, mode=mode, temperature=0.9, w_std=0.2,
                  base_std=1.0, wconf_std=0.1, seed=100 + R)
     wl = make_workload(cfg)
-    _full_path_check(wl, layout=layout)
+    _full_path_check(wl, layout=layout, bias_rows=bias)
+
+
+# Rank 512 without a bias output, in the layouts and request counts that pick
+# each kernel the hot path runs: sampling -> K-split pairs (1, 2 or 4 pairs per
+# workgroup: R <= 32, R <= 96, R > 96); greedy -> the plain kernel with 1, 2,
+# 4 (deeper rings) or 8 waves.  V = 5000 has a partial last chunk, V = 8192 none.
+RANK512 = [
+    (20, 3, 5000, SAMPLE), (60, 3, 8192, SAMPLE), (100, 3, 8192, SAMPLE), (200, 2, 5000, SAMPLE),
+    (20, 3, 8192, GREEDY), (40, 2, 5000, GREEDY), (100, 3, 5000, GREEDY),
+    (300, 2, 8192, GREEDY),
+]
+
+
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
+@pytest.mark.parametrize("R,g,V,mode", RANK512)
+def test_rank512_without_bias_output(R, g, V, mode, layout):
+    _say(f"case rank512 no-bias R={R} g={g} V={V} mode={mode} layout={layout}")
+    cfg = Config("edge", R=R, gamma=g, V=V, r=512, d=64, mode=mode, temperature=0.8, w_std=0.1,
+                 base_std=1.0, wconf_std=0.1, seed=900 + R)
+    _full_path_check(make_workload(cfg), layout=layout, bias_rows=False)
 
 
 @pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
@@ -392,6 +415,17 @@ def _sample_rows(R, n, seed):
     return np.unique(np.concatenate([[0, R - 1], rng.choice(R, size=min(n, R), replace=False)]))
 
 
+def _tile_rows(R, per_tile, seed):
+    """`per_tile` random requests from every 32-request tile (so every wave's tile
+    of every workgroup is checked), plus the first and last request."""
+    rng = np.random.default_rng(seed)
+    rows = [0, R - 1]
+    for t0 in range(0, R, 32):
+        n = min(32, R - t0)
+        rows += list(t0 + rng.choice(n, size=min(per_tile, n), replace=False))
+    return np.unique(np.asarray(rows))
+
+
 @pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
 def test_qwen3_8b_full(layout):
     _say(f"case qwen3_8b (R=64, V=151936, r=256) layout={layout}")
@@ -399,11 +433,13 @@ def test_qwen3_8b_full(layout):
     _full_path_check(wl, layout=layout)
 
 
+@pytest.mark.parametrize("bias", [False, True])
 @pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
-def test_dsv4_full(layout):
-    _say(f"case dsv4 (R=256, V=129280, r=512, sampling) layout={layout}")
+def test_dsv4_full(layout, bias):
+    # bias=False is the benchmarked call (no bias output).
+    _say(f"case dsv4 (R=256, V=129280, r=512, sampling) layout={layout} bias={bias}")
     wl = make_workload(CONFIGS["dsv4"])
-    _full_path_check(wl, rows=_sample_rows(256, 24, 1), layout=layout)
+    _full_path_check(wl, rows=_tile_rows(256, 3, 1), layout=layout, bias_rows=bias)
 
 
 def test_long_block_full():
@@ -411,7 +447,7 @@ def test_long_block_full():
     wl = make_workload(CONFIGS["long_block"])
     g = H.to_device(wl, DEV)
     toks, _ = H.run_draft(wl, g, bias=False)
-    H.check_draft(wl, toks, _sample_rows(1024, 8, 2))
+    H.check_draft(wl, toks, _tile_rows(1024, 1, 2))
     del g["base"]
     tok_dev = torch.from_numpy(toks).to(DEV)
     conf, surv = H.run_confidence(wl, g, tok_dev)

@@ -161,3 +161,102 @@ def test_bias_dominant_variant_moves_the_argmax():
     out = O.markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"])
     plain = np.argmax(wl["base"], axis=2)
     assert (out["tokens"] != plain).any()
+
+
+# --------------------------------------------------------------------------- step_scores
+
+def _planted_chain(V=32, R=5, gamma=6, seed=11, lift=5.0):
+    rng = np.random.default_rng(seed)
+    pi = rng.permutation(V)
+    W1 = np.eye(V, V, dtype=np.float32)
+    W2 = np.zeros((V, V), dtype=np.float32)
+    for t in range(V):
+        W2[pi[t], t] = lift
+    base = rng.uniform(-1, 1, size=(R, gamma, V)).astype(np.float32)
+    anchors = rng.integers(0, V, size=R).astype(np.int32)
+    return pi, _bf16(W1), _bf16(W2), base, anchors
+
+
+def test_step_scores_on_planted_chain_greedy_and_sampled():
+    # One step on its own must land on pi(x_{k-1}) for any given x_{k-1}: greedy,
+    # and sampled at T = 0.5 with a lift (+40 / T) far above the Gumbel range
+    # (-ln(-ln u) lies in [-2.8, 16.6] for the open-interval uniforms).
+    from draft_head_step_amd.inputs import open_uniforms
+    pi, W1, W2, base, anchors = _planted_chain(lift=40.0)
+    R, g, V = base.shape
+    u = open_uniforms(np.random.Generator(np.random.PCG64(4)), (R, V))
+    for prev in (anchors, (anchors + 3) % V, np.arange(R) % V):
+        x, s, mg = O.step_scores(W1, W2, base[:, 2], prev)
+        assert np.array_equal(x, pi[prev]) and np.all(mg > 30)
+        xs, ss, mgs = O.step_scores(W1, W2, base[:, 2], prev, O.SAMPLE, 0.5, u)
+        assert np.array_equal(xs, pi[prev]) and np.all(mgs > 30)
+
+
+@pytest.mark.parametrize("mode,T", [(O.GREEDY, 1.0), (O.SAMPLE, 0.7), (O.SAMPLE, 1.3)])
+def test_step_scores_replays_markov_draft(mode, T):
+    # The per-step function the GPU checks use, fed the chain's own previous
+    # tokens, reproduces markov_draft's tokens and margins at every step (so a
+    # slip in how it passes the temperature or the step's uniforms would show).
+    import dataclasses
+    from draft_head_step_amd.inputs import SAMPLE
+    cfg = CONFIGS["tiny"]
+    if mode == O.SAMPLE:
+        cfg = dataclasses.replace(cfg, mode=SAMPLE, temperature=T)
+    wl = make_workload(cfg, w_std=0.3)
+    out = O.markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"], mode, T, wl["uniforms"])
+    R, g, V = wl["base"].shape
+    prev = wl["anchors"]
+    for k in range(g):
+        u = None if wl["uniforms"] is None else wl["uniforms"][:, k]
+        x, s, mg = O.step_scores(wl["W1"], wl["W2"], wl["base"][:, k], prev, mode, T, u)
+        assert np.array_equal(x, out["tokens"][:, k])
+        assert np.array_equal(mg, out["margin"][:, k])
+        # the maximised score of the chosen token, from its parts
+        bias = O.markov_bias(wl["W1"], wl["W2"], prev)
+        z = wl["base"][np.arange(R), k, x].astype(np.float64) + bias[np.arange(R), x]
+        want = z if mode == O.GREEDY else z / T - np.log(-np.log(u[np.arange(R), x].astype(np.float64)))
+        np.testing.assert_allclose(s[np.arange(R), x], want, rtol=0, atol=1e-12)
+        prev = out["tokens"][:, k]
+
+
+def test_step_scores_temperature_scales_only_the_logits():
+    # With uniforms fixed at 1/2 the Gumbel term is the same constant for every v,
+    # so the sampled scores are z / T + const: halving T doubles every gap.
+    rng = np.random.default_rng(2)
+    V, r, R = 40, 16, 3
+    W1 = _bf16(rng.standard_normal((V, r)) * 0.3)
+    W2 = _bf16(rng.standard_normal((V, r)) * 0.3)
+    base = rng.standard_normal((R, V)).astype(np.float32)
+    prev = np.array([1, 7, 39])
+    u = np.full((R, V), 0.5, np.float32)
+    _, s1, m1 = O.step_scores(W1, W2, base, prev, O.SAMPLE, 1.0, u)
+    _, s2, m2 = O.step_scores(W1, W2, base, prev, O.SAMPLE, 0.5, u)
+    np.testing.assert_allclose(s2 - s2[:, :1], 2 * (s1 - s1[:, :1]), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(m2, 2 * m1, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- run_path
+
+@pytest.mark.parametrize("name,mode", [("tiny", O.GREEDY), ("tiny", O.SAMPLE)])
+def test_run_path_equals_the_composed_calls(name, mode):
+    import dataclasses
+    cfg = CONFIGS[name]
+    if mode == O.SAMPLE:
+        cfg = dataclasses.replace(cfg, mode=mode, temperature=0.8, sts=(1.0, 1.2, 0.9, 1.1, 1.5))
+    wl = make_workload(cfg, w_std=0.3)
+    got = O.run_path(wl)
+    dr = O.markov_draft(wl["W1"], wl["W2"], wl["base"], wl["anchors"], wl["mode"],
+                        wl["temperature"], wl["uniforms"])
+    c = O.confidence(wl["h"], wl["W1"], wl["anchors"], dr["tokens"], wl["w_conf"], wl["sts"])
+    a = O.survival(c)
+    sc = O.schedule(a, wl["sps"])
+    assert np.array_equal(got["draft"]["tokens"], dr["tokens"])
+    assert np.array_equal(got["conf"], c) and np.array_equal(got["surv"], a)
+    for key in ("lengths", "order"):
+        assert np.array_equal(got["schedule"][key], sc[key])
+    assert got["schedule"]["m_star"] == sc["m_star"] and got["schedule"]["theta"] == sc["theta"]
+    # rows: the same requests drafted on their own (the chains are independent)
+    rows = np.array([0, 2])
+    sub = O.run_path(wl, rows=rows)
+    assert np.array_equal(sub["draft"]["tokens"], dr["tokens"][rows])
+    assert np.array_equal(sub["conf"], c[rows])
