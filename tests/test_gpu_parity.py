@@ -539,3 +539,26 @@ def test_bias_only_dsv4_shape():
     _say("case bias-only at R=256, V=129280, r=512")
     cfg = dataclasses.replace(CONFIGS["dsv4"], mode=GREEDY, w_std=0.05)
     _bias_only_case(make_workload(cfg), rows=_sample_rows(256, 16, 4), bias=False)
+
+
+def test_stream_argument_that_is_not_current():
+    # Calls given a stream that is not the current one: the binding's own
+    # allocations (outputs, workspaces) are made on that stream, and the results
+    # equal those of calls on the current stream.
+    _say("case non-current stream argument")
+    wl = make_workload(CONFIGS["tiny"], w_std=0.3)
+    g = H.to_device(wl, DEV)
+    ref_t = D.dspark_markov_draft(g["W1"], g["W2"], g["base"], g["anchors"], GREEDY)
+    ref_c, ref_s = D.dspark_confidence(g["h"], g["W1"], g["anchors"], ref_t, g["w_conf"])
+    ref_l, ref_o, _ = D.dspark_schedule(ref_s, g["sps"], want_order=True)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    assert torch.cuda.current_stream() != st
+    for _ in range(3):
+        t = D.dspark_markov_draft(g["W1"], g["W2"], g["base"], g["anchors"], GREEDY, stream=st)
+        c, s = D.dspark_confidence(g["h"], g["W1"], g["anchors"], t, g["w_conf"], stream=st)
+        l, o, info = D.dspark_schedule(s, g["sps"], want_order=True, want_info=True, stream=st)
+        st.synchronize()
+        assert torch.equal(t, ref_t) and torch.equal(c, ref_c) and torch.equal(s, ref_s)
+        assert torch.equal(l, ref_l) and torch.equal(o, ref_o)
+        assert D.schedule_info(info).m_star == O.schedule(ref_s.cpu().numpy(), wl["sps"])["m_star"]
