@@ -21,7 +21,7 @@ from typing import Optional
 
 __all__ = [
     "DsparkError", "GREEDY", "SAMPLE", "LAYOUT_RGV", "LAYOUT_TILED", "lib", "lib_path",
-    "dspark_markov_draft", "dspark_confidence", "dspark_survival", "dspark_schedule",
+    "dspark_markov_draft", "dspark_markov_draft_noalloc", "dspark_confidence", "dspark_survival", "dspark_schedule",
     "dspark_schedule_ex", "dspark_verify_pack", "dspark_verify_greedy", "dspark_accept_prob",
     "dspark_markov_draft_workspace", "dspark_schedule_workspace",
     "ScheduleInfo", "SCHED_GLOBAL", "SCHED_EARLY_STOP", "SCHED_CAPACITY",
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
     L.dspark_markov_draft.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, vp,
                                       vp, vp, sz, ctypes.POINTER(StepEvents), vp]
     L.dspark_markov_draft.restype = i32
+    L.dspark_markov_draft_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                              vp, vp, vp]
+    L.dspark_markov_draft_noalloc.restype = i32
     L.dspark_confidence.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.dspark_confidence.restype = i32
     L.dspark_survival.argtypes = [vp, i32, i32, vp, vp]
@@ -225,6 +228,37 @@ def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: 
                                _ptr(tokens), _ptr(bias_out), _ptr(workspace), workspace.numel(),
                                ctypes.byref(ev) if ev is not None else None, _stream(stream))
     _check(st, "dspark_markov_draft")
+    return tokens
+
+
+def dspark_markov_draft_noalloc(W1, W2, base, anchors, tokens, mode: int = GREEDY,
+                                temperature: float = 1.0, uniforms=None, stream=None,
+                                layout: int = LAYOUT_RGV, gamma=None):
+    """dspark_markov_draft without a workspace: the library's static scratch array
+    serves instead (R * gamma <= 32768).  `tokens` [R, gamma] int32 is required, so
+    the call allocates nothing, here or in the library."""
+    torch = _torch()
+    V, r = W1.shape
+    R = anchors.shape[0]
+    dev = W1.device
+    if gamma is None:
+        if base is None:
+            raise ValueError("gamma must be given when base is None")
+        gamma = base.shape[0] if layout == LAYOUT_TILED else base.shape[1]
+    shape = (gamma, (V + 31) // 32, 32, R) if layout == LAYOUT_TILED else (R, gamma, V)
+    _need(W1, "W1", _bf16_types(), (V, r), dev)
+    _need(W2, "W2", _bf16_types(), (V, r), dev)
+    if base is not None:
+        _need(base, "base", (torch.float32,), shape, dev)
+    if uniforms is not None:
+        _need(uniforms, "uniforms", (torch.float32,), shape, dev)
+    _need(anchors, "anchors", (torch.int32,), (R,), dev)
+    _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
+    st = lib().dspark_markov_draft_noalloc(_ptr(W1), _ptr(W2), _ptr(base), _ptr(anchors), R,
+                                           gamma, V, r, int(layout), int(mode),
+                                           float(temperature), _ptr(uniforms), _ptr(tokens),
+                                           _stream(stream))
+    _check(st, "dspark_markov_draft_noalloc")
     return tokens
 
 

@@ -23,7 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
-SOURCES = ["api.hip", "markov_step.hip", "confidence.hip", "schedule.hip", "verify.hip"]
+SOURCES = ["api.hip", "markov_step.hip", "confidence.hip", "schedule.hip", "verify.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -28,43 +28,12 @@ dspark_status check_launch(const char* what) {
   return DSPARK_OK;
 }
 
-}  // namespace dspark
-
-using dspark::aligned16;
-using dspark::fail;
-
-extern "C" {
-
-const char* dspark_status_string(int status) {
-  switch (status) {
-    case DSPARK_OK: return "ok";
-    case DSPARK_EINVAL: return "invalid argument";
-    case DSPARK_EWORKSPACE: return "workspace too small";
-    case DSPARK_EUNSUPPORTED: return "unsupported size";
-    case DSPARK_EDEVICE: return "device error";
-    default: return "unknown status";
-  }
-}
-
-const char* dspark_last_error(void) { return dspark::g_last_error; }
-
-#ifndef DSPARK_SOURCE_HASH
-#define DSPARK_SOURCE_HASH "unknown"
-#endif
-const char* dspark_source_hash(void) { return DSPARK_SOURCE_HASH; }
-
-size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r) {
-  if (R <= 0 || gamma <= 0 || V < 2 || r <= 0) return 0;
-  return dspark::plan_markov(R, gamma, V, r, DSPARK_GREEDY, false).ws_bytes;
-}
-
-dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
-                                  const int32_t* anchors, int R, int gamma, int V, int r,
-                                  int layout, int mode, float temperature, const float* uniforms,
-                                  int32_t* tokens, float* bias_out, void* workspace,
-                                  size_t ws_bytes, const dspark_step_events* events,
-                                  void* stream) {
-  dspark::g_last_error[0] = 0;
+// Host-visible argument checks of the Markov-head draft (everything except the
+// workspace), shared by the entry points that launch it.
+dspark_status check_markov_args(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                const int32_t* anchors, int R, int gamma, int V, int r,
+                                int layout, int mode, float temperature, const float* uniforms,
+                                const int32_t* tokens, const dspark_step_events* events) {
   if (!W1 || !W2 || !anchors || !tokens)
     return fail(DSPARK_EINVAL, "markov_draft: NULL required pointer");
   if (!base && mode != DSPARK_GREEDY)
@@ -103,6 +72,49 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   }
   if (events && (events->count < gamma))
     return fail(DSPARK_EINVAL, "markov_draft: events->count < gamma");
+  return DSPARK_OK;
+}
+
+}  // namespace dspark
+
+using dspark::aligned16;
+using dspark::fail;
+
+extern "C" {
+
+const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_EINVAL: return "invalid argument";
+    case DSPARK_EWORKSPACE: return "workspace too small";
+    case DSPARK_EUNSUPPORTED: return "unsupported size";
+    case DSPARK_EDEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* dspark_last_error(void) { return dspark::g_last_error; }
+
+#ifndef DSPARK_SOURCE_HASH
+#define DSPARK_SOURCE_HASH "unknown"
+#endif
+const char* dspark_source_hash(void) { return DSPARK_SOURCE_HASH; }
+
+size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r) {
+  if (R <= 0 || gamma <= 0 || V < 2 || r <= 0) return 0;
+  return dspark::plan_markov(R, gamma, V, r, DSPARK_GREEDY, false).ws_bytes;
+}
+
+dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                  const int32_t* anchors, int R, int gamma, int V, int r,
+                                  int layout, int mode, float temperature, const float* uniforms,
+                                  int32_t* tokens, float* bias_out, void* workspace,
+                                  size_t ws_bytes, const dspark_step_events* events,
+                                  void* stream) {
+  dspark::g_last_error[0] = 0;
+  const dspark_status st = dspark::check_markov_args(W1, W2, base, anchors, R, gamma, V, r, layout,
+                                                     mode, temperature, uniforms, tokens, events);
+  if (st != DSPARK_OK) return st;
   const size_t need = dspark_markov_draft_workspace(R, gamma, V, r);
   if (!workspace || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "markov_draft: workspace needs %zu bytes (got %zu)", need,

@@ -29,6 +29,12 @@ struct MarkovPlan {
   size_t ws_bytes; // packed per-step results: gamma * R * 16 words of 8 bytes
 };
 
+// Host-visible argument checks of the draft (all but the workspace).
+dspark_status check_markov_args(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                const int32_t* anchors, int R, int gamma, int V, int r,
+                                int layout, int mode, float temperature, const float* uniforms,
+                                const int32_t* tokens, const dspark_step_events* events);
+
 // for_launch = false: only the static parts (buckets, workspace); no device queries.
 MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch);
 

@@ -156,6 +156,29 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
                                   void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * draft as dspark_markov_draft with no bias output, no timing hooks and no
+ * workspace argument.  Its scratch (the packed per-step results) lives in a
+ * static device array of DSPARK_NOALLOC_SCRATCH_BYTES that each GPU holds
+ * until the process ends; the call allocates nothing.
+ * Limit: dspark_markov_draft_workspace(R, gamma, V, r) <= DSPARK_NOALLOC_SCRATCH_BYTES,
+ * i.e. R * gamma <= 32768; larger sizes return DSPARK_EUNSUPPORTED.
+ * Concurrency: every call on one GPU uses that GPU's one array, so calls that
+ * overlap in time on the same device (other streams, other host threads) race
+ * and must be serialised by the caller.  Each call clears what it uses first.
+ * Errors: as dspark_markov_draft (without the workspace errors), plus
+ * EUNSUPPORTED above the limit and EDEVICE if the array's address cannot be
+ * found on the current device.
+ */
+#define DSPARK_NOALLOC_SCRATCH_BYTES (4u << 20)
+dspark_status dspark_markov_draft_noalloc(const uint16_t* W1, const uint16_t* W2,
+                                          const float* base, const int32_t* anchors, int R,
+                                          int gamma, int V, int r, int layout, int mode,
+                                          float temperature, const float* uniforms,
+                                          int32_t* tokens, void* stream);
+
+/*
  * Confidence head with STS calibration, [P1] section 二 design 2 (confidence
  * head equation, sequential temperature scaling) and [P4] (fp32 scores):
  *     s_{m,k} = sum_{i<d} w[i] h[m,k-1,i] + sum_{i<r} w[d+i] W1[x_{k-1}, i]

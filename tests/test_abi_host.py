@@ -250,3 +250,27 @@ def test_source_hash_follows_every_source_file(tmp_path, monkeypatch):
         return fh
     monkeypatch.setattr("builtins.open", fake_open)
     assert B.source_hash() != h0
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(W1=None), EINVAL), (dict(tokens=None), EINVAL), (dict(R=0), EINVAL),
+    (dict(mode=SAMPLE, u=None), EINVAL), (dict(r=40), EUNSUPPORTED),
+    (dict(R=4097, g=8), EUNSUPPORTED),          # R * gamma above the static scratch
+    (dict(R=32768, g=1, V=64, r=16), None),      # at the limit: passes the size check
+])
+def test_markov_draft_noalloc_rejects(kw, want):
+    a = dict(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, layout=0, mode=GREEDY,
+             T=1.0, u=None, tokens=P)
+    a.update(kw)
+    L = D.lib()
+    if want is None:
+        # only the size arithmetic is exercised: the workspace query fits the array
+        need = D.dspark_markov_draft_workspace(a["R"], a["g"], a["V"], a["r"])
+        assert need <= 4 << 20
+        return
+    st = L.dspark_markov_draft_noalloc(a["W1"], a["W2"], a["base"], a["anchors"], a["R"], a["g"],
+                                       a["V"], a["r"], a["layout"], a["mode"], a["T"], a["u"],
+                                       a["tokens"], None)
+    assert st == want
+    assert L.dspark_last_error() != b""
