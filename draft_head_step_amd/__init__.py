@@ -21,7 +21,8 @@ from typing import Optional
 
 __all__ = [
     "DsparkError", "GREEDY", "SAMPLE", "LAYOUT_RGV", "LAYOUT_TILED", "lib", "lib_path",
-    "dspark_markov_draft", "dspark_markov_draft_noalloc", "dspark_confidence", "dspark_survival", "dspark_schedule",
+    "dspark_markov_draft", "dspark_markov_draft_noalloc", "dspark_draft_step",
+    "dspark_draft_step_workspace", "dspark_confidence", "dspark_survival", "dspark_schedule",
     "dspark_schedule_ex", "dspark_verify_pack", "dspark_verify_greedy", "dspark_accept_prob",
     "dspark_markov_draft_workspace", "dspark_schedule_workspace",
     "ScheduleInfo", "SCHED_GLOBAL", "SCHED_EARLY_STOP", "SCHED_CAPACITY",
@@ -106,6 +107,12 @@ def lib() -> ctypes.CDLL:
     L.dspark_markov_draft_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                               vp, vp, vp]
     L.dspark_markov_draft_noalloc.restype = i32
+    L.dspark_draft_step_workspace.argtypes = [i32, i32, i32, i32]
+    L.dspark_draft_step_workspace.restype = sz
+    L.dspark_draft_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp,
+                                    vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz,
+                                    ctypes.POINTER(StepEvents), vp]
+    L.dspark_draft_step.restype = i32
     L.dspark_confidence.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.dspark_confidence.restype = i32
     L.dspark_survival.argtypes = [vp, i32, i32, vp, vp]
@@ -229,6 +236,80 @@ def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: 
                                ctypes.byref(ev) if ev is not None else None, _stream(stream))
     _check(st, "dspark_markov_draft")
     return tokens
+
+
+def dspark_draft_step_workspace(R: int, gamma: int, V: int, r: int) -> int:
+    return int(lib().dspark_draft_step_workspace(R, gamma, V, r))
+
+
+def _events(events):
+    if events is None:
+        return None
+    b, e = events
+    return StepEvents((ctypes.c_void_p * len(b))(*b), (ctypes.c_void_p * len(e))(*e),
+                      min(len(b), len(e)))
+
+
+def dspark_draft_step(W1, W2, base, anchors, h, w_conf, sps, mode: int = GREEDY,
+                      temperature: float = 1.0, uniforms=None, sts_temp=None, tokens=None,
+                      conf=None, surv=None, lengths=None, order=None, want_order: bool = False,
+                      info=None, want_info: bool = False, workspace=None, events=None,
+                      stream=None, layout: int = LAYOUT_RGV):
+    """The whole step in one call: draft, confidence + STS + survival, schedule.
+    Arguments as for dspark_markov_draft, dspark_confidence and dspark_schedule.
+    Returns (tokens, conf, surv, lengths, order or None, info or None)."""
+    torch = _torch()
+    L = lib()
+    V, r = W1.shape
+    R = anchors.shape[0]
+    dev = W1.device
+    _, gamma, d = h.shape
+    shape = (gamma, (V + 31) // 32, 32, R) if layout == LAYOUT_TILED else (R, gamma, V)
+    _need(W1, "W1", _bf16_types(), (V, r), dev)
+    _need(W2, "W2", _bf16_types(), (V, r), dev)
+    if base is not None:
+        _need(base, "base", (torch.float32,), shape, dev)
+    if uniforms is not None:
+        _need(uniforms, "uniforms", (torch.float32,), shape, dev)
+    _need(anchors, "anchors", (torch.int32,), (R,), dev)
+    _need(h, "h", _bf16_types(), (R, gamma, d), dev)
+    _need(w_conf, "w_conf", (torch.float32,), (d + r,), dev)
+    if sts_temp is not None:
+        _need(sts_temp, "sts_temp", (torch.float32,), (gamma,), dev)
+    if sps.dim() != 1 or sps.dtype != torch.float32 or sps.device != dev or not sps.is_contiguous():
+        raise ValueError("sps must be a contiguous 1-D float32 tensor on the same device")
+    need = int(L.dspark_draft_step_workspace(R, gamma, V, r))
+    with _on(stream):
+        if tokens is None:
+            tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+        if conf is None:
+            conf = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+        if surv is None:
+            surv = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+        if lengths is None:
+            lengths = torch.empty((R,), dtype=torch.int32, device=dev)
+        if order is None and want_order:
+            order = torch.empty((R * gamma,), dtype=torch.int32, device=dev)
+        if info is None and want_info:
+            info = torch.empty((32,), dtype=torch.uint8, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    for t, name, dt, shp in ((tokens, "tokens", torch.int32, (R, gamma)),
+                             (conf, "conf", torch.float32, (R, gamma)),
+                             (surv, "surv", torch.float32, (R, gamma)),
+                             (lengths, "lengths", torch.int32, (R,))):
+        _need(t, name, (dt,), shp, dev)
+    if order is not None:
+        _need(order, "order", (torch.int32,), (R * gamma,), dev)
+    ev = _events(events)
+    st = L.dspark_draft_step(_ptr(W1), _ptr(W2), _ptr(base), _ptr(anchors), R, gamma, V, r,
+                             int(layout), int(mode), float(temperature), _ptr(uniforms), _ptr(h),
+                             _ptr(w_conf), _ptr(sts_temp), d, _ptr(sps), sps.numel(),
+                             _ptr(tokens), _ptr(conf), _ptr(surv), _ptr(lengths), _ptr(order),
+                             _ptr(info), _ptr(workspace), workspace.numel(),
+                             ctypes.byref(ev) if ev is not None else None, _stream(stream))
+    _check(st, "dspark_draft_step")
+    return tokens, conf, surv, lengths, order, info
 
 
 def dspark_markov_draft_noalloc(W1, W2, base, anchors, tokens, mode: int = GREEDY,

@@ -75,6 +75,21 @@ dspark_status check_markov_args(const uint16_t* W1, const uint16_t* W2, const fl
   return DSPARK_OK;
 }
 
+// Size checks of the scheduler: B_max covers every budget (when an SPS table
+// is used), R * gamma within the candidate limit, and R * (1 + gamma) < 2^24 so
+// the fixed-point tau (at most R (1 + gamma) 2^40 with survivals in [0, 1])
+// stays below 2^64.
+dspark_status check_schedule_sizes(int R, int gamma, int B_max, bool uses_sps, const char* who) {
+  if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "%s: sizes must be positive", who);
+  if (uses_sps && (long long)B_max < (long long)R * (1LL + gamma))
+    return fail(DSPARK_EINVAL, "%s: B_max %d < R * (1 + gamma)", who, B_max);
+  if ((long long)R * gamma > DSPARK_MAX_CANDIDATES)
+    return fail(DSPARK_EUNSUPPORTED, "%s: R * gamma above %d", who, DSPARK_MAX_CANDIDATES);
+  if ((long long)R * (1LL + gamma) >= (1LL << 24))
+    return fail(DSPARK_EUNSUPPORTED, "%s: R * (1 + gamma) must be below 2^24", who);
+  return DSPARK_OK;
+}
+
 }  // namespace dspark
 
 using dspark::aligned16;
@@ -126,6 +141,44 @@ dspark_status dspark_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
                                      reinterpret_cast<hipStream_t>(stream));
 }
 
+size_t dspark_draft_step_workspace(int R, int gamma, int V, int r) {
+  if (R <= 0 || gamma <= 0 || V < 2 || r <= 0) return 0;
+  if ((long long)R * gamma > DSPARK_MAX_CANDIDATES) return 0;
+  if ((long long)R * (1LL + gamma) >= (1LL << 24)) return 0;
+  return dspark::draft_step_workspace_bytes(R, gamma, V, r);
+}
+
+dspark_status dspark_draft_step(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                const int32_t* anchors, int R, int gamma, int V, int r,
+                                int layout, int mode, float temperature, const float* uniforms,
+                                const uint16_t* h, const float* w_conf, const float* sts_temp,
+                                int d, const float* sps, int B_max, int32_t* tokens, float* conf,
+                                float* surv, int32_t* lengths, int32_t* order,
+                                dspark_schedule_info* info, void* workspace, size_t ws_bytes,
+                                const dspark_step_events* events, void* stream) {
+  dspark::g_last_error[0] = 0;
+  dspark_status st = dspark::check_markov_args(W1, W2, base, anchors, R, gamma, V, r, layout, mode,
+                                               temperature, uniforms, tokens, events);
+  if (st != DSPARK_OK) return st;
+  if (!h || !w_conf || !sps || !conf || !surv || !lengths)
+    return fail(DSPARK_EINVAL, "draft_step: NULL required pointer");
+  if (d <= 0) return fail(DSPARK_EINVAL, "draft_step: d must be positive (got %d)", d);
+  if (!aligned16(w_conf) || d % 4 != 0)
+    return fail(DSPARK_EUNSUPPORTED, "draft_step: w_conf must be 16-byte aligned and d a multiple of 4");
+  st = dspark::check_schedule_sizes(R, gamma, B_max, true, "draft_step");
+  if (st != DSPARK_OK) return st;
+  const size_t need = dspark_draft_step_workspace(R, gamma, V, r);
+  if (!workspace || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "draft_step: workspace needs %zu bytes (got %zu)", need,
+                workspace ? ws_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DSPARK_EINVAL, "draft_step: workspace must be 256-byte aligned");
+  return dspark::launch_draft_step(W1, W2, base, anchors, R, gamma, V, r, layout, mode,
+                                   temperature, uniforms, h, w_conf, sts_temp, d, sps, tokens,
+                                   conf, surv, lengths, order, info, workspace, events,
+                                   reinterpret_cast<hipStream_t>(stream));
+}
+
 dspark_status dspark_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
                                 const int32_t* tokens, const float* w_conf,
                                 const float* sts_temp, int R, int gamma, int d, int V, int r,
@@ -150,6 +203,7 @@ dspark_status dspark_survival(const float* conf, int R, int gamma, float* surv, 
 size_t dspark_schedule_workspace(int R, int gamma) {
   if (R <= 0 || gamma <= 0) return 0;
   if ((long long)R * gamma > DSPARK_MAX_CANDIDATES) return 0;
+  if ((long long)R * (1LL + gamma) >= (1LL << 24)) return 0;
   return dspark::schedule_workspace_bytes(R, gamma);
 }
 
@@ -158,11 +212,8 @@ dspark_status dspark_schedule(const float* surv, const float* sps, int R, int ga
                               void* workspace, size_t ws_bytes, void* stream) {
   dspark::g_last_error[0] = 0;
   if (!surv || !sps || !lengths) return fail(DSPARK_EINVAL, "schedule: NULL required pointer");
-  if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "schedule: sizes must be positive");
-  if ((long long)B_max < (long long)R * (1LL + gamma))
-    return fail(DSPARK_EINVAL, "schedule: B_max %d < R * (1 + gamma)", B_max);
-  if ((long long)R * gamma > DSPARK_MAX_CANDIDATES)
-    return fail(DSPARK_EUNSUPPORTED, "schedule: R * gamma above %d", DSPARK_MAX_CANDIDATES);
+  const dspark_status sz = dspark::check_schedule_sizes(R, gamma, B_max, true, "schedule");
+  if (sz != DSPARK_OK) return sz;
   const size_t need = dspark_schedule_workspace(R, gamma);
   if (!workspace || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "schedule: workspace needs %zu bytes (got %zu)", need,
@@ -183,12 +234,10 @@ dspark_status dspark_schedule_ex(const float* surv, const float* sps, int R, int
   if (!surv || !lengths || (uses_sps && !sps))
     return fail(DSPARK_EINVAL, "schedule_ex: NULL required pointer");
   if (R <= 0 || gamma <= 0) return fail(DSPARK_EINVAL, "schedule_ex: sizes must be positive");
-  if (uses_sps && (long long)B_max < (long long)R * (1LL + gamma))
-    return fail(DSPARK_EINVAL, "schedule_ex: B_max %d < R * (1 + gamma)", B_max);
   if (mode == DSPARK_SCHED_CAPACITY && capacity < 0)
     return fail(DSPARK_EINVAL, "schedule_ex: negative capacity %d", capacity);
-  if ((long long)R * gamma > DSPARK_MAX_CANDIDATES)
-    return fail(DSPARK_EUNSUPPORTED, "schedule_ex: R * gamma above %d", DSPARK_MAX_CANDIDATES);
+  const dspark_status sz = dspark::check_schedule_sizes(R, gamma, B_max, uses_sps, "schedule_ex");
+  if (sz != DSPARK_OK) return sz;
   const size_t need = dspark_schedule_workspace(R, gamma);
   if (!workspace || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "schedule_ex: workspace needs %zu bytes (got %zu)", need,

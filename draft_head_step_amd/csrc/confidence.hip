@@ -6,6 +6,9 @@
 //   c_{m,k} = 1 / (1 + exp(-s_{m,k} / T_k))
 //   a_{m,j} = c_{m,1} * ... * c_{m,j}               (fp32, left to right)
 //
+// Token ids are checked on the device: a position whose x_{k-1} lies outside
+// [0, V) gets c = NaN (and so does its survival and every later one).
+//
 // The work is a dot product of length d + r per (request, position), bound by
 // the HBM read of h.  One workgroup handles all gamma positions of one
 // request, so the survival products are a short sequential tail in the same
@@ -114,8 +117,8 @@ __global__ __launch_bounds__(1024) void confidence_kernel(
       part_range(d, P, j, vec_h, lo, hi);
       float part = dot_part(w_h, h + ((size_t)m * gamma + k) * d, lo, hi, vec_h, lane);
       if (j == P - 1) {
-        x = min(max(x, 0), V - 1);
-        part += dot_part(w_e, W1 + (size_t)x * r, 0, r, vec_e, lane);
+        if (x >= 0 && x < V) part += dot_part(w_e, W1 + (size_t)x * r, 0, r, vec_e, lane);
+        else part = NAN;
       }
       const float s = wave_sum(part);
       if (lane == 0) parts[wave] = s;
@@ -140,6 +143,24 @@ __global__ __launch_bounds__(1024) void confidence_kernel(
       }
     }
     __syncthreads();
+  }
+}
+
+// Prologue of the fused draft step: one wavefront per (request, position) dot
+// w_h . h[m, k, :] (the token-independent part of the confidence logit), and a
+// grid-stride clear of the packed words the step kernels combine into.
+__global__ __launch_bounds__(256) void conf_prologue_kernel(const uint16_t* __restrict__ h,
+                                                            const float* __restrict__ w_h,
+                                                            int n_dots, int d, int vec,
+                                                            float* __restrict__ sh,
+                                                            uint4* __restrict__ words,
+                                                            size_t nclear) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nclear; i += (size_t)gridDim.x * 256)
+    words[i] = make_uint4(0u, 0u, 0u, 0u);
+  const int lane = threadIdx.x & 63;
+  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < n_dots; t += gridDim.x * 4) {
+    const float s = wave_sum(dot_part(w_h, h + (size_t)t * d, 0, d, vec, lane));
+    if (lane == 0) sh[t] = s;
   }
 }
 
@@ -170,6 +191,22 @@ dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int
   hipLaunchKernelGGL(confidence_kernel, dim3(R), dim3(64 * P * G), 0, stream, h, W1, anchors,
                      tokens, w_conf, sts_temp, gamma, d, V, r, P, vec_h, vec_e, conf, surv);
   return check_launch("confidence_kernel");
+}
+
+dspark_status launch_conf_prologue(const uint16_t* h, const float* w_h, int R, int gamma, int d,
+                                   float* sh, unsigned long long* words, size_t n_words,
+                                   hipStream_t stream) {
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const int vec = (d % 8 == 0) && a16(h) && a16(w_h);
+  const int n_dots = R * gamma;
+  const size_t nclear = (n_words + 1) / 2;   // 16-byte stores (the area is rounded up)
+  size_t blocks = ((size_t)n_dots + 3) / 4;
+  const size_t cblocks = (nclear + 255) / 256;
+  if (cblocks > blocks) blocks = cblocks;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(conf_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, h, w_h,
+                     n_dots, d, vec, sh, reinterpret_cast<uint4*>(words), nclear);
+  return check_launch("conf_prologue_kernel");
 }
 
 dspark_status launch_survival(const float* conf, int R, int gamma, float* surv,

@@ -45,6 +45,28 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
                                   void* workspace, const dspark_step_events* events,
                                   hipStream_t stream);
 
+// ---- fused draft step: draft + confidence + survival + schedule ----
+size_t draft_step_workspace_bytes(int R, int gamma, int V, int r);
+dspark_status launch_draft_step(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                const int32_t* anchors, int R, int gamma, int V, int r,
+                                int layout, int mode, float temperature, const float* uniforms,
+                                const uint16_t* h, const float* w_conf, const float* sts_temp,
+                                int d, const float* sps, int32_t* tokens, float* conf,
+                                float* surv, int32_t* lengths, int32_t* order,
+                                dspark_schedule_info* info, void* workspace,
+                                const dspark_step_events* events, hipStream_t stream);
+// Clears n_words packed words and writes sh[m * gamma + k] = w_h . h[m, k, :].
+dspark_status launch_conf_prologue(const uint16_t* h, const float* w_h, int R, int gamma, int d,
+                                   float* sh, unsigned long long* words, size_t n_words,
+                                   hipStream_t stream);
+// Last tokens from the packed words, c = sigmoid((sh + se0 + se1) / T_k),
+// survival, then the global-search schedule.
+dspark_status launch_draft_finish(const unsigned long long* words_last, int S, int V,
+                                  const float* sh, const float* se, const float* sts_temp, int R,
+                                  int gamma, int32_t* tokens, float* conf, float* surv,
+                                  const float* sps, int32_t* lengths, int32_t* order,
+                                  dspark_schedule_info* info, void* sched_ws, hipStream_t stream);
+
 // ---- confidence head + survival ----
 dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
                                 const int32_t* tokens, const float* w_conf, const float* sts_temp,
@@ -65,6 +87,7 @@ dspark_status launch_accept_prob(const float* draft_logits, const float* target_
                                  int V, float temperature, float* out, hipStream_t stream);
 
 // ---- prefix scheduler ----
+dspark_status check_schedule_sizes(int R, int gamma, int B_max, bool uses_sps, const char* who);
 size_t schedule_workspace_bytes(int R, int gamma);
 // mode: 0 global search, 1 early stop, 2 capacity (m_cap = clamp(K - R, 0, R * gamma)).
 dspark_status launch_schedule(const float* surv, const float* sps, int R, int gamma, int mode,

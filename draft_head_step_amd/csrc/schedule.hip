@@ -18,9 +18,12 @@
 // all in LDS in a single launch.  Beyond that the sort and the scan are spread
 // over tiles of 1024 candidates on the whole device through workspace buffers
 // (a dozen short launches, no host sync).
+#include <math.h>
+
 #include <atomic>
 
 #include "dspark_internal.h"
+#include "packed_words.h"
 
 namespace dspark {
 namespace {
@@ -100,9 +103,16 @@ struct MinI32 {
   }
 };
 
+// Survivals are probabilities: a value outside [0, 1] is clamped into it and
+// NaN is taken as 0 (so the fixed-point tau sum stays below R (1 + gamma) 2^40).
+__device__ __forceinline__ float clamp_survival(float a) {
+  return a > 0.0f ? (a < 1.0f ? a : 1.0f) : 0.0f;
+}
+
 __device__ __forceinline__ uint32_t key_of(float a) {
-  // canonical non-negative bits (-0 -> +0), complemented: ascending = descending a
-  return ~(__float_as_uint(a) & 0x7fffffffu);
+  // non-negative bits of the clamped value (-0 -> +0), complemented:
+  // ascending = descending a
+  return ~__float_as_uint(clamp_survival(a));
 }
 
 __device__ __forceinline__ float value_of(uint32_t ck) { return __uint_as_float(~ck); }
@@ -425,14 +435,48 @@ __device__ void write_results(int R, int gamma, const Best& best, const int* ran
 // ---------------------------------------------------------------------------
 // Single-tile path: N <= kT * ITEMS, everything in LDS.
 // ---------------------------------------------------------------------------
-template <int ITEMS>
+// Inputs of the fused draft step's finishing launch: the last step's packed
+// words and the two parts of every confidence logit.
+struct FinishArgs {
+  const unsigned long long* words;   // last step's packed words [R][S]
+  int S;
+  int V;
+  const float* sh;                   // w_h . h, [R * gamma]
+  const float* se;                   // w_e . W1[x_{k-1}] in two K halves, [R * gamma][2]
+  const float* sts;                  // [gamma] or NULL
+  int32_t* tokens;                   // [R][gamma]: column gamma - 1 is written here
+  float* conf;                       // [R][gamma]
+  float* surv;                       // [R][gamma]
+};
+
+// Confidence, STS and survival of request m ([P1] section 二 design 2):
+// c_{m,k} = sigmoid((sh + (se_0 + se_1)) / T_k), a_{m,k} = a_{m,k-1} c_{m,k} in
+// fp32; also the last token.  The survivals go to `sv` (by candidate id) too.
+__device__ __forceinline__ void finish_request(const FinishArgs& fa, int m, int gamma,
+                                               float* __restrict__ sv) {
+  fa.tokens[(size_t)m * gamma + gamma - 1] = read_token(fa.words, m, fa.S, fa.V);
+  float a = 1.0f;
+  for (int k = 0; k < gamma; ++k) {
+    const size_t e = (size_t)m * gamma + k;
+    const float s = fa.sh[e] + (fa.se[2 * e] + fa.se[2 * e + 1]);
+    const float t = fa.sts ? fa.sts[k] : 1.0f;
+    const float c = 1.0f / (1.0f + expf(-(s / t)));
+    fa.conf[e] = c;
+    a = k == 0 ? c : a * c;
+    fa.surv[e] = a;
+    if (sv) sv[e] = a;
+  }
+}
+
+template <int ITEMS, bool FUSED>
 __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restrict__ surv,
                                                           const float* __restrict__ sps, int R,
                                                           int gamma, int N, int mode,
                                                           int m_cap,
                                                           int32_t* __restrict__ lengths,
                                                           int32_t* __restrict__ order,
-                                                          dspark_schedule_info* info) {
+                                                          dspark_schedule_info* info,
+                                                          FinishArgs fa) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   SchedShared& sh = *reinterpret_cast<SchedShared*>(smem_raw);
   uint32_t* skey = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SchedShared));
@@ -440,6 +484,15 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  // Fused draft step: the survivals are made here first (one thread per
+  // request), into the key area of LDS.
+  const float* sv = surv;
+  if constexpr (FUSED) {
+    float* svl = reinterpret_cast<float*>(skey);
+    for (int m = threadIdx.x; m < R; m += kT) finish_request(fa, m, gamma, svl);
+    __syncthreads();
+    sv = svl;
+  }
   // striped arrangement: wave w owns [w*64*ITEMS, (w+1)*64*ITEMS), item-major inside
   uint32_t ck[ITEMS];
   int id[ITEMS];
@@ -449,9 +502,10 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
   for (int i = 0; i < ITEMS; ++i) {
     const int e = w * 64 * ITEMS + i * 64 + lane;
     ok[i] = e < N;
-    ck[i] = ok[i] ? key_of(surv[e]) : 0xffffffffu;
+    ck[i] = ok[i] ? key_of(sv[e]) : 0xffffffffu;
     id[i] = e;
   }
+  if constexpr (FUSED) __syncthreads();   // the keys are read before the sort reuses the area
   // The SPS entries of this thread's sorted positions, fetched now so that the
   // latency hides behind the sort.
   float spv[ITEMS];
@@ -970,10 +1024,16 @@ __global__ __launch_bounds__(256) void sched_count_kernel(const int* __restrict_
   if (p < *mstar) atomicAdd(&lengths[si[p] / gamma], 1);
 }
 
-template <int ITEMS>
+// Fused draft step beyond the LDS path: the survivals go to memory first.
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs fa, int R, int gamma) {
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m < R) finish_request(fa, m, gamma, nullptr);
+}
+
+template <int ITEMS, bool FUSED>
 dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, int N, int mode,
                          int m_cap, int32_t* lengths, int32_t* order, dspark_schedule_info* info,
-                         hipStream_t stream) {
+                         const FinishArgs& fa, hipStream_t stream) {
   const size_t lds = sizeof(SchedShared) + (size_t)kT * ITEMS * 8;
   // The dynamic-LDS attribute, set once per device (bit d of `done`).
   static std::atomic<unsigned long long> done{0};
@@ -981,13 +1041,13 @@ dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, 
   if (hipGetDevice(&dev) != hipSuccess) return fail(DSPARK_EDEVICE, "hipGetDevice failed");
   const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
   if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_lds_kernel<ITEMS>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_lds_kernel<ITEMS, FUSED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the schedule kernel");
     done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL(schedule_lds_kernel<ITEMS>, dim3(1), dim3(kT), lds, stream, surv, sps, R,
-                     gamma, N, mode, m_cap, lengths, order, info);
+  hipLaunchKernelGGL((schedule_lds_kernel<ITEMS, FUSED>), dim3(1), dim3(kT), lds, stream, surv,
+                     sps, R, gamma, N, mode, m_cap, lengths, order, info, fa);
   return check_launch("schedule_lds_kernel");
 }
 
@@ -1019,7 +1079,7 @@ dspark_status launch_schedule(const float* surv, const float* sps, int R, int ga
                               dspark_schedule_info* info, void* workspace, hipStream_t stream) {
   const int N = R * gamma;
 #define DSPARK_LDS(I) \
-  launch_lds<I>(surv, sps, R, gamma, N, mode, m_cap, lengths, order, info, stream)
+  launch_lds<I, false>(surv, sps, R, gamma, N, mode, m_cap, lengths, order, info, FinishArgs{}, stream)
   if (N <= kT * 1) return DSPARK_LDS(1);
   if (N <= kT * 2) return DSPARK_LDS(2);
   if (N <= kT * 4) return DSPARK_LDS(4);
@@ -1081,6 +1141,23 @@ dspark_status launch_schedule(const float* surv, const float* sps, int R, int ga
   hipLaunchKernelGGL(sched_count_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, i0, gamma,
                      mstar, lengths);
   return check_launch("schedule scan");
+}
+
+dspark_status launch_draft_finish(const unsigned long long* words_last, int S, int V,
+                                  const float* sh, const float* se, const float* sts_temp, int R,
+                                  int gamma, int32_t* tokens, float* conf, float* surv,
+                                  const float* sps, int32_t* lengths, int32_t* order,
+                                  dspark_schedule_info* info, void* sched_ws, hipStream_t stream) {
+  const FinishArgs fa{words_last, S, V, sh, se, sts_temp, tokens, conf, surv};
+  const int N = R * gamma;
+  if (N <= kT * 1) return launch_lds<1, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  if (N <= kT * 2) return launch_lds<2, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  if (N <= kT * 4) return launch_lds<4, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  if (N <= kT * 8) return launch_lds<8, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  hipLaunchKernelGGL(finish_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, fa, R, gamma);
+  const dspark_status st = check_launch("finish_kernel");
+  if (st != DSPARK_OK) return st;
+  return launch_schedule(surv, sps, R, gamma, 0, 0, lengths, order, info, sched_ws, stream);
 }
 
 }  // namespace dspark

@@ -29,8 +29,11 @@
  *     outputs and workspaces may run concurrently.
  *   - Host-visible argument checks run before anything is enqueued; a failing
  *     check returns a status other than DSPARK_OK and enqueues nothing.  Token
- *     ids inside device buffers (anchors, tokens) must lie in [0, V): that is a
- *     precondition the host cannot check.
+ *     ids inside device buffers (anchors, tokens) are checked on the device:
+ *     the draft turns a request whose anchor lies outside [0, V) into tokens
+ *     of -1, and the confidence head gives NaN for a position whose previous
+ *     token lies outside [0, V), so a bad id is detectable rather than
+ *     silently clamped.
  *   - dspark_last_error() returns a thread-local description of the last
  *     failure on the calling thread.
  *
@@ -70,8 +73,9 @@ typedef enum {
  * entry the requests are contiguous, so every load of a 32-request tile reads
  * whole 128-byte lines and a chunk of all requests is one contiguous block
  * (the logits-transposed output of a backbone LM-head GEMM, or a random-number
- * fill, produces it at no extra cost).  Row-major arrays are read in 128-byte
- * pieces per request row instead. */
+ * fill, produces it at no extra cost).  Row-major arrays are read with the
+ * vocabulary entries on the lanes instead, so there a load reads 128
+ * contiguous bytes of one request row. */
 typedef enum {
   DSPARK_LAYOUT_RGV = 0,
   DSPARK_LAYOUT_TILED = 1
@@ -79,7 +83,8 @@ typedef enum {
 
 /* Limits of this build. */
 #define DSPARK_MAX_RANK 512          /* r <= 512 and r % 16 == 0 */
-#define DSPARK_MAX_CANDIDATES (1 << 23) /* R * gamma, keeps the fixed-point tau sum exact */
+#define DSPARK_MAX_CANDIDATES (1 << 23) /* R * gamma; also R * (1 + gamma) < 2^24, which keeps
+                                           the fixed-point tau sum exact (below 2^64) */
 
 /* Optional per-step timing hooks for dspark_markov_draft.  When non-NULL,
  * begin[k] and end[k] (k = 0..gamma-1) receive the start and stop time of the
@@ -125,12 +130,14 @@ size_t dspark_markov_draft_workspace(int R, int gamma, int V, int r);
  *             tiled order holds gamma * C * 32 * R floats).  NULL in GREEDY mode
  *             drafts from the Markov bias alone (base taken as zero; no logits
  *             are read, so a call costs the gather + bias GEMM + argmax only).
- *   anchors   [R] int32     anchor token of each request (x_0), in [0, V).
+ *   anchors   [R] int32     anchor token of each request (x_0); a request whose
+ *                           anchor is outside [0, V) gets tokens -1 throughout.
  *   mode      DSPARK_GREEDY or DSPARK_SAMPLE.
  *   temperature  > 0 and finite when mode == DSPARK_SAMPLE; ignored for GREEDY.
  *   uniforms  [R, gamma, V] fp32 in (0, 1) in `layout` order, required iff SAMPLE
  *             (NULL for GREEDY).
- *   tokens    [R, gamma] int32 output, tokens[m * gamma + k - 1] = x_k.
+ *   tokens    [R, gamma] int32 output, tokens[m * gamma + k - 1] = x_k (-1 after a
+ *             bad anchor, or where every score of a row is -inf or NaN).
  *   bias_out  optional [R, gamma, V] fp32 output (in `layout` order) of the
  *             Markov bias of every step (a debugging aid; NULL on the hot path).
  *   workspace device scratch of ws_bytes >= dspark_markov_draft_workspace(...),
@@ -194,7 +201,9 @@ dspark_status dspark_markov_draft_noalloc(const uint16_t* W1, const uint16_t* W2
  *   conf      [R, gamma] fp32 output c.
  *   surv      optional [R, gamma] fp32 output a (NULL to skip).
  * Errors: EINVAL for NULL required pointers or non-positive sizes; EDEVICE on a
- * launch failure.  Temperatures are device data: they must be positive.
+ * launch failure.  Temperatures are device data: they must be positive.  A
+ * position whose x_{k-1} lies outside [0, V) gets c = NaN (and so do its
+ * survival and the later ones of that request).
  */
 dspark_status dspark_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
                                 const int32_t* tokens, const float* w_conf,
@@ -222,7 +231,9 @@ size_t dspark_schedule_workspace(int R, int gamma);
  * for m = 0..R*gamma; m* is the smallest m attaining the maximum, and l_r is
  * the number of request r's candidates among the first m* ordered ones.
  *
- *   surv      [R, gamma] fp32 survival probabilities, each in [0, 1] (device data).
+ *   surv      [R, gamma] fp32 survival probabilities (device data); values outside
+ *             [0, 1] are clamped into it and NaN is taken as 0 (for the order,
+ *             q and tau alike).
  *   sps       [B_max] fp32, sps[B-1] = SPS(B) >= 0, the engine's profiled steps/s.
  *   B_max     >= R * (1 + gamma).
  *   lengths   [R] int32 output l_r.
@@ -230,8 +241,8 @@ size_t dspark_schedule_workspace(int R, int gamma);
  *   info      optional dspark_schedule_info output (device memory).
  *   workspace >= dspark_schedule_workspace(R, gamma) bytes.
  * Errors: EINVAL for NULL required pointers, non-positive sizes or
- * B_max < R*(1+gamma); EUNSUPPORTED if R*gamma > DSPARK_MAX_CANDIDATES;
- * EWORKSPACE; EDEVICE.
+ * B_max < R*(1+gamma); EUNSUPPORTED if R*gamma > DSPARK_MAX_CANDIDATES or
+ * R*(1+gamma) >= 2^24; EWORKSPACE; EDEVICE.
  */
 dspark_status dspark_schedule(const float* surv, const float* sps, int R, int gamma, int B_max,
                               int32_t* lengths, int32_t* order, dspark_schedule_info* info,
@@ -266,6 +277,44 @@ dspark_status dspark_schedule_ex(const float* surv, const float* sps, int R, int
                                  int mode, int capacity, int32_t* lengths, int32_t* order,
                                  dspark_schedule_info* info, void* workspace, size_t ws_bytes,
                                  void* stream);
+
+/* Bytes of workspace dspark_draft_step needs (0 if invalid). */
+size_t dspark_draft_step_workspace(int R, int gamma, int V, int r);
+
+/*
+ * One whole drafting step of the head in one call: the gamma-step Markov-head
+ * draft ([P1] section 二 design 1, as dspark_markov_draft), the confidence head
+ * with STS and the prefix survivals ([P1] section 二 design 2, as
+ * dspark_confidence), and the global-search schedule ([P1] section 二 design 2
+ * and section 三 challenge 2, as dspark_schedule).  The results are those of
+ * the three calls in sequence (up to the rounding order of the confidence
+ * dot products).  It runs as gamma + 2 launches: a prologue that clears the
+ * draft's packed words and computes the token-independent part w_h . h of
+ * every confidence logit, the gamma step kernels (whose first V group also
+ * computes w_e . W1[x_{k-1}] from the rows it gathered), and one launch that
+ * unpacks the last tokens, applies the sigmoid with STS, takes the survival
+ * products and schedules (up to 8192 candidates; beyond that the schedule's
+ * global path follows it).
+ *   W1 ... uniforms   as for dspark_markov_draft (no bias output).
+ *   h, w_conf, sts_temp, d   as for dspark_confidence; w_conf must be 16-byte
+ *                            aligned and d a multiple of 4.
+ *   sps, B_max               as for dspark_schedule.
+ *   tokens, conf, surv       [R, gamma] outputs; lengths [R]; order [R*gamma]
+ *                            and info optional, as for dspark_schedule.
+ *   workspace  >= dspark_draft_step_workspace(R, gamma, V, r) bytes, 256-byte
+ *              aligned; its contents on entry do not matter.
+ *   events     optional per-step timing hooks of the gamma step kernels.
+ * Errors: the union of the three calls' errors, plus EUNSUPPORTED for a
+ * misaligned w_conf or d % 4 != 0 and EINVAL for a misaligned workspace.
+ */
+dspark_status dspark_draft_step(const uint16_t* W1, const uint16_t* W2, const float* base,
+                                const int32_t* anchors, int R, int gamma, int V, int r,
+                                int layout, int mode, float temperature, const float* uniforms,
+                                const uint16_t* h, const float* w_conf, const float* sts_temp,
+                                int d, const float* sps, int B_max, int32_t* tokens, float* conf,
+                                float* surv, int32_t* lengths, int32_t* order,
+                                dspark_schedule_info* info, void* workspace, size_t ws_bytes,
+                                const dspark_step_events* events, void* stream);
 
 /*
  * Verification side, [P1] section 三 challenge 3 (every verified token is one

@@ -38,6 +38,8 @@ the design notes):
     the fp64 product double(R*2^40 + S_m) * 2^-40 * double(SPS(R+m)).
   * The argmax over the budget takes the smallest B on ties; candidates with
     equal survival are ordered by (request, position).
+  * The scheduler clamps survivals into [0, 1] (NaN taken as 0): they are
+    probabilities, and the clamp keeps the fixed-point tau below 2^64.
 """
 from __future__ import annotations
 
@@ -192,9 +194,17 @@ def survival(conf: np.ndarray) -> np.ndarray:
 # §三 挑战2 (no early stop: global search over every budget); [P3] part 01
 # ---------------------------------------------------------------------------
 
+def clamp_survival(surv: np.ndarray) -> np.ndarray:
+    """Survivals are probabilities: values outside [0, 1] are clamped into it and
+    NaN is taken as 0, before the sort and the fixed-point sums."""
+    a = np.asarray(surv, dtype=np.float32)
+    with np.errstate(invalid="ignore"):
+        return np.where(a > 0, np.minimum(a, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+
+
 def candidate_order(surv: np.ndarray) -> np.ndarray:
     """Candidate ids r*gamma + (j-1) sorted by survival descending, ties by id ascending."""
-    key = np.asarray(surv, dtype=np.float32).reshape(-1)
+    key = clamp_survival(surv).reshape(-1)
     return np.argsort(-key, kind="stable").astype(np.int32)
 
 
@@ -204,7 +214,7 @@ def schedule(surv: np.ndarray, sps: np.ndarray):
     Returns dict: lengths [R] int32, order [R*gamma] int32, m_star, B_star,
     tau_fx (uint64 fixed point), tau (fp64), theta (fp64), theta_all [N+1].
     """
-    a = np.asarray(surv, dtype=np.float32)
+    a = clamp_survival(surv)
     R, g = a.shape
     N = R * g
     sps = np.asarray(sps, dtype=np.float32)
@@ -247,7 +257,7 @@ def schedule_early_stop(surv: np.ndarray, sps: np.ndarray):
     the sorted order, look Theta up after each admission, and stop as soon as Theta
     no longer increases (Theta_m <= Theta_{m-1}: the m-th candidate is not
     admitted).  Theta_m is computed exactly as in schedule().  Sequential on purpose."""
-    a = np.asarray(surv, dtype=np.float32)
+    a = clamp_survival(surv)
     R, g = a.shape
     N = R * g
     sps = np.asarray(sps, dtype=np.float32)
@@ -277,7 +287,7 @@ def schedule_capacity(surv: np.ndarray, capacity: int):
     steps earlier, is filled with the anchors plus the top candidates by current
     survival: m* = clamp(K - R, 0, R * gamma) in the sorted order of schedule().
     There is no SPS table here; Theta is reported as tau*."""
-    a = np.asarray(surv, dtype=np.float32)
+    a = clamp_survival(surv)
     R, g = a.shape
     order = candidate_order(a)
     m = min(max(int(capacity) - R, 0), R * g)

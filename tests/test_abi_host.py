@@ -274,3 +274,58 @@ def test_markov_draft_noalloc_rejects(kw, want):
                                        a["tokens"], None)
     assert st == want
     assert L.dspark_last_error() != b""
+
+
+def test_scratch_check_recognises_counted_wait_kernels():
+    from draft_head_step_amd import build as B
+    rem = ("x.hip:1:1: remark: Function Name: _ZN6dspark12_GLOBAL__N_125markov_step_ksplit_kernelILi4ELi1ELi2ELb0EEEvPKt [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark: Function Name: _ZN6dspark12_GLOBAL__N_118markov_step_kernelILi512ELi8ELi0ELi2ELb1ELi1EEEvPKt [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 64 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark: Function Name: _ZN6dspark12_GLOBAL__N_118markov_step_kernelILi256ELi8ELi1ELi2ELb0ELi1EEEvPKt [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 32 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark: Function Name: _ZN6dspark12_GLOBAL__N_118markov_step_kernelILi512ELi4ELi0ELi2ELb0ELi1EEEvPKt [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass-analysis=kernel-resource-usage]\n")
+    bad = B.scratch_offenders(rem)
+    # the K-split and the rank-512 plain kernel without bias output count their
+    # waits; the bias-output (Lb1E) and register-staged rank-256 ones do not
+    assert len(bad) == 2 and "ksplit" in bad[0] and "ILi512ELi4E" in bad[1]
+
+
+def _step(**kw):
+    a = dict(W1=P, W2=P, base=P, anchors=P, R=4, g=5, V=4096, r=64, layout=0, mode=GREEDY,
+             T=1.0, u=None, h=P, w=P, sts=None, d=256, sps=P, B_max=24, tokens=P, conf=P,
+             surv=P, lengths=P, order=None, info=None, ws=0x100000, ws_bytes=1 << 30)
+    a.update(kw)
+    L = D.lib()
+    return L.dspark_draft_step(a["W1"], a["W2"], a["base"], a["anchors"], a["R"], a["g"], a["V"],
+                               a["r"], a["layout"], a["mode"], a["T"], a["u"], a["h"], a["w"],
+                               a["sts"], a["d"], a["sps"], a["B_max"], a["tokens"], a["conf"],
+                               a["surv"], a["lengths"], a["order"], a["info"], a["ws"],
+                               a["ws_bytes"], None, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(W1=None), EINVAL), (dict(h=None), EINVAL), (dict(w=None), EINVAL),
+    (dict(sps=None), EINVAL), (dict(conf=None), EINVAL), (dict(surv=None), EINVAL),
+    (dict(lengths=None), EINVAL), (dict(d=0), EINVAL), (dict(B_max=23), EINVAL),
+    (dict(mode=SAMPLE, u=None), EINVAL), (dict(r=40), EUNSUPPORTED),
+    (dict(d=30), EUNSUPPORTED), (dict(w=P + 4), EUNSUPPORTED),
+    (dict(R=1 << 21, g=8, B_max=9 << 21), EUNSUPPORTED),
+    (dict(ws=None), EWORKSPACE), (dict(ws_bytes=16), EWORKSPACE), (dict(ws=0x100000 + 16), EINVAL),
+])
+def test_draft_step_rejects(kw, want):
+    assert _step(**kw) == want
+    assert D.lib().dspark_last_error() != b""
+
+
+@no_gpu
+def test_schedule_rejects_tau_overflow_sizes():
+    # R * (1 + gamma) must stay below 2^24 (gamma = 1, R = 2^23 has 2^23 candidates
+    # but a fixed-point tau that could reach 2^64).
+    L = D.lib()
+    R = 1 << 23
+    assert L.dspark_schedule(P, P, R, 1, 2 * R, P, None, None, P, 1 << 30, None) == EUNSUPPORTED
+    assert D.dspark_schedule_workspace(R, 1) == 0
+    assert D.dspark_schedule_workspace(R - 1, 1) > 0

@@ -190,3 +190,37 @@ def test_theta_ties_take_the_smallest_budget():
     a = O.survival(np.array([[0.9, 0.0, 0.0], [0.8, 0.5, 0.0]], np.float32))
     got = O.schedule(a, np.ones(2 * 4, np.float32))
     assert got["m_star"] == 3 and list(got["lengths"]) == [1, 2]
+
+
+# --------------------------------------------------------------------------- input clamp
+
+def test_survivals_outside_the_unit_interval_are_clamped():
+    # Survivals are probabilities: above 1 counts as 1, below 0 and NaN as 0, for
+    # the order, q and tau alike.
+    rng = np.random.default_rng(17)
+    R, g = 30, 4
+    a = O.survival(rng.uniform(0.3, 1.0, size=(R, g)).astype(np.float32))
+    sps = (0.99 ** np.arange(R * (1 + g))).astype(np.float32)
+    raw = a.copy()
+    raw[0, 0], raw[3, 1], raw[7, 2], raw[9, 3] = 1.5, np.inf, -0.25, np.nan
+    clipped = a.copy()
+    clipped[0, 0], clipped[3, 1], clipped[7, 2], clipped[9, 3] = 1.0, 1.0, 0.0, 0.0
+    got, want = O.schedule(raw, sps), O.schedule(clipped, sps)
+    for k in ("lengths", "order"):
+        assert np.array_equal(got[k], want[k])
+    assert got["tau_fx"] == want["tau_fx"] and got["m_star"] == want["m_star"]
+    # clamped values tie with 1.0 / 0.0 and keep (request, position) order
+    order = list(O.candidate_order(raw))
+    assert order.index(0 * g + 0) < order.index(3 * g + 1)
+    assert order.index(7 * g + 2) < order.index(9 * g + 3)
+
+
+def test_fixed_point_tau_at_its_largest():
+    # With every survival 1, tau_fx after all R * gamma candidates is exactly
+    # R (1 + gamma) 2^40: the bound R (1 + gamma) < 2^24 keeps it below 2^64.
+    R, g = 7, 3
+    a = np.ones((R, g), np.float32)
+    B = np.arange(1, R * (1 + g) + 1)
+    res = O.schedule(a, np.ones(B.size, np.float32))          # constant SPS: admit all
+    assert res["m_star"] == R * g and res["tau_fx"] == R * (1 + g) * (1 << 40)
+    assert ((1 << 24) - 1) * (1 << 40) < (1 << 64)
