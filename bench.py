@@ -1,16 +1,19 @@
 """Benchmark: draft tokens/s of the DSpark drafter hot path on one MI355X.
 
-One step = one call of each entry point over one batch that is already
-resident in HBM: dspark_markov_draft (gamma fused refinement steps), then
-dspark_confidence (confidence head, STS, survival), then dspark_schedule
-(global sort + tau * SPS(B) search).  The default workload is the
-DeepSeek-V4-shaped drafter: R = 256 requests, gamma = 5, V = 129280,
-Markov rank r = 512, hidden d = 7168, Gumbel-max sampling at T = 1.
+One step = one dspark_draft_step call over one batch that is already resident
+in HBM: the gamma fused refinement steps of the Markov-head draft, the
+confidence head with STS and survival, and the global-search schedule
+(tau * SPS(B) over every budget).  The default workload is the
+DeepSeek-V4-shaped drafter: R = 256 requests, gamma = 5, V = 129280, Markov
+rank r = 512, hidden d = 7168, Gumbel-max sampling at T = 1.
 
-The base logits and uniforms are handed over in the column-tiled layout
-([gamma][ceil(V/32)][32][R], what an LM-head GEMM that writes its logits
-transposed, or a random-number fill, emits) by default; the row-major [R][gamma][V] layout is timed in the same run
-and reported beside it (``row_major``).
+The base logits and uniforms are handed over row-major ([R][gamma][V]) by
+default; the column-tiled layout ([gamma][ceil(V/32)][32][R]), the three
+separate entry points, and the same call re-using one weight copy (so that
+W2 stays in the Infinity Cache from call to call) are timed in the same run
+and reported beside it.  The headline steps take several copies of W1/W2 in
+turn, so no step finds W2 left in the Infinity Cache by the step before, as
+in a serving loop where the target model runs between two drafting calls.
 
 Prints one JSON line with the throughput, the roofline position of the
 dominant kernel (the fused Markov step, timed live with HIP events on the
@@ -19,7 +22,6 @@ stream it runs on), and the CPU oracle's throughput on the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,12 +36,12 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 METRIC = "draft tokens/s (Markov refine+confidence+schedule) at R=256,V=129280; % roofline"
 COUNTERS_FMT = os.path.join(ROOT, "profiles", "markov_step_{cfg}_{layout}_counters.txt")
-STEP_SRC = os.path.join(ROOT, "draft_head_step_amd", "csrc", "markov_step.hip")
 
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash():
+    """Hash of the library sources (the same one the built library carries)."""
+    from draft_head_step_amd import build
+    return build.source_hash()
 
 
 def step_bytes(wl) -> int:
@@ -68,7 +70,7 @@ def whole_step_bytes(wl) -> int:
 
 def read_traffic(cfg, layout):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    if the counters were taken on a different version of the kernel source."""
+    if the counters were taken on a different version of the library source."""
     path = COUNTERS_FMT.format(cfg=cfg, layout=layout)
     if not os.path.exists(path):
         return None
@@ -77,7 +79,7 @@ def read_traffic(cfg, layout):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != _sha(STEP_SRC):
+    if kv.get("library_source_hash") != source_hash():
         return None
     try:
         return int(float(kv["traffic_bytes_per_launch"]))
@@ -165,13 +167,17 @@ def main():
                     help="time-based warm-up before the counted warm-up steps (the GPU "
                          "reaches its sustained clocks only after ~20 ms of work)")
     ap.add_argument("--config", default="dsv4")
-    ap.add_argument("--layout", choices=["tiled", "rgv"], default="tiled",
+    ap.add_argument("--layout", choices=["tiled", "rgv"], default="rgv",
                     help="storage order of base / uniforms handed to the draft")
-    ap.add_argument("--no-row-major", action="store_true",
-                    help="skip the secondary timing in the row-major layout")
+    ap.add_argument("--path", choices=["fused", "calls"], default="fused",
+                    help="one dspark_draft_step call per step, or the three separate calls")
+    ap.add_argument("--weight-copies", type=int, default=-1,
+                    help="copies of W1/W2 the steps take in turn (default: enough that three "
+                         "times the 256 MB Infinity Cache separates two uses of one copy)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the side measurements (cold caches, GEMM-only, scheduler "
-                         "stress, other configurations, measured bandwidth, row-major)")
+                    help="skip the side measurements (same weights, other layout, three calls, "
+                         "cold caches, GEMM-only, scheduler stress, other configurations, "
+                         "measured bandwidth)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
@@ -295,24 +301,58 @@ def main():
 
     prewarm_ms = max(float(args.prewarm_ms), 0.0)
 
-    def run(layout, steps, warmup, ev_steps=50):
-        """Time `steps` whole steps; return (ms per step, fused-step launch durations in ms).
+    def weight_copies(W1_, W2_, n):
+        """n copies of the head's weights in separate device memory (copy 0 is the
+        original).  Steps take them in turn, so no call finds its W2 left in the
+        256 MB Infinity Cache by the call before it, as in a serving loop where
+        the target model's forward pass runs between two drafting calls."""
+        out = [(W1_, W2_)]
+        for _ in range(n - 1):
+            out.append((W1_.clone(), W2_.clone()))
+        return out
+
+    def copies_for(w2_bytes):
+        return max(4, -(-3 * (256 << 20) // w2_bytes))
+
+    n_copies = copies_for(V * r * 2) if args.weight_copies < 0 else max(args.weight_copies, 1)
+    heads = weight_copies(W1, W2, n_copies)
+    ws_f = torch.empty(D.dspark_draft_step_workspace(R, g, V, r), dtype=torch.uint8, device=dev)
+
+    def make_step(path, layout, base, unif):
+        lay = layouts[layout]
+
+        def one_step(i, ev=None):
+            hW1, hW2 = heads[i % len(heads)]
+            if path == "fused":
+                D.dspark_draft_step(hW1, hW2, base, anchors, h, w_conf, sps, wl["mode"],
+                                    wl["temperature"], unif, sts_temp=sts, tokens=tokens, conf=conf,
+                                    surv=surv, lengths=lengths, workspace=ws_f, events=ev,
+                                    stream=stream, layout=lay)
+            else:
+                D.dspark_markov_draft(hW1, hW2, base, anchors, wl["mode"], wl["temperature"],
+                                      unif, tokens=tokens, workspace=ws_d, events=ev,
+                                      stream=stream, layout=lay)
+                D.dspark_confidence(h, hW1, anchors, tokens, w_conf, sts, conf=conf, surv=surv,
+                                    stream=stream)
+                D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
+        return one_step
+
+    def run(path, layout, steps, warmup, ev_steps=50, copies=None):
+        """Time `steps` whole steps; return (ms per step, fused-step launch durations in
+        ms as [ev_steps][gamma]).
 
         Everything the timed region needs (events included) is made before the
         warm-up, and the timed steps follow the warm-up at once: the GPU runs at
         its sustained clocks (after an idle gap the first ~20 ms of steps run
-        about 10% slower).  The per-launch durations come from a second run of
+        about 10% slower; the time-based pre-warm covers that whatever the
+        counted warm-up).  The per-launch durations come from a second run of
         `ev_steps` steps with HIP events attached to each fused launch's dispatch."""
+        nonlocal heads
+        saved = heads
+        if copies is not None:
+            heads = heads[:copies]
         base, unif = inputs(layout)
-        lay = layouts[layout]
-
-        def one_step(ev=None):
-            D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
-                                  tokens=tokens, workspace=ws_d, events=ev, stream=stream,
-                                  layout=lay)
-            D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv,
-                                stream=stream)
-            D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
+        one_step = make_step(path, layout, base, unif)
 
         def mk():
             e = torch.cuda.Event(enable_timing=True)
@@ -324,31 +364,41 @@ def main():
                for i in range(ev_steps)]
         torch.cuda.synchronize()
 
-        warm(one_step, prewarm_ms)
+        cnt = [0]
+
+        def next_step():
+            one_step(cnt[0])
+            cnt[0] += 1
+        warm(next_step, prewarm_ms)
         for _ in range(warmup):
-            one_step()
+            next_step()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            one_step()
+            next_step()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         # HIP events bracketing every fused Markov step launch.
         for i in range(ev_steps):
-            one_step(evs[i])
+            one_step(cnt[0], evs[i])
+            cnt[0] += 1
         torch.cuda.synchronize()
-        durs = [begins[i][k].elapsed_time(ends[i][k]) for i in range(ev_steps) for k in range(g)]
+        durs = np.array([[begins[i][k].elapsed_time(ends[i][k]) for k in range(g)]
+                         for i in range(ev_steps)])
         del base, unif
+        heads = saved
         return (t1 - t0) * 1e3 / steps, durs
 
     def cold_steps(layout, n):
-        """Per-step time with the caches flushed first (a 512 MB fill outside the
-        bracketed step): median over n steps, in ms, and the median duration of the
+        """Per-step time of the fused call with the caches flushed first (a 512 MB
+        read, outside the bracketed step, so no dirty lines are written back
+        inside it): median over n steps, in ms, and the median duration of the
         fused launch at each position (position 1 reads W2 cold; later positions
         may find it in the 256 MB Infinity Cache)."""
         base, unif = inputs(layout)
-        lay = layouts[layout]
-        scratch = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        one_step = make_step("fused", layout, base, unif)
+        scratch = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
 
         def mk():
             e = torch.cuda.Event(enable_timing=True)
@@ -357,19 +407,13 @@ def main():
         evs = [(mk(), mk()) for _ in range(n + 1)]
         kb = [[mk() for _ in range(g)] for _ in range(n + 1)]
         ke = [[mk() for _ in range(g)] for _ in range(n + 1)]
-        warm(lambda: scratch.fill_(0.0))
+        warm(lambda: torch.sum(scratch, dim=0, out=sink))
         times, per_pos = [], []
         for i in range(n + 1):
-            scratch.fill_(float(i))
+            torch.sum(scratch, dim=0, out=sink)
             b, e = evs[i]
             b.record(stream)
-            D.dspark_markov_draft(W1, W2, base, anchors, wl["mode"], wl["temperature"], unif,
-                                  tokens=tokens, workspace=ws_d, stream=stream, layout=lay,
-                                  events=([x.cuda_event for x in kb[i]],
-                                          [x.cuda_event for x in ke[i]]))
-            D.dspark_confidence(h, W1, anchors, tokens, w_conf, sts, conf=conf, surv=surv,
-                                stream=stream)
-            D.dspark_schedule(surv, sps, lengths=lengths, workspace=ws_s, stream=stream)
+            one_step(0, ([x.cuda_event for x in kb[i]], [x.cuda_event for x in ke[i]]))
             e.record(stream)
             torch.cuda.synchronize()
             if i:
@@ -411,31 +455,34 @@ def main():
                 "tflops": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
 
     def whole_step_config(name, steps=20):
-        """Another configuration's whole step (draft + confidence + schedule) with
-        inputs drawn on the device, tiled logits; per-step ms and fused-launch us."""
+        """Another configuration's whole step (the fused call) with inputs drawn on
+        the device, in the headline layout, weight copies taken in turn; per-step
+        ms and fused-launch us."""
         c = CONFIGS[name]
         w = device_workload(c, dev)
         cR, cg, cV, cr = w["R"], w["gamma"], w["V"], w["r"]
-        cb = tiled_on_device(w["base"])
-        del w["base"]
-        cu = tiled_on_device(w["uniforms"]) if w["uniforms"] is not None else None
-        w["uniforms"] = None
+        cb = tiled_on_device(w["base"]) if args.layout == "tiled" else w["base"]
+        cu = w["uniforms"]
+        if cu is not None and args.layout == "tiled":
+            cu = tiled_on_device(cu)
+        w["base"] = w["uniforms"] = None
+        lay = layouts[args.layout]
+        ch = weight_copies(w["W1"], w["W2"], copies_for(cV * cr * 2))
         ctok = torch.empty((cR, cg), dtype=torch.int32, device=dev)
         cconf = torch.empty((cR, cg), dtype=torch.float32, device=dev)
         csurv = torch.empty((cR, cg), dtype=torch.float32, device=dev)
         clen = torch.empty((cR,), dtype=torch.int32, device=dev)
-        cwd = torch.empty(D.dspark_markov_draft_workspace(cR, cg, cV, cr), dtype=torch.uint8,
+        cws = torch.empty(D.dspark_draft_step_workspace(cR, cg, cV, cr), dtype=torch.uint8,
                           device=dev)
-        cws = torch.empty(max(D.dspark_schedule_workspace(cR, cg), 1), dtype=torch.uint8,
-                          device=dev)
+        cnt = [0]
 
         def one(ev=None):
-            D.dspark_markov_draft(w["W1"], w["W2"], cb, w["anchors"], c.mode, c.temperature, cu,
-                                  tokens=ctok, workspace=cwd, events=ev, stream=stream,
-                                  layout=D.LAYOUT_TILED)
-            D.dspark_confidence(w["h"], w["W1"], w["anchors"], ctok, w["w_conf"], w["sts"],
-                                conf=cconf, surv=csurv, stream=stream)
-            D.dspark_schedule(csurv, w["sps"], lengths=clen, workspace=cws, stream=stream)
+            hW1, hW2 = ch[cnt[0] % len(ch)]
+            cnt[0] += 1
+            D.dspark_draft_step(hW1, hW2, cb, w["anchors"], w["h"], w["w_conf"], w["sps"], c.mode,
+                                c.temperature, cu, sts_temp=w["sts"], tokens=ctok, conf=cconf,
+                                surv=csurv, lengths=clen, workspace=cws, events=ev, stream=stream,
+                                layout=lay)
 
         evb = [[torch.cuda.Event(enable_timing=True) for _ in range(cg)] for _ in range(steps)]
         eve = [[torch.cuda.Event(enable_timing=True) for _ in range(cg)] for _ in range(steps)]
@@ -454,13 +501,15 @@ def main():
         kd = [evb[i][k].elapsed_time(eve[i][k]) for i in range(steps) for k in range(cg)]
         kms = float(np.mean(kd))
         nb = cV * cr * 2 + cR * cV * 4 * (2 if cu is not None else 1) + cR * cr * 2 + cR * 4
-        del w, cb, cu, cwd, cws
+        nch = len(ch)
+        del w, cb, cu, cws, ch
         return {"workload": f"{name}: R={cR}, gamma={cg}, V={cV}, r={cr}, d={c.d}, "
-                            f"{'sampling' if c.mode else 'greedy'}",
+                            f"{'sampling' if c.mode else 'greedy'}, layout {args.layout}",
                 "ms_per_step": round(ms, 4), "value": round(cR * cg / (ms / 1e3), 1),
                 "unit": "draft tokens/s", "avg_launch_ms": round(kms, 5),
                 "launch_ms_p10_p50_p90": [round(float(x), 5) for x in np.percentile(kd, [10, 50, 90])],
                 "frac": round(nb / (kms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "weight_copies": nch,
                 "data": "synthetic, drawn on the device (seeded torch generator)"}
 
     def verify_side(vR=256, vg=5, vV=129280, calls=20):
@@ -560,8 +609,9 @@ def main():
         return {"copy_GBps": round(2 * nbytes / (float(np.median(ts)) / 1e3) / 1e9, 1),
                 "bytes_copied": nbytes}
 
-    ms_per_step, durs = run(args.layout, args.steps, args.warmup)
+    ms_per_step, durs = run(args.path, args.layout, args.steps, args.warmup)
     k_ms = float(np.mean(durs))
+    pos_ms = durs.mean(axis=0)
     value = R * g / (ms_per_step / 1e3)
     nbytes = step_bytes(wl)
     achieved = nbytes / (k_ms / 1e3) / 1e9
@@ -569,6 +619,14 @@ def main():
     # on the plain one.
     kernel = "markov_step_ksplit_kernel" if (r > 256 and wl["mode"]) else "markov_step_kernel"
     whole = whole_step_bytes(wl)
+    launches = g + 2 if args.path == "fused" else g + 4
+
+    def summary(ms, dd):
+        km = float(np.mean(dd))
+        return {"ms_per_step": round(ms, 4), "value": round(R * g / (ms / 1e3), 1),
+                "avg_launch_ms": round(km, 5),
+                "frac": round(nbytes / (km / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "whole_step_frac_of_hbm": round(whole / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     out = {
         "metric": METRIC,
@@ -585,7 +643,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: R={R}, gamma={g}, V={V}, r={r}, d={d}, "
                                f"{'Gumbel-max sampling T=%g' % wl['temperature'] if wl['mode'] else 'greedy'}",
-                   "R": R, "gamma": g, "V": V, "r": r, "d": d, "layout": args.layout},
+                   "R": R, "gamma": g, "V": V, "r": r, "d": d, "layout": args.layout,
+                   "call": "dspark_draft_step" if args.path == "fused"
+                           else "dspark_markov_draft + dspark_confidence + dspark_schedule",
+                   "launches_per_step": launches, "weight_copies": n_copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(cfg.name, args.layout),
@@ -593,6 +654,7 @@ def main():
                      "avg_launch_ms": round(k_ms, 5), "launches_per_step": g,
                      "launch_ms_p10_p50_p90": [round(float(x), 5)
                                                for x in np.percentile(durs, [10, 50, 90])],
+                     "avg_launch_ms_by_position": [round(float(x), 5) for x in pos_ms],
                      "mfma_frac": round(2.0 * R * r * V / (k_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "whole_step": {"algorithmic_bytes": whole,
                        "achieved_GBps": round(whole / (ms_per_step / 1e3) / 1e9, 1),
@@ -604,26 +666,34 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_extras:
+        # The same call with one weight copy (W2 stays in the Infinity Cache from
+        # call to call), the other layout, and the three separate entry points.
+        ms_h, d_h = run(args.path, args.layout, max(args.steps // 2, 1), max(args.warmup, 1),
+                        ev_steps=20, copies=1)
+        out["same_weights_every_step"] = dict(summary(ms_h, d_h), weight_copies=1,
+                                              note="W2 found in the Infinity Cache by later calls")
+        other = "tiled" if args.layout == "rgv" else "rgv"
+        ms_o, d_o = run(args.path, other, max(args.steps // 2, 1), max(args.warmup, 1), ev_steps=20)
+        out["other_layout"] = dict(summary(ms_o, d_o), layout=other)
+        if args.path == "fused":
+            ms_c, d_c = run("calls", args.layout, max(args.steps // 2, 1), max(args.warmup, 1),
+                            ev_steps=20)
+            out["three_calls"] = dict(summary(ms_c, d_c), launches_per_step=g + 4,
+                                      call="dspark_markov_draft + dspark_confidence + dspark_schedule")
         cold, cold_pos = cold_steps(args.layout, 10)
         out["cold"] = {"ms_per_step_median": round(cold, 4), "value": round(R * g / (cold / 1e3), 1),
                        "whole_step_frac_of_hbm": round(whole / (cold / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                        "fused_launch_us_by_position": cold_pos,
                        "frac_by_position": [round(nbytes / (u / 1e6) / 1e9 / HBM_PEAK_GBS, 4)
                                             for u in cold_pos],
-                       "note": "512 MB cache flush before each step, outside its events"}
+                       "note": "a 512 MB read before each step (outside its events) evicts the "
+                               "caches without leaving dirty lines to write back"}
         out["gemm_only"] = [gemm_only(args.config), gemm_only("long_block")]
         out["scheduler"] = scheduler_only()
         out["other_configs"] = [whole_step_config("qwen3_8b"), whole_step_config("long_block")]
         out["confidence"] = confidence_side()
         out["verify"] = verify_side()
         out["hbm_measured"] = hbm_measured()
-    if not args.no_row_major and not args.no_extras and args.layout != "rgv":
-        ms2, d2 = run("rgv", max(args.steps // 2, 1), max(args.warmup, 1), ev_steps=20)
-        k2 = float(np.mean(d2))
-        out["row_major"] = {"layout": "rgv", "ms_per_step": round(ms2, 4),
-                            "value": round(R * g / (ms2 / 1e3), 1),
-                            "avg_launch_ms": round(k2, 5),
-                            "frac": round(nbytes / (k2 / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

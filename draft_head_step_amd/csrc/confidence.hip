@@ -146,21 +146,36 @@ __global__ __launch_bounds__(1024) void confidence_kernel(
   }
 }
 
-// Prologue of the fused draft step: one wavefront per (request, position) dot
-// w_h . h[m, k, :] (the token-independent part of the confidence logit), and a
-// grid-stride clear of the packed words the step kernels combine into.
-__global__ __launch_bounds__(256) void conf_prologue_kernel(const uint16_t* __restrict__ h,
-                                                            const float* __restrict__ w_h,
-                                                            int n_dots, int d, int vec,
-                                                            float* __restrict__ sh,
-                                                            uint4* __restrict__ words,
-                                                            size_t nclear) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < nclear; i += (size_t)gridDim.x * 256)
+// Prologue of the fused draft step: the token-independent part of every
+// confidence logit, w_h . h[m, k, :], one workgroup of four wavefronts per
+// (request, position) (each wavefront a quarter of the row, so every lane has
+// only a few 16-byte pieces in flight; the quarters are added in a fixed
+// order), and a grid-stride clear of the packed words the step kernels
+// combine into.
+constexpr int kProWaves = 4;
+
+__global__ __launch_bounds__(64 * kProWaves) void conf_prologue_kernel(
+    const uint16_t* __restrict__ h, const float* __restrict__ w_h, int n_dots, int d, int vec,
+    float* __restrict__ sh, uint4* __restrict__ words, size_t nclear) {
+  __shared__ float part[kProWaves];
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nclear;
+       i += (size_t)gridDim.x * blockDim.x)
     words[i] = make_uint4(0u, 0u, 0u, 0u);
   const int lane = threadIdx.x & 63;
-  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < n_dots; t += gridDim.x * 4) {
-    const float s = wave_sum(dot_part(w_h, h + (size_t)t * d, 0, d, vec, lane));
-    if (lane == 0) sh[t] = s;
+  const int wave = threadIdx.x >> 6;
+  for (int t = blockIdx.x; t < n_dots; t += gridDim.x) {
+    int lo, hi;
+    part_range(d, kProWaves, wave, vec, lo, hi);
+    const float s = wave_sum(dot_part(w_h, h + (size_t)t * d, lo, hi, vec, lane));
+    if (lane == 0) part[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kProWaves; ++j) a += part[j];
+      sh[t] = a;
+    }
+    __syncthreads();
   }
 }
 
@@ -200,12 +215,12 @@ dspark_status launch_conf_prologue(const uint16_t* h, const float* w_h, int R, i
   const int vec = (d % 8 == 0) && a16(h) && a16(w_h);
   const int n_dots = R * gamma;
   const size_t nclear = (n_words + 1) / 2;   // 16-byte stores (the area is rounded up)
-  size_t blocks = ((size_t)n_dots + 3) / 4;
-  const size_t cblocks = (nclear + 255) / 256;
+  size_t blocks = (size_t)n_dots;
+  const size_t cblocks = (nclear + 64 * kProWaves - 1) / (64 * kProWaves);
   if (cblocks > blocks) blocks = cblocks;
-  if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(conf_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, h, w_h,
-                     n_dots, d, vec, sh, reinterpret_cast<uint4*>(words), nclear);
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(conf_prologue_kernel, dim3((unsigned)blocks), dim3(64 * kProWaves), 0,
+                     stream, h, w_h, n_dots, d, vec, sh, reinterpret_cast<uint4*>(words), nclear);
   return check_launch("conf_prologue_kernel");
 }
 

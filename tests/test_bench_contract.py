@@ -23,14 +23,11 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_needs_the_counted_source(tmp_path, monkeypatch):
     import bench
-    src = tmp_path / "step.hip"
-    src.write_text("kernel v1\n")
-    counters = tmp_path / "markov_step_cfg_tiled_counters.txt"
-    counters.write_text(f"kernel_source_sha256_16: {bench._sha(str(src))}\n"
+    counters = tmp_path / "markov_step_cfg_rgv_counters.txt"
+    counters.write_text(f"library_source_hash: {bench.source_hash()}\n"
                         "traffic_bytes_per_launch: 12345\n")
     monkeypatch.setattr(bench, "COUNTERS_FMT", str(tmp_path / "markov_step_{cfg}_{layout}_counters.txt"))
-    monkeypatch.setattr(bench, "STEP_SRC", str(src))
-    assert bench.read_traffic("cfg", "tiled") == 12345
-    src.write_text("kernel v2\n")
-    assert bench.read_traffic("cfg", "tiled") is None
-    assert bench.read_traffic("other", "tiled") is None
+    assert bench.read_traffic("cfg", "rgv") == 12345
+    monkeypatch.setattr(bench, "source_hash", lambda: "another build")
+    assert bench.read_traffic("cfg", "rgv") is None
+    assert bench.read_traffic("other", "rgv") is None
