@@ -105,7 +105,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 CHUNK = 1 << 22
 TAGS = {"W1": 1, "W2": 2, "base": 3, "boost": 4, "h": 5, "w_conf": 6, "anchors": 7,
         "uniforms": 8, "conf": 9, "v_tokens": 10, "v_target": 11, "v_match": 12,
-        "v_draft_logits": 13, "v_noise": 14}
+        "v_draft_logits": 13, "v_noise": 14, "U_rnn": 15, "b_rnn": 16}
 
 
 def _gen(seed: int, tag: str, idx: int = 0) -> np.random.Generator:
@@ -253,6 +253,20 @@ def make_head(cfg: Config, seed: Optional[int] = None, *, w_std: Optional[float]
     return {"W1": _normal_bf16(seed, "W1", (V, r), ws), "W2": _normal_bf16(seed, "W2", (V, r), ws),
             "anchors": _gen(seed, "anchors").integers(0, V, size=(cfg.R,), dtype=np.int32),
             "R": cfg.R, "gamma": cfg.gamma, "V": V, "r": r}
+
+
+def make_rnn_head(cfg: Config, seed: Optional[int] = None, u_std: Optional[float] = None,
+                  b_std: float = 0.5) -> dict:
+    """Weights of the RNN head for cfg's sizes: U [2r, 2r + d] bf16 (rows: r gate
+    units, then r candidate units; columns: the state, embedding and hidden
+    blocks) ~ N(0, u_std) with u_std = 1/sqrt(2r + d) by default (pre-activations
+    of order one), and b [2r] fp32 ~ N(0, b_std)."""
+    seed = cfg.seed if seed is None else seed
+    r, d = cfg.r, cfg.d
+    std = (2 * r + d) ** -0.5 if u_std is None else u_std
+    U = _normal_bf16(seed, "U_rnn", (2 * r, 2 * r + d), std)
+    b = _normal_f32(b_std)(_gen(seed, "b_rnn"), 2 * r)
+    return {"U": U, "b": b}
 
 
 def make_verify_workload(R: int, gamma: int, V: int, seed: int = 11, match_rate: float = 0.7,

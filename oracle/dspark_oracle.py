@@ -145,6 +145,92 @@ def step_scores(W1, W2_store, base_k, prev, mode=GREEDY, temperature=1.0, u_k=No
 
 
 # ---------------------------------------------------------------------------
+# RNN head -- [P3] part 01 (the second, lightweight sequential stage: a recurrent
+# in-block state, updated by a gate over the concatenation of the history
+# state, the previous token's embedding and the backbone hidden state);
+# [P1] §二 设计一 (the RNN head keeps a recurrent state that remembers the whole
+# prefix).  The pages give no equations; the reading taken here:
+#   u_k   = [s_{k-1}; e_k; h_k],  e_k = W1[x_{k-1}] (x_0 = anchor), s_0 = 0
+#   g_k   = sigmoid(G u_k + b_g)                 (update gate, r units)
+#   c_k   = e_k + tanh(C u_k + b_c)              (candidate: the embedding row
+#                                                 plus a correction)
+#   s_k   = g_k * c_k + (1 - g_k) * s_{k-1}
+#   z_k   = base_k + s_k W2                      (the same low-rank projection
+#                                                 to the vocabulary as the Markov head)
+# G and C are stored stacked as U [2r, 2r + d] (rows: the r gate units, then the
+# r candidate units; columns: the s, e and h blocks), b = [b_g; b_c] [2r].
+# Products take bf16 operands (weights, h and e are bf16; the state, kept in
+# higher precision, is rounded to bf16 where it enters a product: fp32 first,
+# then bf16, each to nearest even).  A saturated gate (g = 1) with C = 0 and
+# b_c = 0 gives s_k = e_k: the Markov head.
+# ---------------------------------------------------------------------------
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Value of x rounded to fp32 and then to bf16 (both to nearest, ties to even),
+    as float64."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = x32.view(np.uint32).astype(np.uint64)
+    keep = ((u >> 16) & 1) + 0x7FFF
+    top = ((u + keep) >> 16) << 16
+    finite = np.isfinite(x32)
+    out = np.where(finite, top, u & 0xFFFF0000).astype(np.uint32)
+    return out.view(np.float32).astype(np.float64)
+
+
+def rnn_update(s_prev, e, h_k, U, b):
+    """One gated update of the recurrent state: [n, r] states, [n, r] embedding
+    rows (fp64 values of bf16), [n, d] hidden states -> new states [n, r] fp64."""
+    r = e.shape[1]
+    Uf = bf16_to_f64(U)                                   # [2r, 2r + d]
+    u = np.concatenate([bf16_round(s_prev), e, h_k], axis=1)
+    pre = u @ Uf.T + np.asarray(b, dtype=np.float64)[None, :]
+    g = sigmoid(pre[:, :r])
+    cand = e + np.tanh(pre[:, r:])
+    return g * cand + (1.0 - g) * s_prev
+
+
+def rnn_draft(W1, W2_store, U, b, base, h, anchors, mode=GREEDY, temperature=1.0,
+              uniforms=None, prev_tokens=None, rows=None, keep_state=False, keep_scores=False):
+    """The gamma-step RNN-head refinement (reading above).  ``prev_tokens`` replays
+    the chain with another implementation's tokens as the previous-token inputs
+    (the state then evolves from those tokens), as in markov_draft.
+
+    Returns dict with tokens [n, gamma], margin [n, gamma], and optionally the
+    states [n, gamma, r] (fp64) and the maximised scores [n, gamma, V]."""
+    R, g, V = base.shape
+    r = W1.shape[1]
+    rows = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    n = rows.size
+    tokens = np.zeros((n, g), dtype=np.int32)
+    margin = np.zeros((n, g), dtype=np.float64)
+    states = np.zeros((n, g, r)) if keep_state else None
+    scores = np.zeros((n, g, V)) if keep_scores else None
+    prev = np.asarray(anchors, dtype=np.int64)[rows]
+    s = np.zeros((n, r), dtype=np.float64)
+    W2m = w2_matrix(W2_store)
+    for k in range(g):
+        e = bf16_to_f64(W1[prev])
+        s = rnn_update(s, e, bf16_to_f64(h[rows, k, :]), U, b)
+        z = base[rows, k, :].astype(np.float64) + bf16_round(s) @ W2m
+        u = None if uniforms is None else uniforms[rows, k, :]
+        x, sc, mg = select(z, mode, temperature, u)
+        tokens[:, k] = x
+        margin[:, k] = mg
+        if keep_state:
+            states[:, k, :] = s
+        if keep_scores:
+            scores[:, k, :] = sc
+        prev = x.astype(np.int64) if prev_tokens is None else \
+            np.asarray(prev_tokens, dtype=np.int64)[rows, k]
+    out = {"tokens": tokens, "margin": margin}
+    if keep_state:
+        out["states"] = states
+    if keep_scores:
+        out["scores"] = scores
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Confidence head and STS -- [P1] §二 设计二 (Confidence Head, STS); [P4] fp32 output
 # ---------------------------------------------------------------------------
 
