@@ -22,7 +22,8 @@ from typing import Optional
 __all__ = [
     "DsparkError", "GREEDY", "SAMPLE", "LAYOUT_RGV", "LAYOUT_TILED", "lib", "lib_path",
     "dspark_markov_draft", "dspark_markov_draft_noalloc", "dspark_draft_step",
-    "dspark_draft_step_workspace", "dspark_confidence", "dspark_survival", "dspark_schedule",
+    "dspark_draft_step_workspace", "dspark_rnn_draft", "dspark_rnn_draft_workspace",
+    "dspark_confidence", "dspark_survival", "dspark_schedule",
     "dspark_schedule_ex", "dspark_verify_pack", "dspark_verify_greedy", "dspark_accept_prob",
     "dspark_markov_draft_workspace", "dspark_schedule_workspace",
     "ScheduleInfo", "SCHED_GLOBAL", "SCHED_EARLY_STOP", "SCHED_CAPACITY",
@@ -113,6 +114,11 @@ def lib() -> ctypes.CDLL:
                                     vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz,
                                     ctypes.POINTER(StepEvents), vp]
     L.dspark_draft_step.restype = i32
+    L.dspark_rnn_draft_workspace.argtypes = [i32, i32, i32, i32, i32]
+    L.dspark_rnn_draft_workspace.restype = sz
+    L.dspark_rnn_draft.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                   f32, vp, vp, vp, vp, sz, ctypes.POINTER(StepEvents), vp]
+    L.dspark_rnn_draft.restype = i32
     L.dspark_confidence.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     L.dspark_confidence.restype = i32
     L.dspark_survival.argtypes = [vp, i32, i32, vp, vp]
@@ -310,6 +316,53 @@ def dspark_draft_step(W1, W2, base, anchors, h, w_conf, sps, mode: int = GREEDY,
                              ctypes.byref(ev) if ev is not None else None, _stream(stream))
     _check(st, "dspark_draft_step")
     return tokens, conf, surv, lengths, order, info
+
+
+def dspark_rnn_draft_workspace(R: int, gamma: int, V: int, r: int, d: int) -> int:
+    return int(lib().dspark_rnn_draft_workspace(R, gamma, V, r, d))
+
+
+def dspark_rnn_draft(W1, W2, U, b_rnn, base, h, anchors, mode: int = GREEDY,
+                     temperature: float = 1.0, uniforms=None, tokens=None, state_out=None,
+                     workspace=None, events=None, stream=None, layout: int = LAYOUT_RGV):
+    """gamma-step RNN-head draft.  U [2r, 2r + d] bf16, b_rnn [2r] fp32, h [R, gamma, d]
+    bf16; the other arguments as for dspark_markov_draft; state_out (optional,
+    [R, r] fp32) receives the last state.  Returns tokens [R, gamma]."""
+    torch = _torch()
+    L = lib()
+    V, r = W1.shape
+    R = anchors.shape[0]
+    dev = W1.device
+    _, gamma, d = h.shape
+    shape = (gamma, (V + 31) // 32, 32, R) if layout == LAYOUT_TILED else (R, gamma, V)
+    _need(W1, "W1", _bf16_types(), (V, r), dev)
+    _need(W2, "W2", _bf16_types(), (V, r), dev)
+    _need(U, "U", _bf16_types(), (2 * r, 2 * r + d), dev)
+    _need(b_rnn, "b_rnn", (torch.float32,), (2 * r,), dev)
+    _need(h, "h", _bf16_types(), (R, gamma, d), dev)
+    if base is not None:
+        _need(base, "base", (torch.float32,), shape, dev)
+    if uniforms is not None:
+        _need(uniforms, "uniforms", (torch.float32,), shape, dev)
+    _need(anchors, "anchors", (torch.int32,), (R,), dev)
+    need = int(L.dspark_rnn_draft_workspace(R, gamma, V, r, d))
+    with _on(stream):
+        if tokens is None:
+            tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(tokens, "tokens", (torch.int32,), (R, gamma), dev)
+    if state_out is not None:
+        _need(state_out, "state_out", (torch.float32,), (R, r), dev)
+    ev = _events(events)
+    st = L.dspark_rnn_draft(_ptr(W1), _ptr(W2), _ptr(U), _ptr(b_rnn), _ptr(base), _ptr(h),
+                            _ptr(anchors), R, gamma, V, r, d, int(layout), int(mode),
+                            float(temperature), _ptr(uniforms), _ptr(tokens), _ptr(state_out),
+                            _ptr(workspace),
+                            workspace.numel(), ctypes.byref(ev) if ev is not None else None,
+                            _stream(stream))
+    _check(st, "dspark_rnn_draft")
+    return tokens
 
 
 def dspark_markov_draft_noalloc(W1, W2, base, anchors, tokens, mode: int = GREEDY,

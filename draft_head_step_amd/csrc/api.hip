@@ -179,6 +179,38 @@ dspark_status dspark_draft_step(const uint16_t* W1, const uint16_t* W2, const fl
                                    reinterpret_cast<hipStream_t>(stream));
 }
 
+size_t dspark_rnn_draft_workspace(int R, int gamma, int V, int r, int d) {
+  if (R <= 0 || gamma <= 0 || V < 2 || r <= 0 || d <= 0) return 0;
+  return dspark::rnn_workspace_bytes(R, gamma, V, r);
+}
+
+dspark_status dspark_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uint16_t* U,
+                               const float* b_rnn, const float* base, const uint16_t* h,
+                               const int32_t* anchors, int R, int gamma, int V, int r, int d,
+                               int layout, int mode, float temperature, const float* uniforms,
+                               int32_t* tokens, float* state_out, void* workspace, size_t ws_bytes,
+                               const dspark_step_events* events, void* stream) {
+  dspark::g_last_error[0] = 0;
+  dspark_status st = dspark::check_markov_args(W1, W2, base, anchors, R, gamma, V, r, layout, mode,
+                                               temperature, uniforms, tokens, events);
+  if (st != DSPARK_OK) return st;
+  if (!U || !b_rnn || !h) return fail(DSPARK_EINVAL, "rnn_draft: NULL required pointer");
+  if (d <= 0) return fail(DSPARK_EINVAL, "rnn_draft: d must be positive (got %d)", d);
+  if (d % 8 != 0 || !aligned16(U) || !aligned16(h))
+    return fail(DSPARK_EUNSUPPORTED, "rnn_draft: d must be a multiple of 8 and U, h 16-byte aligned");
+  if ((long long)R * gamma * 2LL * r >= (1LL << 31))
+    return fail(DSPARK_EUNSUPPORTED, "rnn_draft: R * gamma * 2r must be below 2^31");
+  const size_t need = dspark_rnn_draft_workspace(R, gamma, V, r, d);
+  if (!workspace || ws_bytes < need)
+    return fail(DSPARK_EWORKSPACE, "rnn_draft: workspace needs %zu bytes (got %zu)", need,
+                workspace ? ws_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(DSPARK_EINVAL, "rnn_draft: workspace must be 256-byte aligned");
+  return dspark::launch_rnn_draft(W1, W2, U, b_rnn, base, h, anchors, R, gamma, V, r, d, layout,
+                                  mode, temperature, uniforms, tokens, state_out, workspace, events,
+                                  reinterpret_cast<hipStream_t>(stream));
+}
+
 dspark_status dspark_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
                                 const int32_t* tokens, const float* w_conf,
                                 const float* sts_temp, int R, int gamma, int d, int V, int r,

@@ -67,6 +67,33 @@ dspark_status launch_draft_finish(const unsigned long long* words_last, int S, i
                                   const float* sps, int32_t* lengths, int32_t* order,
                                   dspark_schedule_info* info, void* sched_ws, hipStream_t stream);
 
+// ---- RNN head ----
+// Workspace of the RNN-head draft: packed words, the token-independent
+// pre-activations P [R * gamma][2r] fp32, and a ping-pong pair of states in
+// fp32 and in bf16 ([2][R][r] each).
+struct RnnBuffers {
+  unsigned long long* words;
+  size_t words_bytes;
+  float* P;
+  float* s[2];
+  uint16_t* sb[2];
+};
+size_t rnn_workspace_bytes(int R, int gamma, int V, int r);
+RnnBuffers rnn_buffers(void* workspace, int R, int gamma, int V, int r);
+dspark_status launch_rnn_pre(const uint16_t* h, const uint16_t* U, const float* b, int R,
+                             int gamma, int r, int d, const RnnBuffers& B, size_t n_words,
+                             hipStream_t stream);
+dspark_status launch_rnn_state(const uint16_t* W1, const uint16_t* U, const int32_t* anchors,
+                               const unsigned long long* prev, int sub, int R, int gamma, int V,
+                               int r, int d, int k, const RnnBuffers& B, float* s_out,
+                               hipStream_t stream);
+dspark_status launch_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uint16_t* U,
+                               const float* b_rnn, const float* base, const uint16_t* h,
+                               const int32_t* anchors, int R, int gamma, int V, int r, int d,
+                               int layout, int mode, float temperature, const float* uniforms,
+                               int32_t* tokens, float* state_out, void* workspace,
+                               const dspark_step_events* events, hipStream_t stream);
+
 // ---- confidence head + survival ----
 dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int32_t* anchors,
                                 const int32_t* tokens, const float* w_conf, const float* sts_temp,

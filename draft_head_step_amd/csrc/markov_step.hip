@@ -142,36 +142,49 @@ dspark_status prepare_draft(int R, int gamma, int V, int r, int layout, int mode
   return DSPARK_OK;
 }
 
-// The gamma fused step launches.  `w_e` / `se` (optional) ask the steps for
-// the confidence head's embedding term.
+// One fused step launch (position k).  `w_e` / `se` (optional) ask the step
+// for the confidence head's embedding term; `dense` (optional) replaces the
+// gathered W1 rows with dense [R, r] rows.
+dspark_status launch_one_step(const DraftLaunch& L, int k, const uint16_t* W1, const uint16_t* W2,
+                              const float* base, const int32_t* anchors, int R, int gamma, int V,
+                              int r, const float* uniforms, int32_t* tokens, float* bias_out,
+                              unsigned long long* packed, const float* w_e, float* se,
+                              const uint16_t* dense, const dspark_step_events* events,
+                              hipStream_t stream) {
+  Addr ad;
+  ad.row_stride = L.tiled ? 1 : (size_t)gamma * V;
+  ad.cstride = L.tiled ? (size_t)kChunk * R : (size_t)kChunk;
+  ad.vstride = L.tiled ? (size_t)R : 1;
+  ad.total = (size_t)R * gamma * V;
+  const StepIO io{anchors, k == 0 ? nullptr : packed + (size_t)(k - 1) * L.words,
+                  packed + (size_t)k * L.words, tokens, gamma, k, L.sub, w_e, se, dense};
+  ad.k_off = L.tiled ? (size_t)k * L.step_floats : (size_t)k * V;
+  if (L.tiled) ad.total = ad.k_off + L.step_floats;
+  // Timing hooks ride on the dispatch itself (start / stop timestamps of the
+  // kernel's packet), so they add no marker packets between kernels.
+  hipEvent_t ev_begin = nullptr, ev_end = nullptr;
+  if (events && k < events->count) {
+    if (events->begin) ev_begin = reinterpret_cast<hipEvent_t>(events->begin[k]);
+    if (events->end) ev_end = reinterpret_cast<hipEvent_t>(events->end[k]);
+  }
+  hipExtLaunchKernelGGL(L.var.fn, L.grid, dim3(L.var.threads), (uint32_t)L.var.lds, stream,
+                        ev_begin, ev_end, 0u, W1, W2, base, uniforms, io, R, V, r, L.inv_t,
+                        L.p.n_rblocks, L.p.n_vgroups, L.p.cpg, L.cstep, L.p.n_chunks, ad,
+                        bias_out);
+  return check_launch("markov_step_kernel");
+}
+
+// The gamma fused step launches.
 dspark_status launch_steps(const DraftLaunch& L, const uint16_t* W1, const uint16_t* W2,
                            const float* base, const int32_t* anchors, int R, int gamma, int V,
                            int r, const float* uniforms, int32_t* tokens, float* bias_out,
                            unsigned long long* packed, const float* w_e, float* se,
                            const uint16_t* dense, const dspark_step_events* events,
                            hipStream_t stream) {
-  Addr ad;
-  ad.row_stride = L.tiled ? 1 : (size_t)gamma * V;
-  ad.cstride = L.tiled ? (size_t)kChunk * R : (size_t)kChunk;
-  ad.vstride = L.tiled ? (size_t)R : 1;
-  ad.total = (size_t)R * gamma * V;
   for (int k = 0; k < gamma; ++k) {
-    const StepIO io{anchors, k == 0 ? nullptr : packed + (size_t)(k - 1) * L.words,
-                    packed + (size_t)k * L.words, tokens, gamma, k, L.sub, w_e, se, dense};
-    ad.k_off = L.tiled ? (size_t)k * L.step_floats : (size_t)k * V;
-    if (L.tiled) ad.total = ad.k_off + L.step_floats;
-    // Timing hooks ride on the dispatch itself (start / stop timestamps of the
-    // kernel's packet), so they add no marker packets between kernels.
-    hipEvent_t ev_begin = nullptr, ev_end = nullptr;
-    if (events && k < events->count) {
-      if (events->begin) ev_begin = reinterpret_cast<hipEvent_t>(events->begin[k]);
-      if (events->end) ev_end = reinterpret_cast<hipEvent_t>(events->end[k]);
-    }
-    hipExtLaunchKernelGGL(L.var.fn, L.grid, dim3(L.var.threads), (uint32_t)L.var.lds, stream,
-                          ev_begin, ev_end, 0u, W1, W2, base, uniforms, io, R, V, r, L.inv_t,
-                          L.p.n_rblocks, L.p.n_vgroups, L.p.cpg, L.cstep, L.p.n_chunks, ad,
-                          bias_out);
-    dspark_status st = check_launch("markov_step_kernel");
+    const dspark_status st = launch_one_step(L, k, W1, W2, base, anchors, R, gamma, V, r, uniforms,
+                                             tokens, bias_out, packed, w_e, se, dense, events,
+                                             stream);
     if (st != DSPARK_OK) return st;
   }
   return DSPARK_OK;
@@ -274,6 +287,35 @@ dspark_status launch_draft_step(const uint16_t* W1, const uint16_t* W2, const fl
   return launch_draft_finish(packed + (size_t)(gamma - 1) * L.words, L.sub, V, sh, se, sts_temp,
                              R, gamma, tokens, conf, surv, sps, lengths, order, info, sched_ws,
                              stream);
+}
+
+dspark_status launch_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uint16_t* U,
+                               const float* b_rnn, const float* base, const uint16_t* h,
+                               const int32_t* anchors, int R, int gamma, int V, int r, int d,
+                               int layout, int mode, float temperature, const float* uniforms,
+                               int32_t* tokens, float* state_out, void* workspace,
+                               const dspark_step_events* events, hipStream_t stream) {
+  DraftLaunch L;
+  dspark_status st = prepare_draft(R, gamma, V, r, layout, mode, temperature, base != nullptr,
+                                   false, L);
+  if (st != DSPARK_OK) return st;
+  const RnnBuffers B = rnn_buffers(workspace, R, gamma, V, r);
+  st = launch_rnn_pre(h, U, b_rnn, R, gamma, r, d, B, (size_t)gamma * L.words, stream);
+  if (st != DSPARK_OK) return st;
+  for (int k = 0; k < gamma; ++k) {
+    const unsigned long long* prev = k == 0 ? nullptr : B.words + (size_t)(k - 1) * L.words;
+    // the last update may go to the caller's state output (no later step reads it)
+    st = launch_rnn_state(W1, U, anchors, prev, L.sub, R, gamma, V, r, d, k, B,
+                          k == gamma - 1 ? state_out : nullptr, stream);
+    if (st != DSPARK_OK) return st;
+    st = launch_one_step(L, k, W1, W2, base, anchors, R, gamma, V, r, uniforms, tokens, nullptr,
+                         B.words, nullptr, nullptr, B.sb[(k + 1) & 1], events, stream);
+    if (st != DSPARK_OK) return st;
+  }
+  hipLaunchKernelGGL(last_tokens_kernel, dim3((R + 255) / 256), dim3(256), 0, stream,
+                     B.words + (size_t)(gamma - 1) * L.words, L.sub, R, V, gamma, gamma - 1,
+                     tokens);
+  return check_launch("last_tokens_kernel");
 }
 
 }  // namespace dspark

@@ -185,6 +185,46 @@ dspark_status dspark_markov_draft_noalloc(const uint16_t* W1, const uint16_t* W2
                                           float temperature, const float* uniforms,
                                           int32_t* tokens, void* stream);
 
+/* Bytes of workspace dspark_rnn_draft needs (0 if invalid). */
+size_t dspark_rnn_draft_workspace(int R, int gamma, int V, int r, int d);
+
+/*
+ * RNN-head draft: the alternative sequential stage of [P3] part 01 (a
+ * recurrent in-block state updated by a gate over the concatenated history
+ * state, previous-token embedding and backbone hidden state; [P1] section 二
+ * design 1, the RNN head that remembers the whole prefix).  The pages give no
+ * equations; this build reads them as, for k = 1..gamma and every request m,
+ *     u_k = [s_{k-1}; e_k; h_k],  e_k = W1[x_{k-1}, :] (x_0 = anchor),  s_0 = 0
+ *     g_k = sigmoid(G u_k + b_g)             (update gate, r units)
+ *     c_k = e_k + tanh(C u_k + b_c)          (candidate: embedding row + correction)
+ *     s_k = g_k * c_k + (1 - g_k) * s_{k-1}  (fp32 state)
+ *     z_v = base[m, k-1, v] + sum_i bf16(s_k)_i W2(i, v),  x_k selected as in
+ *           dspark_markov_draft (GREEDY or SAMPLE)
+ * Products take bf16 operands with fp32 accumulation: the state enters them
+ * rounded to bf16.  A gate saturated at 1 with C = 0, b_c = 0 is the Markov head.
+ *   U         [2r, 2r + d] bf16, 16-byte aligned: rows 0..r-1 are G, rows
+ *             r..2r-1 are C; columns [0, r) act on s_{k-1}, [r, 2r) on e_k,
+ *             [2r, 2r + d) on h_k.
+ *   b_rnn     [2r] fp32 = [b_g; b_c].
+ *   h         [R, gamma, d] bf16 backbone hidden states (16-byte aligned), d % 8 == 0.
+ *   W1, W2, base, anchors, layout, mode, temperature, uniforms, tokens, events
+ *             as for dspark_markov_draft (no bias output).
+ *   state_out optional [R, r] fp32 output: the state s_gamma after the last step
+ *             (a debugging aid; NULL on the hot path).
+ *   workspace >= dspark_rnn_draft_workspace(R, gamma, V, r, d) bytes, 256-byte
+ *             aligned: packed words, the token-independent pre-activations and
+ *             two copies of the state.
+ * A call is 2 gamma + 2 launches.  Errors: as dspark_markov_draft, plus EINVAL
+ * for NULL U / b_rnn / h or d <= 0, EUNSUPPORTED for d % 8 != 0, a misaligned U
+ * or h, or R * gamma * 2r >= 2^31.
+ */
+dspark_status dspark_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uint16_t* U,
+                               const float* b_rnn, const float* base, const uint16_t* h,
+                               const int32_t* anchors, int R, int gamma, int V, int r, int d,
+                               int layout, int mode, float temperature, const float* uniforms,
+                               int32_t* tokens, float* state_out, void* workspace, size_t ws_bytes,
+                               const dspark_step_events* events, void* stream);
+
 /*
  * Confidence head with STS calibration, [P1] section 二 design 2 (confidence
  * head equation, sequential temperature scaling) and [P4] (fp32 scores):

@@ -123,3 +123,26 @@ def check_schedule(surv_np, sps_np, lengths, order, info):
     assert info.tau_fx == ref["tau_fx"]
     assert info.tau == ref["tau"] and info.theta == ref["theta"]
     return ref
+
+
+def check_rnn_draft(wl, hd, gpu_tokens, rows=None):
+    """Forced-sequence comparison of RNN-head draft tokens on `rows`: the oracle
+    replays each request with the GPU's previous tokens (its state evolving from
+    them); where the oracle's margin exceeds MARGIN the ids must match, elsewhere
+    the GPU's token must score within MARGIN of the maximum."""
+    R, gm, V = wl["base"].shape
+    rows = np.arange(R) if rows is None else np.asarray(rows)
+    ref = O.rnn_draft(wl["W1"], wl["W2"], hd["U"], hd["b"], wl["base"], wl["h"], wl["anchors"],
+                      wl["mode"], wl["temperature"], wl["uniforms"], prev_tokens=gpu_tokens,
+                      rows=rows, keep_scores=True)
+    gt = gpu_tokens[rows]
+    assert np.all((gt >= 0) & (gt < V)), "token id out of range"
+    clear = ref["margin"] > MARGIN
+    bad = clear & (gt != ref["tokens"])
+    assert not bad.any(), (f"{bad.sum()} RNN tokens differ where the margin exceeds {MARGIN}; "
+                           f"first at {np.argwhere(bad)[:4].tolist()}")
+    sc = ref["scores"]
+    smax = sc.max(axis=2)
+    sg = np.take_along_axis(sc, gt[:, :, None].astype(np.int64), axis=2)[:, :, 0]
+    assert np.all(smax - sg <= MARGIN), "an RNN token scores more than the margin below the max"
+    return int(clear.sum()), int((~clear).sum())
