@@ -259,7 +259,7 @@ def main():
                 "capacity_us_p10_p50_p90": capy, "capacity_K": cap,
                 "algorithmic_bytes": int(nbytes),
                 "achieved_GBps_at_p50": round(nbytes / (glob[1] / 1e6) / 1e9, 2),
-                "bound": "latency (launches: 1 survival + 12 schedule)"}
+                "bound": "latency (launches: 1 survival + 11 schedule)"}
 
     cfg = CONFIGS[args.config]
     if cfg.beta_means is not None:
@@ -590,6 +590,55 @@ def main():
                 "frac_of_hbm": round(nb / (p50 / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
                 "note": "one call per event pair: includes the launch"}
 
+    def rnn_side(calls=20):
+        """dspark_rnn_draft on the default workload (the RNN head's alternative
+        sequential stage, same W1 / W2 / logits, seeded head weights U, b): per
+        call ms and the step kernels' launch durations from HIP events; the
+        pre-activation and state-update kernels take the rest of the call."""
+        from draft_head_step_amd.inputs import make_rnn_head
+        hd = make_rnn_head(cfg)
+        U = bf16(hd["U"])
+        b = torch.from_numpy(hd["b"]).to(dev)
+        base, unif = inputs(args.layout)
+        lay = layouts[args.layout]
+        rws = torch.empty(D.dspark_rnn_draft_workspace(R, g, V, r, d), dtype=torch.uint8, device=dev)
+        cnt = [0]
+
+        def one(ev=None):
+            hW1, hW2 = heads[cnt[0] % len(heads)]
+            cnt[0] += 1
+            D.dspark_rnn_draft(hW1, hW2, U, b, base, h, anchors, wl["mode"], wl["temperature"],
+                               unif, tokens=tokens, workspace=rws, events=ev, stream=stream,
+                               layout=lay)
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(g)] for _ in range(calls)]
+        eve = [[torch.cuda.Event(enable_timing=True) for _ in range(g)] for _ in range(calls)]
+        cb = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+        for lst in evb + eve + [cb, ce]:
+            for e in lst:
+                e.record(stream)
+        warm(one, 20.0)
+        for i in range(calls):
+            cb[i].record(stream)
+            one(([e.cuda_event for e in evb[i]], [e.cuda_event for e in eve[i]]))
+            ce[i].record(stream)
+        torch.cuda.synchronize()
+        call_ms = float(np.median([cb[i].elapsed_time(ce[i]) for i in range(calls)]))
+        step_ms = float(np.mean([evb[i][k].elapsed_time(eve[i][k])
+                                 for i in range(calls) for k in range(g)]))
+        flops_pre = 2.0 * R * g * d * 2 * r
+        flops_state = 2.0 * R * 2 * r * 2 * r * g
+        del base, unif, rws, U
+        return {"workload": f"{cfg.name} shapes, RNN head (U [2r, 2r + d] bf16), layout {args.layout}",
+                "ms_per_call_median": round(call_ms, 4),
+                "value": round(R * g / (call_ms / 1e3), 1), "unit": "draft tokens/s",
+                "step_kernel_avg_ms": round(step_ms, 5),
+                "step_kernel_frac_of_hbm": round(nbytes / (step_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "launches_per_call": 2 * g + 2,
+                "recurrent_gemm_flops_per_call": flops_pre + flops_state,
+                "note": "events on the step kernels only; the call also runs the pre-activation "
+                        "GEMM and gamma state updates (rocprofv3 summary in profiles/)"}
+
     def hbm_measured(nbytes=1 << 31, reps=5):
         """Large-copy bandwidth (read + write bytes over time) of torch's device copy:
         a measured reference beside the published peak."""
@@ -693,6 +742,7 @@ def main():
         out["other_configs"] = [whole_step_config("qwen3_8b"), whole_step_config("long_block")]
         out["confidence"] = confidence_side()
         out["verify"] = verify_side()
+        out["rnn_head"] = rnn_side()
         out["hbm_measured"] = hbm_measured()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -17,7 +17,7 @@
 // Up to 8192 candidates one workgroup of 1024 threads (16 wavefronts) does it
 // all in LDS in a single launch.  Beyond that the sort and the scan are spread
 // over tiles of 1024 candidates on the whole device through workspace buffers
-// (a dozen short launches, no host sync).
+// (eleven short launches, no host sync).
 #include <math.h>
 
 #include <atomic>
@@ -566,10 +566,12 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
 //            counts (or, with many tiles, reads it from one separate scan), ranks
 //            its tile stably (the ballot ranking of the single-tile path) and
 //            writes keys and ids to their places.
-// Then: per tile, the sum of its fixed-point survivals; per tile, the carry of
-// the tiles before it, the prefix sums, Theta at each position and the tile's
-// best; one workgroup picks m* over the tiles; lengths count the candidates
-// ranked below m*.  All on the caller's stream, no host sync.
+// Then: per tile, the sum of its fixed-point survivals (this launch also
+// clears the lengths); per tile, the carry of the tiles before it, the prefix
+// sums, Theta at each position and the tile's best; then one launch in which
+// every workgroup takes m* from the tiles' results and counts its positions
+// below m* into the lengths.  Eleven launches (one more beyond 512 tiles, for
+// the digit scans), all on the caller's stream, no host sync.
 // ---------------------------------------------------------------------------
 constexpr int kGT = 256;                  // threads of a sort workgroup
 constexpr int kGW = kGT / 64;
@@ -766,8 +768,11 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long* 
 // Per tile: the sum of its fixed-point survivals.
 __global__ __launch_bounds__(kGT) void sched_tsum_kernel(const uint32_t* __restrict__ sk,
                                                          const int* __restrict__ si, int N,
-                                                         unsigned long long* __restrict__ tsum) {
+                                                         unsigned long long* __restrict__ tsum,
+                                                         int R, int32_t* __restrict__ lengths) {
   __shared__ unsigned long long red[kGW];
+  // The lengths the finishing kernel counts into start at zero.
+  for (int r = blockIdx.x * kGT + threadIdx.x; r < R; r += gridDim.x * kGT) lengths[r] = 0;
   const int p0 = blockIdx.x * kGTile + 4 * threadIdx.x;
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   uint32_t ck[4];
@@ -952,76 +957,70 @@ __global__ __launch_bounds__(kGT) void sched_tbreak_kernel(
   }
 }
 
-// Early stop / capacity: m* (the first break over the tiles, or m_cap), tau*
-// from the tile sums below m*'s tile plus that tile's keys below m*, info,
-// m*; clears lengths for the count.  One workgroup.
-__global__ __launch_bounds__(kT) void sched_pick_ex_kernel(
-    const uint32_t* __restrict__ sk, const unsigned long long* __restrict__ tsum,
-    const int* __restrict__ tbrk, int ntiles, int N, int R, int mode, int m_cap,
-    const float* __restrict__ sps, dspark_schedule_info* info, int* __restrict__ mstar,
-    int32_t* __restrict__ lengths) {
-  __shared__ SchedShared sh;
+// m* and the lengths in one launch: every workgroup takes m* from the
+// per-tile results itself (one wavefront, a fixed-order reduction, so all get
+// the same value), then counts its positions p < m* into l_r (cleared by the
+// tile-sum kernel); workgroup 0 also writes info.
+//   mode 0: the first argmax over m = 0 (tau = R) and the tiles' bests;
+//   mode 1: the first break over the tiles (N if none);
+//   mode 2: m_cap.
+// Modes 1 and 2 take tau* from the tile sums below m*'s tile plus that tile's
+// keys below m*.
+__global__ __launch_bounds__(256) void sched_finish_kernel(
+    const TileBest* __restrict__ tbest, const int* __restrict__ tbrk,
+    const unsigned long long* __restrict__ tsum, const uint32_t* __restrict__ sk,
+    const int* __restrict__ si, int ntiles, int N, int R, int gamma, int mode, int m_cap,
+    const float* __restrict__ sps, dspark_schedule_info* info, int32_t* __restrict__ lengths) {
+  __shared__ int s_m;
+  __shared__ unsigned long long s_S;
+  __shared__ double s_theta;
   const int tid = threadIdx.x;
-  for (int r = tid; r < R; r += kT) lengths[r] = 0;
-  int m_star = m_cap;
-  if (mode == 1) {
-    int b = 0x7fffffff;
-    for (int t = tid; t < ntiles; t += kT) b = min(b, tbrk[t]);
-    m_star = block_min_int(sh, b);
-    if (m_star > N) m_star = N;
-  }
-  const int t_full = m_star / kGTile;
-  unsigned long long part = 0;
-  for (int t = tid; t < t_full; t += kT) part += tsum[t];
-  for (int p = t_full * kGTile + tid; p < m_star; p += kT) part += qfx(sk[p]);
-  const unsigned long long Sm = block_sum_sh(sh, part);
-  if (tid == 0) {
-    *mstar = m_star;
-    if (info) {
-      const unsigned long long tau_fx = ((unsigned long long)R << 40) + Sm;
-      info->B_star = R + m_star;
-      info->m_star = m_star;
-      info->tau_fx = tau_fx;
-      info->tau = __ull2double_rn(tau_fx) * kTauInv;
-      info->theta = theta_at(R, Sm, mode == 1 ? sps[R + m_star - 1] : 1.0f);
+  if (tid < 64) {
+    const int lane = tid;
+    if (mode == 0) {
+      Best best{-1.0, 0x7fffffff, 0ull};
+      if (lane == 0) best = Best{(double)R * (double)sps[R - 1], 0, 0ull};
+      for (int t = lane; t < ntiles; t += 64) better(best, Best{tbest[t].theta, tbest[t].m, tbest[t].S});
+      const Best b = wave_best(best);
+      if (lane == 0) {
+        s_m = b.m;
+        s_S = b.S;
+        s_theta = b.theta;
+      }
+    } else {
+      int m_star = m_cap;
+      if (mode == 1) {
+        uint32_t b = 0x7fffffffu;
+        for (int t = lane; t < ntiles; t += 64) b = min(b, (uint32_t)tbrk[t]);
+        m_star = (int)lane_u32(wave_iscan(b, 0x7fffffffu, MinI32{}), 63);
+        if (m_star > N) m_star = N;
+      }
+      if (blockIdx.x == 0) {
+        const int t_full = m_star / kGTile;
+        unsigned long long part = 0;
+        for (int t = lane; t < t_full; t += 64) part += tsum[t];
+        for (int p = t_full * kGTile + lane; p < m_star; p += 64) part += qfx(sk[p]);
+        const unsigned long long Sm = lane_u64(wave_iscan(part, 0ull, AddU64{}), 63);
+        if (lane == 0) {
+          s_S = Sm;
+          s_theta = theta_at(R, Sm, mode == 1 ? sps[R + m_star - 1] : 1.0f);
+        }
+      }
+      if (lane == 0) s_m = m_star;
     }
   }
-}
-
-// First argmax over m = 0 (tau = R) and the tiles' bests; writes m*, info, and
-// clears lengths for the count.  One workgroup.
-__global__ __launch_bounds__(kT) void sched_pick_kernel(const TileBest* __restrict__ tbest,
-                                                        int ntiles, const float* __restrict__ sps,
-                                                        int R, dspark_schedule_info* info,
-                                                        int* __restrict__ mstar,
-                                                        int32_t* __restrict__ lengths) {
-  __shared__ SchedShared sh;
-  const int tid = threadIdx.x;
-  for (int r = tid; r < R; r += kT) lengths[r] = 0;
-  Best best{-1.0, 0x7fffffff, 0ull};
-  if (tid == 0) best = Best{(double)R * (double)sps[R - 1], 0, 0ull};
-  for (int t = tid; t < ntiles; t += kT) better(best, Best{tbest[t].theta, tbest[t].m, tbest[t].S});
-  block_best(sh, best);
-  if (tid == 0) {
-    *mstar = best.m;
-    if (info) {
-      const unsigned long long tau_fx = ((unsigned long long)R << 40) + best.S;
-      info->B_star = R + best.m;
-      info->m_star = best.m;
-      info->tau_fx = tau_fx;
-      info->tau = __ull2double_rn(tau_fx) * kTauInv;
-      info->theta = best.theta;
-    }
+  __syncthreads();
+  const int m_star = s_m;
+  if (blockIdx.x == 0 && tid == 0 && info) {
+    const unsigned long long tau_fx = ((unsigned long long)R << 40) + s_S;
+    info->B_star = R + m_star;
+    info->m_star = m_star;
+    info->tau_fx = tau_fx;
+    info->tau = __ull2double_rn(tau_fx) * kTauInv;
+    info->theta = s_theta;
   }
-}
-
-// l_r = number of request r's candidates among the first m* sorted positions
-// (the definition; lengths were cleared by the pick kernel).
-__global__ __launch_bounds__(256) void sched_count_kernel(const int* __restrict__ si, int gamma,
-                                                          const int* __restrict__ mstar,
-                                                          int32_t* __restrict__ lengths) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p < *mstar) atomicAdd(&lengths[si[p] / gamma], 1);
+  const int p = blockIdx.x * 256 + tid;
+  if (p < m_star) atomicAdd(&lengths[si[p] / gamma], 1);
 }
 
 // Fused draft step beyond the LDS path: the survivals go to memory first.
@@ -1099,7 +1098,6 @@ dspark_status launch_schedule(const float* surv, const float* sps, int R, int ga
   unsigned long long* tsum =
       reinterpret_cast<unsigned long long*>(hist + (size_t)kDig * ntiles);   // 8-byte aligned
   TileBest* tbest = reinterpret_cast<TileBest*>(tsum + ntiles);
-  int* mstar = reinterpret_cast<int*>(tbest + ntiles);
   const bool inl = ntiles <= kInlineTiles;
   // Keys and ids: surv -> (k1, i1) -> (k0, i0) -> (k1, i1) -> (k0, i0).
   uint32_t* dk[4] = {k1, k0, k1, k0};
@@ -1125,21 +1123,17 @@ dspark_status launch_schedule(const float* surv, const float* sps, int R, int ga
     dspark_status st = check_launch("schedule sort pass");
     if (st != DSPARK_OK) return st;
   }
-  hipLaunchKernelGGL(sched_tsum_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, N, tsum);
-  if (mode == 0) {
+  hipLaunchKernelGGL(sched_tsum_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, N, tsum, R,
+                     lengths);
+  int* tbrk = reinterpret_cast<int*>(tbest);   // one int per tile in the tile-best area
+  if (mode == 0)
     hipLaunchKernelGGL(sched_tscan_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, sps, R, N,
                        tsum, order, tbest);
-    hipLaunchKernelGGL(sched_pick_kernel, dim3(1), dim3(kT), 0, stream, tbest, ntiles, sps, R,
-                       info, mstar, lengths);
-  } else {
-    int* tbrk = reinterpret_cast<int*>(tbest);   // one int per tile in the tile-best area
+  else
     hipLaunchKernelGGL(sched_tbreak_kernel, dim3(ntiles), dim3(kGT), 0, stream, k0, i0, sps, R,
                        N, mode, tsum, order, tbrk);
-    hipLaunchKernelGGL(sched_pick_ex_kernel, dim3(1), dim3(kT), 0, stream, k0, tsum, tbrk,
-                       ntiles, N, R, mode, m_cap, sps, info, mstar, lengths);
-  }
-  hipLaunchKernelGGL(sched_count_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, i0, gamma,
-                     mstar, lengths);
+  hipLaunchKernelGGL(sched_finish_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, tbest, tbrk,
+                     tsum, k0, i0, ntiles, N, R, gamma, mode, m_cap, sps, info, lengths);
   return check_launch("schedule scan");
 }
 
