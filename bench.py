@@ -38,10 +38,23 @@ METRIC = "draft tokens/s (Markov refine+confidence+schedule) at R=256,V=129280; 
 COUNTERS_FMT = os.path.join(ROOT, "profiles", "markov_step_{cfg}_{layout}_counters.txt")
 
 
+STEP_SOURCES = ["markov_kernels.h", "markov_types.h", "packed_words.h", "markov_step.hip",
+                "markov_pick_greedy_row.hip", "markov_pick_greedy_col.hip",
+                "markov_pick_sample_row.hip", "markov_pick_sample_col.hip",
+                "markov_pick_bias_only.hip", "dspark_internal.h"]
+
+
 def source_hash():
-    """Hash of the library sources (the same one the built library carries)."""
+    """Hash of the sources and flags of the fused step kernels (what the counters
+    measure): a change to any other part of the library leaves them valid."""
+    import hashlib
     from draft_head_step_amd import build
-    return build.source_hash()
+    h = hashlib.sha256()
+    for name in STEP_SOURCES:
+        with open(os.path.join(build.CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read() + b"\0")
+    h.update(" ".join(build.HIPCC_FLAGS).encode())
+    return h.hexdigest()[:32]
 
 
 def step_bytes(wl) -> int:
@@ -79,7 +92,7 @@ def read_traffic(cfg, layout):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("library_source_hash") != source_hash():
+    if kv.get("step_source_hash") != source_hash():
         return None
     try:
         return int(float(kv["traffic_bytes_per_launch"]))
@@ -179,6 +192,8 @@ def main():
                          "cold caches, GEMM-only, scheduler stress, other configurations, "
                          "measured bandwidth)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["gemm", "rnn", "sched", "verify"],
+                    help="run one side measurement alone and print its JSON (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -658,11 +673,16 @@ def main():
         return {"copy_GBps": round(2 * nbytes / (float(np.median(ts)) / 1e3) / 1e9, 1),
                 "bytes_copied": nbytes}
 
+    nbytes = step_bytes(wl)
+    if args.only:
+        res = {"gemm": lambda: [gemm_only(args.config), gemm_only("long_block")],
+               "rnn": rnn_side, "sched": scheduler_only, "verify": verify_side}[args.only]()
+        print(json.dumps({"only": args.only, "result": res}), flush=True)
+        return
     ms_per_step, durs = run(args.path, args.layout, args.steps, args.warmup)
     k_ms = float(np.mean(durs))
     pos_ms = durs.mean(axis=0)
     value = R * g / (ms_per_step / 1e3)
-    nbytes = step_bytes(wl)
     achieved = nbytes / (k_ms / 1e3) / 1e9
     # The library runs rank-512 sampling on the K-split kernel, everything else
     # on the plain one.
