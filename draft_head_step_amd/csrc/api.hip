@@ -181,7 +181,7 @@ dspark_status dspark_draft_step(const uint16_t* W1, const uint16_t* W2, const fl
 
 size_t dspark_rnn_draft_workspace(int R, int gamma, int V, int r, int d) {
   if (R <= 0 || gamma <= 0 || V < 2 || r <= 0 || d <= 0) return 0;
-  return dspark::rnn_workspace_bytes(R, gamma, V, r);
+  return dspark::rnn_workspace_bytes(R, gamma, V, r, d);
 }
 
 dspark_status dspark_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uint16_t* U,
@@ -200,6 +200,9 @@ dspark_status dspark_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uin
     return fail(DSPARK_EUNSUPPORTED, "rnn_draft: d must be a multiple of 8 and U, h 16-byte aligned");
   if ((long long)R * gamma * 2LL * r >= (1LL << 31))
     return fail(DSPARK_EUNSUPPORTED, "rnn_draft: R * gamma * 2r must be below 2^31");
+  if (2 * (int64_t)r + d > (1 << 22))
+    return fail(DSPARK_EUNSUPPORTED, "rnn_draft: 2r + d must be at most 2^22 (got %lld)",
+                (long long)(2 * (int64_t)r + d));
   const size_t need = dspark_rnn_draft_workspace(R, gamma, V, r, d);
   if (!workspace || ws_bytes < need)
     return fail(DSPARK_EWORKSPACE, "rnn_draft: workspace needs %zu bytes (got %zu)", need,

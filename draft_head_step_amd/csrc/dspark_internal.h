@@ -69,17 +69,19 @@ dspark_status launch_draft_finish(const unsigned long long* words_last, int S, i
 
 // ---- RNN head ----
 // Workspace of the RNN-head draft: packed words, the token-independent
-// pre-activations P [R * gamma][2r] fp32, and a ping-pong pair of states in
-// fp32 and in bf16 ([2][R][r] each).
+// pre-activations as `splits` partial sums P [splits][R * gamma][2r] fp32, and a
+// ping-pong pair of states in fp32 and in bf16 ([2][R][r] each).
 struct RnnBuffers {
   unsigned long long* words;
   size_t words_bytes;
+  int splits;
   float* P;
   float* s[2];
   uint16_t* sb[2];
 };
-size_t rnn_workspace_bytes(int R, int gamma, int V, int r);
-RnnBuffers rnn_buffers(void* workspace, int R, int gamma, int V, int r);
+int rnn_pre_splits(int R, int gamma, int r, int d);
+size_t rnn_workspace_bytes(int R, int gamma, int V, int r, int d);
+RnnBuffers rnn_buffers(void* workspace, int R, int gamma, int V, int r, int d);
 dspark_status launch_rnn_pre(const uint16_t* h, const uint16_t* U, const float* b, int R,
                              int gamma, int r, int d, const RnnBuffers& B, size_t n_words,
                              hipStream_t stream);

@@ -299,7 +299,7 @@ dspark_status launch_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uin
   dspark_status st = prepare_draft(R, gamma, V, r, layout, mode, temperature, base != nullptr,
                                    false, L);
   if (st != DSPARK_OK) return st;
-  const RnnBuffers B = rnn_buffers(workspace, R, gamma, V, r);
+  const RnnBuffers B = rnn_buffers(workspace, R, gamma, V, r, d);
   st = launch_rnn_pre(h, U, b_rnn, R, gamma, r, d, B, (size_t)gamma * L.words, stream);
   if (st != DSPARK_OK) return st;
   for (int k = 0; k < gamma; ++k) {

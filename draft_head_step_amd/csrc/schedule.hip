@@ -452,20 +452,41 @@ struct FinishArgs {
 // Confidence, STS and survival of request m ([P1] section 二 design 2):
 // c_{m,k} = sigmoid((sh + (se_0 + se_1)) / T_k), a_{m,k} = a_{m,k-1} c_{m,k} in
 // fp32; also the last token.  The survivals go to `sv` (by candidate id) too.
+// The loads of up to kFinBatch positions are issued before any of them is
+// used, so a request costs one memory round trip per kFinBatch positions.
+constexpr int kFinBatch = 8;
+
 __device__ __forceinline__ void finish_request(const FinishArgs& fa, int m, int gamma,
                                                float* __restrict__ sv) {
-  fa.tokens[(size_t)m * gamma + gamma - 1] = read_token(fa.words, m, fa.S, fa.V);
+  const int32_t last = read_token(fa.words, m, fa.S, fa.V);
   float a = 1.0f;
-  for (int k = 0; k < gamma; ++k) {
-    const size_t e = (size_t)m * gamma + k;
-    const float s = fa.sh[e] + (fa.se[2 * e] + fa.se[2 * e + 1]);
-    const float t = fa.sts ? fa.sts[k] : 1.0f;
-    const float c = 1.0f / (1.0f + expf(-(s / t)));
-    fa.conf[e] = c;
-    a = k == 0 ? c : a * c;
-    fa.surv[e] = a;
-    if (sv) sv[e] = a;
+  for (int k0 = 0; k0 < gamma; k0 += kFinBatch) {
+    float s[kFinBatch], t[kFinBatch];
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) {
+      const int k = k0 + j;
+      s[j] = 0.0f;
+      t[j] = 1.0f;
+      if (k < gamma) {
+        const size_t e = (size_t)m * gamma + k;
+        s[j] = fa.sh[e] + (fa.se[2 * e] + fa.se[2 * e + 1]);
+        if (fa.sts) t[j] = fa.sts[k];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) {
+      const int k = k0 + j;
+      if (k < gamma) {
+        const size_t e = (size_t)m * gamma + k;
+        const float c = 1.0f / (1.0f + expf(-(s[j] / t[j])));
+        fa.conf[e] = c;
+        a = k == 0 ? c : a * c;
+        fa.surv[e] = a;
+        if (sv) sv[e] = a;
+      }
+    }
   }
+  fa.tokens[(size_t)m * gamma + gamma - 1] = last;
 }
 
 template <int ITEMS, bool FUSED>

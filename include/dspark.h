@@ -216,7 +216,7 @@ size_t dspark_rnn_draft_workspace(int R, int gamma, int V, int r, int d);
  *             two copies of the state.
  * A call is 2 gamma + 2 launches.  Errors: as dspark_markov_draft, plus EINVAL
  * for NULL U / b_rnn / h or d <= 0, EUNSUPPORTED for d % 8 != 0, a misaligned U
- * or h, or R * gamma * 2r >= 2^31.
+ * or h, R * gamma * 2r >= 2^31, or 2r + d > 2^22.
  */
 dspark_status dspark_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uint16_t* U,
                                const float* b_rnn, const float* base, const uint16_t* h,

@@ -329,3 +329,37 @@ def test_schedule_rejects_tau_overflow_sizes():
     assert L.dspark_schedule(P, P, R, 1, 2 * R, P, None, None, P, 1 << 30, None) == EUNSUPPORTED
     assert D.dspark_schedule_workspace(R, 1) == 0
     assert D.dspark_schedule_workspace(R - 1, 1) > 0
+
+
+def _rnn(**kw):
+    a = dict(W1=P, W2=P, U=P, b=P, base=P, h=P, anchors=P, R=4, g=5, V=4096, r=64, d=256,
+             layout=0, mode=GREEDY, T=1.0, u=None, tokens=P, state=None, ws=0x100000,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return D.lib().dspark_rnn_draft(a["W1"], a["W2"], a["U"], a["b"], a["base"], a["h"],
+                                    a["anchors"], a["R"], a["g"], a["V"], a["r"], a["d"],
+                                    a["layout"], a["mode"], a["T"], a["u"], a["tokens"],
+                                    a["state"], a["ws"], a["ws_bytes"], None, None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(U=None), EINVAL), (dict(b=None), EINVAL), (dict(h=None), EINVAL), (dict(d=0), EINVAL),
+    (dict(d=30), EUNSUPPORTED), (dict(U=P + 4), EUNSUPPORTED), (dict(h=P + 8), EUNSUPPORTED),
+    (dict(R=1 << 20, g=16, r=128), EUNSUPPORTED),
+    (dict(r=512, d=(1 << 22) - 1016), EUNSUPPORTED),
+    (dict(ws=None), EWORKSPACE), (dict(ws_bytes=16), EWORKSPACE), (dict(ws=0x100000 + 16), EINVAL),
+])
+def test_rnn_draft_rejects(kw, want):
+    assert _rnn(**kw) == want
+    assert D.lib().dspark_last_error() != b""
+
+
+@no_gpu
+def test_rnn_workspace_holds_the_pre_activation_partials():
+    # At the DeepSeek-V4 shape the pre-activations are split over K into 4
+    # partial sums of R * gamma * 2r floats; a small shape keeps one.
+    big = D.dspark_rnn_draft_workspace(256, 5, 129280, 512, 7168)
+    assert big >= 4 * 256 * 5 * 1024 * 4
+    small = D.dspark_rnn_draft_workspace(4, 5, 4096, 64, 256)
+    assert 4 * 5 * 128 * 4 <= small < 2 * 4 * 5 * 128 * 4 + (1 << 20)

@@ -59,6 +59,8 @@ CASES = [
     (40, 3, 5000, 512, 64, SAMPLE),      # rank 512 sampling: K-split pairs on dense rows
     (300, 2, 3000, 512, 16, GREEDY),     # rank 512 greedy: eight plain waves, two staging rounds
     (130, 2, 999, 128, 32, GREEDY),
+    (70, 3, 3000, 64, 1000, GREEDY),     # pre-activation GEMM: K in 4 splits, ragged K and M tails
+    (33, 3, 1001, 48, 520, SAMPLE),      # 2 splits, 96 units in a 128-unit tile
 ]
 
 
@@ -92,6 +94,11 @@ def test_rnn_draft_dsv4_shape():
     rng = np.random.default_rng(8)
     rows = np.unique(np.concatenate([[0, 255], [t + rng.integers(32) for t in range(0, 256, 32)]]))
     H.check_rnn_draft(wl, hd, toks, rows)
+    ref = O.rnn_draft(wl["W1"], wl["W2"], hd["U"], hd["b"], wl["base"], wl["h"], wl["anchors"],
+                      wl["mode"], wl["temperature"], wl["uniforms"], prev_tokens=toks, rows=rows,
+                      keep_state=True)
+    err = np.abs(_run.state[rows] - ref["states"][:, -1, :])
+    assert err.max() <= STATE_ATOL, f"state error {err.max():.3g}"
 
 
 @pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
