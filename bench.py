@@ -404,6 +404,44 @@ def main():
         heads = saved
         return (t1 - t0) * 1e3 / steps, durs
 
+    def graph_steps(layout, steps, warmup):
+        """ms per step with the fused call captured in a HIP graph (one graph per
+        weight copy, taken in turn as in the timed steps) and replayed."""
+        base, unif = inputs(layout)
+        lay = layouts[layout]
+
+        def call(i):   # on the current stream: the capture stream inside torch.cuda.graph
+            hW1, hW2 = heads[i % len(heads)]
+            D.dspark_draft_step(hW1, hW2, base, anchors, h, w_conf, sps, wl["mode"],
+                                wl["temperature"], unif, sts_temp=sts, tokens=tokens, conf=conf,
+                                surv=surv, lengths=lengths, workspace=ws_f, layout=lay)
+        for i in range(len(heads)):
+            call(i)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(len(heads)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                call(i)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        cnt = [0]
+
+        def next_replay():
+            graphs[cnt[0] % len(graphs)].replay()
+            cnt[0] += 1
+        warm(next_replay, prewarm_ms)
+        for _ in range(warmup):
+            next_replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            next_replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del graphs, base, unif
+        return (t1 - t0) * 1e3 / steps
+
     def cold_steps(layout, n):
         """Per-step time of the fused call with the caches flushed first (a 512 MB
         read, outside the bracketed step, so no dirty lines are written back
@@ -749,6 +787,12 @@ def main():
                             ev_steps=20)
             out["three_calls"] = dict(summary(ms_c, d_c), launches_per_step=g + 4,
                                       call="dspark_markov_draft + dspark_confidence + dspark_schedule")
+            ms_g = graph_steps(args.layout, max(args.steps // 2, 1), max(args.warmup, 1))
+            out["graph_replay"] = {"ms_per_step": round(ms_g, 4),
+                                   "value": round(R * g / (ms_g / 1e3), 1),
+                                   "weight_copies": len(heads),
+                                   "note": "the fused call captured in a HIP graph (one per "
+                                           "weight copy) and replayed"}
         cold, cold_pos = cold_steps(args.layout, 10)
         out["cold"] = {"ms_per_step_median": round(cold, 4), "value": round(R * g / (cold / 1e3), 1),
                        "whole_step_frac_of_hbm": round(whole / (cold / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -429,12 +429,18 @@ __device__ __forceinline__ int n_whole(int c0, int cstep, int n_valid, int V) {
 // p ^ (q & (COLS/8 - 1)).  Each lane takes one 16-byte piece (its eight w_e
 // values stay in registers) of RPP rows per pass; the lanes of a row add their
 // products in a fixed shuffle order.  Row q is request mbase + q, its token is
-// lane q's x (NaN is written for an invalid token).
+// lane q's x (NaN is written for an invalid token).  The 32 / RPP passes are
+// shared out over the first V groups of the R block (this workgroup takes the
+// passes congruent to `share` mod `nshare`): done by one workgroup alone they
+// would make it finish well after the others.
+template <int COLS>
+constexpr int conf_embed_passes() { return 32 / (64 / (COLS / 8)); }
+
 template <int COLS>
 __device__ __forceinline__ void conf_embed_part(const uint16_t* greg, const float* __restrict__ w_e,
                                                 int k0, int r, int mbase, int R, int x,
                                                 float* __restrict__ se, int gamma, int k, int slot,
-                                                int lane) {
+                                                int lane, int share, int nshare) {
   constexpr int PPR = COLS / 8;
   constexpr int RPP = 64 / PPR;
   const int c = lane % PPR;
@@ -449,7 +455,7 @@ __device__ __forceinline__ void conf_embed_part(const uint16_t* greg, const floa
     for (int t = 0; t < 8; ++t) w[t] = 0.0f;
   }
 #pragma unroll 1
-  for (int ps = 0; ps < 32 / RPP; ++ps) {
+  for (int ps = share; ps < 32 / RPP; ps += nshare) {
     const int q = ps * RPP + lane / PPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(greg + q * COLS + ((c ^ (q & (PPR - 1))) * 8));
     float p = w[0] * bf_lo(v.x);
@@ -724,20 +730,23 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
     }
   };
   // Waits for everything this wave issued, then reads the rows (and, in the
-  // fused draft step, the first V group computes the confidence head's
-  // embedding term from them).
+  // fused draft step, the first V groups share out the confidence head's
+  // embedding term over them).
   auto gather_read = [&]() {
     wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
-    if (io.se && vg == 0) {
+    const int nshare = min(n_vgroups, conf_embed_passes<RK>());
+    if (io.se && vg < nshare) {
 #pragma unroll
       for (int t = 0; t < TW; ++t)
         conf_embed_part<RK>(lds + (gslot * TW + t) * 32 * RK, io.w_e, 0, r, tbase[t], R, xt[t],
-                            io.se, io.gamma, io.k, 0, lane);
+                            io.se, io.gamma, io.k, 0, lane, vg, nshare);
       // the plain kernel holds whole rows: the second K half is empty
+      if (vg == 0) {
 #pragma unroll
-      for (int t = 0; t < TW; ++t)
-        if (half == 0 && m_ok[t]) io.se[((size_t)(tbase[t] + col) * io.gamma + io.k) * 2 + 1] = 0.0f;
+        for (int t = 0; t < TW; ++t)
+          if (half == 0 && m_ok[t]) io.se[((size_t)(tbase[t] + col) * io.gamma + io.k) * 2 + 1] = 0.0f;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -951,8 +960,10 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
     }
     wait_vmcnt<0>();
     __builtin_amdgcn_sched_barrier(0);
-    if (io.se && vg == 0)
-      conf_embed_part<256>(greg, io.w_e, kh * 256, r, pbase, R, x, io.se, io.gamma, io.k, kh, lane);
+    const int nshare = min(n_vgroups, conf_embed_passes<256>());
+    if (io.se && vg < nshare)
+      conf_embed_part<256>(greg, io.w_e, kh * 256, r, pbase, R, x, io.se, io.gamma, io.k, kh, lane,
+                           vg, nshare);
     __builtin_amdgcn_sched_barrier(0);
     const int er = ROWF ? (col ^ (16 * kh)) : col;
 #pragma unroll
