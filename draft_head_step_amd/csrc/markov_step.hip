@@ -201,12 +201,14 @@ MarkovPlan plan_markov(int R, int gamma, int V, int r, int mode, bool for_launch
   // Choices measured on MI355X.  Rank 512 sampling: K-split wave pairs (a
   // plain wave would need the whole SIMD); rank 512 greedy: eight plain waves;
   // up to 64 requests: two-wave workgroups, at most two per CU (fewer,
-  // longer groups).  DSPARK_MARKOV_KSPLIT / _NW / _WG / _STRIDED override the
+  // longer groups).  DSPARK_MARKOV_KSPLIT / _NP / _NW / _WG / _STRIDED override the
   // choice for tuning (and DSPARK_MARKOV_SUBWORDS the words per request).
   if (p.rk == 512 && mode == DSPARK_SAMPLE && nw == 8) nw = 4;
   const int ks_env = env_int("DSPARK_MARKOV_KSPLIT", -1);
   p.ksplit = p.rk == 512 && (ks_env < 0 ? mode == DSPARK_SAMPLE : ks_env != 0);
   if (p.ksplit) nw = 2 * (waves_needed >= 4 ? 4 : waves_needed >= 2 ? 2 : 1);
+  const int np_env = env_int("DSPARK_MARKOV_NP", 0);   // K-split wave pairs per workgroup
+  if (p.ksplit && (np_env == 1 || np_env == 2 || np_env == 4)) nw = 2 * np_env;
   const int nw_env = env_int("DSPARK_MARKOV_NW", 0);
   if (!p.ksplit && (nw_env == 1 || nw_env == 2 || nw_env == 4 || nw_env == 8)) nw = nw_env;
   p.nw = nw;
