@@ -9,7 +9,7 @@
 //   verify_pack:   cu_seqlens = exclusive scan of (1 + l_r) (one workgroup,
 //                  chunks of 1024 with a carry), then one thread per (r, j)
 //                  writes token (anchor or draft j), position pos0[r] + j and
-//                  the request id r;
+//                  the request id r; up to 1024 requests both in one launch;
 //   verify_greedy: one workgroup per flattened row takes the target's argmax
 //                  (16-byte loads, per-thread running max in increasing v,
 //                  smallest id on ties), then one thread per request walks
@@ -81,6 +81,56 @@ __global__ __launch_bounds__(256) void verify_scatter_kernel(
   flat_tokens[dst] = j == 0 ? anchors[r] : tokens[(size_t)r * gamma + j - 1];
   if (flat_pos) flat_pos[dst] = (pos0 ? pos0[r] : 0) + j;
   if (flat_req) flat_req[dst] = r;
+}
+
+// The whole flattening in one workgroup when R <= kPackT: the scan of the
+// sequence lengths, then every (r, j) element scattered by the same threads
+// (one launch instead of two: at these sizes the work is a few microseconds
+// and the second launch cost as much again).
+__global__ __launch_bounds__(kPackT) void verify_pack_small_kernel(
+    const int32_t* __restrict__ anchors, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ lengths, const int32_t* __restrict__ pos0, int R, int gamma,
+    int32_t* __restrict__ cu, int32_t* __restrict__ flat_tokens, int32_t* __restrict__ flat_pos,
+    int32_t* __restrict__ flat_req) {
+  __shared__ int wtot[kPackT / 64];
+  __shared__ int scu[kPackT];
+  __shared__ int slen[kPackT];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int len = t < R ? clamp_len(lengths[t], gamma) : 0;
+  const int v = t < R ? 1 + len : 0;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wtot[w] = inc;
+  __syncthreads();
+  int pre = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < kPackT / 64; ++j) {
+    pre += j < w ? wtot[j] : 0;
+    total += wtot[j];
+  }
+  if (t < R) {
+    cu[t] = pre + inc - v;
+    scu[t] = pre + inc - v;
+    slen[t] = len;
+  }
+  if (t == 0) cu[R] = total;
+  __syncthreads();
+  const int per = 1 + gamma;
+  for (int e = t; e < R * per; e += kPackT) {
+    const int r = e / per;
+    const int j = e - r * per;
+    if (j > slen[r]) continue;
+    const int dst = scu[r] + j;
+    flat_tokens[dst] = j == 0 ? anchors[r] : tokens[(size_t)r * gamma + j - 1];
+    if (flat_pos) flat_pos[dst] = (pos0 ? pos0[r] : 0) + j;
+    if (flat_req) flat_req[dst] = r;
+  }
 }
 
 // Running (max, smallest index) of one thread, merged in a fixed tree.
@@ -257,6 +307,11 @@ dspark_status launch_verify_pack(const int32_t* anchors, const int32_t* tokens,
                                  const int32_t* lengths, const int32_t* pos0, int R, int gamma,
                                  int32_t* flat_tokens, int32_t* flat_pos, int32_t* flat_req,
                                  int32_t* cu_seqlens, hipStream_t stream) {
+  if (R <= kPackT && (long long)R * (1 + gamma) <= (1LL << 20)) {
+    hipLaunchKernelGGL(verify_pack_small_kernel, dim3(1), dim3(kPackT), 0, stream, anchors, tokens,
+                       lengths, pos0, R, gamma, cu_seqlens, flat_tokens, flat_pos, flat_req);
+    return check_launch("verify_pack");
+  }
   hipLaunchKernelGGL(verify_scan_kernel, dim3(1), dim3(kPackT), 0, stream, lengths, R, gamma,
                      cu_seqlens);
   const long long n = (long long)R * (1 + gamma);
