@@ -61,6 +61,8 @@ CASES = [
     (130, 2, 999, 128, 32, GREEDY),
     (70, 3, 3000, 64, 1000, GREEDY),     # pre-activation GEMM: K in 4 splits, ragged K and M tails
     (33, 3, 1001, 48, 520, SAMPLE),      # 2 splits, 96 units in a 128-unit tile
+    (1, 1, 100, 16, 8, GREEDY),          # the smallest shapes: one request, one step, r = 16, d = 8
+    (17, 1, 2000, 32, 24, SAMPLE),       # one step; 16 + 1 requests (a one-request state tile)
 ]
 
 
