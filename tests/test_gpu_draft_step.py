@@ -74,6 +74,8 @@ CASES = [
     ("r512s", 40, 3, 5000, 512, 64, SAMPLE),
     ("r512g", 300, 2, 3000, 512, 16, GREEDY),
     ("global", 2000, 5, 2000, 64, 32, GREEDY),    # 10000 candidates: the schedule's global path
+    ("g1", 50, 1, 3000, 64, 16, SAMPLE),          # one position: prologue, one step, finish
+    ("g16", 20, 16, 2000, 128, 24, GREEDY),       # a long block of sixteen positions
 ]
 
 
