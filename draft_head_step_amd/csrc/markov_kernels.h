@@ -704,29 +704,56 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   constexpr int PPR = RK / 8;       // 16-byte pieces per row
   constexpr int RPI = 64 / PPR;     // rows per direct load
   const int gslot = wave % GWPR;
-  auto gather_issue = [&]() {
-    const u32x4 dw1 = io.dense ? raw_desc(io.dense, (uint32_t)R * (uint32_t)r * 2u)
-                               : raw_desc(W1, (uint32_t)V * (uint32_t)r * 2u);
+  const uint32_t w1_bytes = io.dense ? (uint32_t)R * (uint32_t)r * 2u : (uint32_t)V * (uint32_t)r * 2u;
+  // Source byte offset of the 16-byte piece that direct load i of tile t moves
+  // for this lane (out of range for a row that reads as zeros).
+  auto gather_voff = [&](int t, int i) -> uint32_t {
     const int c = lane % PPR;
+    const int qq = i * RPI + lane / PPR;
+    const int xq = __shfl(xt[t], qq);
+    const int mq = tbase[t] + qq;
+    const bool okq = mq < R && (io.dense != nullptr || xq >= 0);
+    const int src = io.dense ? mq : xq;
+    const int piece = c ^ (qq & (PPR - 1));
+    return (okq && piece * 8 < r) ? (uint32_t)src * (uint32_t)r * 2u + (uint32_t)(piece * 16)
+                                  : kOutOfRange;
+  };
+  auto gather_issue = [&]() {
+    const u32x4 dw1 = raw_desc(io.dense ? io.dense : W1, w1_bytes);
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
       uint16_t* greg = lds + (gslot * TW + t) * 32 * RK;
 #pragma unroll
       for (int i = 0; i < 32 / RPI; ++i) {
-        const int qq = i * RPI + lane / PPR;
-        const int xq = __shfl(xt[t], qq);
-        const int mq = tbase[t] + qq;
-        const bool okq = mq < R && (io.dense != nullptr || xq >= 0);
-        const int src = io.dense ? mq : xq;
-        const int piece = c ^ (qq & (PPR - 1));
-        const uint32_t voff = (okq && piece * 8 < r)
-                                  ? (uint32_t)src * (uint32_t)r * 2u + (uint32_t)(piece * 16)
-                                  : kOutOfRange;
+        const uint32_t voff = gather_voff(t, i);
         asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                      :
                      : "v"(voff), "s"(dw1), "{m0}"(lds_addr(greg + i * RPI * RK))
                      : "memory");
       }
+    }
+  };
+  // Second round: the same pieces are loaded at the start, beside the first
+  // round's direct loads, into the registers that will hold the rows (a lane
+  // has KS pieces of 16 bytes per tile, as many as its MFMA operand), and are
+  // written where the direct loads would put them once the first round has
+  // read the area.  So only one round waits for the memory system.
+  static_assert(32 / RPI == KS, "a lane's gathered pieces fill its operand registers");
+  auto gather_prefetch = [&]() {
+    const Rsrc rw1 = make_rsrc(io.dense ? io.dense : W1, w1_bytes);
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int i = 0; i < KS; ++i)
+        e[t][i] = __builtin_bit_cast(bf16x8, buf_load16(rw1, opaque(gather_voff(t, i))));
+  };
+  auto gather_put = [&]() {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      uint16_t* greg = lds + (gslot * TW + t) * 32 * RK;
+#pragma unroll
+      for (int i = 0; i < KS; ++i)
+        *reinterpret_cast<bf16x8*>(greg + i * RPI * RK + lane * 8) = e[t][i];
     }
   };
   // Waits for everything this wave issued, then reads the rows (and, in the
@@ -779,11 +806,15 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   // staged.  Direct-to-LDS W2 writes the area the rows pass through, so it
   // starts after the last round.  The barrier after each round frees the area
   // for the next round or for the stage buffers.
+  if constexpr (GROUNDS == 2) {
+    if (wave >= GWPR) gather_prefetch();
+  }
   if constexpr (!DMA) prologue();
 #pragma unroll
   for (int rd = 0; rd < GROUNDS; ++rd) {
     if (wave / GWPR == rd) {
-      gather_issue();
+      if (rd == 0) gather_issue();
+      else gather_put();
       gather_read();
     }
     lds_barrier();
