@@ -551,10 +551,10 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
   const int rb = q % n_rblocks;
   const int vg = (q / n_rblocks) * 8 + (id & 7);
   if (vg >= n_vgroups) return;
-  // Iteration i (0 <= i < cpg, a multiple of UNR) handles chunk c0 + i * cstep:
-  // contiguous groups (cstep 1) or groups strided across V (cstep = number of
-  // groups).  Iterations past the group's n_valid chunks are masked, and
-  // prefetches are clamped to the group's last chunk.
+  // Iteration i (0 <= i < n_valid rounded up to a multiple of UNR) handles
+  // chunk c0 + i * cstep: contiguous groups (cstep 1) or groups strided across
+  // V (cstep = number of groups).  Iterations past the group's n_valid chunks
+  // are masked, and prefetches are clamped to the group's last chunk.
   const int c0 = cstep == 1 ? vg * cpg : vg;
   const int n_valid = cstep == 1 ? min(cpg, n_chunks - c0) : (n_chunks - 1 - vg) / cstep + 1;
   auto chunk = [&](int i) { return c0 + min(i, n_valid - 1) * cstep; };
@@ -835,14 +835,18 @@ __attribute__((amdgpu_waves_per_eu(1, plain_max_waves<RK>()))) void markov_step_
       body(std::false_type{}, std::false_type{}, i0 + j, stage[DMA ? 0 : j % WD], accs[j & 1],
            accs[(j + 1) & 1], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS]);
   }
-  for (; i0 < cpg; i0 += UNR) {
+  // Iterations past n_valid (rounded up to the unroll) would only repeat the
+  // group's last chunk under a mask: a short last group stops early instead of
+  // finishing last.
+  const int n_iter = (n_valid + UNR - 1) / UNR * UNR;
+  for (; i0 < n_iter; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
       body(std::true_type{}, std::false_type{}, i0 + j, stage[DMA ? 0 : j % WD], accs[j & 1],
            accs[(j + 1) & 1], eb[(j + NS - 1) % NS], eu[(j + NS - 1) % NS]);
   }
-  // cpg is a multiple of UNR: the last iteration used accs[1] and slot NS - 1.
-  finish(std::true_type{}, cpg - 1, accs[1], eb[NS - 1], eu[NS - 1]);
+  // n_iter is a multiple of UNR: the last iteration used accs[1] and slot NS - 1.
+  finish(std::true_type{}, n_iter - 1, accs[1], eb[NS - 1], eu[NS - 1]);
   if constexpr (DMA) wait_vmcnt<0>();   // no direct load lands in LDS after exit
 
 #pragma unroll
@@ -1129,7 +1133,9 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
       body(std::false_type{}, std::false_type{}, i0 + j, eb[(j + NS - 1) % NS],
            eu[(j + NS - 1) % NS], eb[(j + PD) % NS], eu[(j + PD) % NS]);
   }
-  for (; i0 < cpg; i0 += UNR) {
+  // As in the plain kernel, a short last group stops after its own chunks.
+  const int n_iter = (n_valid + UNR - 1) / UNR * UNR;
+  for (; i0 < n_iter; i0 += UNR) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j)
       body(std::true_type{}, std::false_type{}, i0 + j, eb[(j + NS - 1) % NS],
@@ -1139,8 +1145,8 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   // stage memory, and the workgroup's LDS is released at exit).
   wait_vmcnt<0>();
   lds_barrier();   // the partner's last half-tile
-  // cpg is a multiple of UNR (hence of NS): the last iteration's slot is NS - 1.
-  epilogue(std::true_type{}, cpg - 1, (cpg - 1) & 1, eb[NS - 1], eu[NS - 1]);
+  // n_iter is a multiple of UNR (hence of NS): the last iteration's slot is NS - 1.
+  epilogue(std::true_type{}, n_iter - 1, (n_iter - 1) & 1, eb[NS - 1], eu[NS - 1]);
 
   if constexpr (ROWF) {
     // Each wave holds its 16 requests over all the chunk entries: merge each
