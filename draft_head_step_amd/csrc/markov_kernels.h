@@ -83,6 +83,13 @@ __device__ __forceinline__ void merge_best(float& bv, int& bi, float ov, int oi)
     bi = oi;
   }
 }
+// The same merge without a branch (so that shuffles feeding several merges
+// can all be in flight at once).
+__device__ __forceinline__ void merge_best_sel(float& bv, int& bi, float ov, int oi) {
+  const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+  bv = take ? ov : bv;
+  bi = take ? oi : bi;
+}
 
 // Token x_{k-1} of request m (step 0: the anchor), or -1 if it is not a valid
 // id.  The first V group of each R block also stores it to tokens, which
@@ -188,22 +195,33 @@ __device__ __forceinline__ void select_rows(RowArgmax<N>& am, const float* cb, c
 // each row once.
 template <int N>
 __device__ __forceinline__ void merge_rows(float (&v)[N], int (&id)[N], int lane) {
-  // Both halves are exchanged and merged, and the lane keeps one of the two
-  // results: a select between two array elements would be turned into a
-  // dynamically indexed (scratch) load.
+  // A lane sends its partner the half it drops (the half the partner keeps),
+  // and every shuffle of a level is issued before any merge: the merges are
+  // branch-free selects, so the shuffles do not wait for each other.  The
+  // halves are picked by bit masks, not by selects between array elements
+  // (which the compiler turns into a dynamically indexed scratch load).
 #pragma unroll
   for (int lvl = 0; (N >> lvl) > 1; ++lvl) {
+    constexpr int NH = N / 2;
     const int mask = 16 >> lvl;
     const int H = (N >> lvl) / 2;
-    const bool up = (lane & mask) != 0;
+    const int hi = (lane & mask) ? -1 : 0;   // all ones: this lane keeps the upper half
+    float ov[NH];
+    int oi[NH];
 #pragma unroll
     for (int p = 0; p < H; ++p) {
-      float lo_v = v[p], hi_v = v[H + p];
-      int lo_i = id[p], hi_i = id[H + p];
-      merge_best(lo_v, lo_i, __shfl_xor(v[p], mask), __shfl_xor(id[p], mask));
-      merge_best(hi_v, hi_i, __shfl_xor(v[H + p], mask), __shfl_xor(id[H + p], mask));
-      v[p] = up ? hi_v : lo_v;
-      id[p] = up ? hi_i : lo_i;
+      const int lv = __float_as_int(v[p]), hv = __float_as_int(v[H + p]);
+      ov[p] = __shfl_xor(__int_as_float((lv & hi) | (hv & ~hi)), mask);
+      oi[p] = __shfl_xor((id[p] & hi) | (id[H + p] & ~hi), mask);
+    }
+#pragma unroll
+    for (int p = 0; p < H; ++p) {
+      const int lv = __float_as_int(v[p]), hv = __float_as_int(v[H + p]);
+      float mv = __int_as_float((hv & hi) | (lv & ~hi));
+      int mi = (id[H + p] & hi) | (id[p] & ~hi);
+      merge_best_sel(mv, mi, ov[p], oi[p]);
+      v[p] = mv;
+      id[p] = mi;
     }
   }
   constexpr int LOG = N == 16 ? 4 : N == 8 ? 3 : N == 4 ? 2 : N == 2 ? 1 : 0;
@@ -211,7 +229,7 @@ __device__ __forceinline__ void merge_rows(float (&v)[N], int (&id)[N], int lane
   for (int mask = 16 >> LOG; mask >= 1; mask >>= 1) {
     const float ov = __shfl_xor(v[0], mask);
     const int oi = __shfl_xor(id[0], mask);
-    merge_best(v[0], id[0], ov, oi);
+    merge_best_sel(v[0], id[0], ov, oi);
   }
 }
 
