@@ -192,7 +192,7 @@ def main():
                          "cold caches, GEMM-only, scheduler stress, other configurations, "
                          "measured bandwidth)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["gemm", "rnn", "sched", "verify"],
+    ap.add_argument("--only", choices=["gemm", "rnn", "sched", "verify", "conf"],
                     help="run one side measurement alone and print its JSON (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (counter calibration)")
@@ -713,8 +713,15 @@ def main():
 
     nbytes = step_bytes(wl)
     if args.only:
+        def conf_only():
+            # seeded valid ids in place of a draft's tokens
+            gen = torch.Generator(device="cpu").manual_seed(7)
+            tokens.copy_(torch.randint(0, wl["W1"].shape[0], (R, g), generator=gen,
+                                       dtype=torch.int32))
+            return confidence_side(calls=max(args.steps, 50))
         res = {"gemm": lambda: [gemm_only(args.config), gemm_only("long_block")],
-               "rnn": rnn_side, "sched": scheduler_only, "verify": verify_side}[args.only]()
+               "rnn": rnn_side, "sched": scheduler_only, "verify": verify_side,
+               "conf": conf_only}[args.only]()
         print(json.dumps({"only": args.only, "result": res}), flush=True)
         return
     ms_per_step, durs = run(args.path, args.layout, args.steps, args.warmup)
