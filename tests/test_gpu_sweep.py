@@ -1,0 +1,74 @@
+"""Seeded sweep of the fused draft step over shapes drawn at random (requests,
+positions, vocabulary sizes that are and are not multiples of the 32-entry
+chunk, every Markov rank class, hidden sizes, greedy and sampling at several
+temperatures, both logits layouts, with and without STS), each compared with
+the CPU oracle to the bars stated in gpu_helpers, and its tokens with those of
+dspark_markov_draft on the same inputs.
+
+The draw is fixed (numpy seed), so a failing case can be re-run by its id.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+sys.path.insert(0, os.path.dirname(__file__))
+import gpu_helpers as H  # noqa: E402
+
+import draft_head_step_amd as D  # noqa: E402
+from draft_head_step_amd.inputs import GREEDY, SAMPLE, Config, make_workload, to_tiled  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _cases(n=48, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 3, 31, 32, 33, 64, 97, 130, 257, 300]))
+        g = int(rng.integers(1, 10))
+        V = int(rng.choice([7, 33, 257, 1000, 2048, 3001, 4096]))
+        r = int(16 * rng.integers(1, 33))                  # 16 .. 512
+        d = int(4 * rng.integers(1, 300))                  # multiples of 4
+        mode = int(rng.choice([GREEDY, SAMPLE]))
+        temp = float(rng.choice([0.5, 1.0, 1.7]))
+        sts = bool(rng.integers(0, 2))
+        layout = int(rng.choice([D.LAYOUT_RGV, D.LAYOUT_TILED]))
+        out.append((i, R, g, V, r, d, mode, temp, sts, layout))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("i,R,g,V,r,d,mode,temp,sts,layout", CASES,
+                         ids=[f"sweep{c[0]}" for c in CASES])
+def test_fused_step_sweep(i, R, g, V, r, d, mode, temp, sts, layout):
+    print(f"case sweep{i}: R={R} g={g} V={V} r={r} d={d} mode={mode} T={temp} sts={sts} "
+          f"layout={layout}", flush=True)
+    cfg = Config(f"sweep{i}", R=R, gamma=g, V=V, r=r, d=d, mode=mode, temperature=temp,
+                 w_std=0.2, base_std=1.0, wconf_std=0.05,
+                 sts=tuple(1.0 + 0.15 * k for k in range(g)) if sts else None, seed=900 + i)
+    wl = make_workload(cfg)
+    dev = H.to_device(wl, DEV)
+    if layout == D.LAYOUT_TILED:
+        base = torch.from_numpy(to_tiled(wl["base"])).to(DEV)
+        unif = None if wl["uniforms"] is None else torch.from_numpy(to_tiled(wl["uniforms"])).to(DEV)
+    else:
+        base, unif = dev["base"], dev.get("uniforms")
+    tok, conf, surv, lengths, order, info = D.dspark_draft_step(
+        dev["W1"], dev["W2"], base, dev["anchors"], dev["h"], dev["w_conf"], dev["sps"], mode,
+        temp, unif, sts_temp=dev.get("sts"), want_order=True, want_info=True, layout=layout)
+    ref_tok = D.dspark_markov_draft(dev["W1"], dev["W2"], base, dev["anchors"], mode, temp, unif,
+                                    layout=layout)
+    torch.cuda.synchronize()
+    toks = tok.cpu().numpy()
+    assert np.array_equal(toks, ref_tok.cpu().numpy()), "fused tokens differ from dspark_markov_draft"
+    H.check_draft(wl, toks)
+    H.check_confidence(wl, toks, conf.cpu().numpy(), surv.cpu().numpy())
+    H.check_schedule(surv.cpu().numpy(), wl["sps"], lengths.cpu().numpy(), order.cpu().numpy(),
+                     D.schedule_info(info))
