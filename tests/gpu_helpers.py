@@ -146,3 +146,19 @@ def check_rnn_draft(wl, hd, gpu_tokens, rows=None):
     sg = np.take_along_axis(sc, gt[:, :, None].astype(np.int64), axis=2)[:, :, 0]
     assert np.all(smax - sg <= MARGIN), "an RNN token scores more than the margin below the max"
     return int(clear.sum()), int((~clear).sum())
+
+
+def rnn_state_tol(U_bits: np.ndarray) -> float:
+    """Tolerance of the RNN head's last state (fp32 on the GPU) against the fp64
+    oracle on the forced sequence.  Both round the state to bf16 where it
+    enters a product, so they differ only where the fp32 and fp64 values of a
+    state element fall on the two sides of a bf16 rounding boundary: that
+    element then enters the next product one bf16 step (<= 2^-8, the state lying
+    in (-1, 1)) apart, moving a pre-activation by at most max|U| 2^-8, and the
+    new state by at most 1.5 times that (candidate through tanh, slope <= 1;
+    gate through the sigmoid, slope <= 1/4, times |candidate - old| <= 2).
+    Two such flips are allowed, with 1e-4 as the floor for the fp32 rounding
+    of the update itself."""
+    umax = float(np.abs(O.bf16_to_f64(U_bits)).max())
+    return max(1e-4, 2 * 1.5 * umax * 2.0 ** -8)
+

@@ -1,9 +1,11 @@
-"""Seeded sweep of the fused draft step over shapes drawn at random (requests,
-positions, vocabulary sizes that are and are not multiples of the 32-entry
-chunk, every Markov rank class, hidden sizes, greedy and sampling at several
-temperatures, both logits layouts, with and without STS), each compared with
-the CPU oracle to the bars stated in gpu_helpers, and its tokens with those of
-dspark_markov_draft on the same inputs.
+"""Seeded sweeps over shapes drawn at random (requests, positions, vocabulary
+sizes that are and are not multiples of the 32-entry chunk, every Markov rank
+class, hidden sizes, greedy and sampling at several temperatures, both logits
+layouts, with and without STS):
+  * the fused draft step, compared with the CPU oracle to the bars stated in
+    gpu_helpers, and its tokens with those of dspark_markov_draft on the same
+    inputs;
+  * the RNN-head draft, tokens on the forced sequence and the last state.
 
 The draw is fixed (numpy seed), so a failing case can be re-run by its id.
 """
@@ -72,3 +74,54 @@ def test_fused_step_sweep(i, R, g, V, r, d, mode, temp, sts, layout):
     H.check_confidence(wl, toks, conf.cpu().numpy(), surv.cpu().numpy())
     H.check_schedule(surv.cpu().numpy(), wl["sps"], lengths.cpu().numpy(), order.cpu().numpy(),
                      D.schedule_info(info))
+
+
+# ---------------------------------------------------------------- RNN head
+def _rnn_cases(n=24, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 17, 32, 33, 64, 100, 130, 257]))
+        g = int(rng.integers(1, 7))
+        V = int(rng.choice([33, 257, 1000, 3001]))
+        r = int(16 * rng.integers(1, 33))
+        d = int(8 * rng.integers(1, 160))                  # multiples of 8 (the RNN head's bound)
+        mode = int(rng.choice([GREEDY, SAMPLE]))
+        temp = float(rng.choice([0.7, 1.0, 1.3]))
+        layout = int(rng.choice([D.LAYOUT_RGV, D.LAYOUT_TILED]))
+        out.append((i, R, g, V, r, d, mode, temp, layout))
+    return out
+
+
+RNN_CASES = _rnn_cases()
+
+
+@pytest.mark.parametrize("i,R,g,V,r,d,mode,temp,layout", RNN_CASES,
+                         ids=[f"rnn{c[0]}" for c in RNN_CASES])
+def test_rnn_draft_sweep(i, R, g, V, r, d, mode, temp, layout):
+    print(f"case rnn sweep{i}: R={R} g={g} V={V} r={r} d={d} mode={mode} T={temp} "
+          f"layout={layout}", flush=True)
+    from draft_head_step_amd.inputs import make_rnn_head
+    from oracle import dspark_oracle as O
+    cfg = Config(f"rnn{i}", R=R, gamma=g, V=V, r=r, d=d, mode=mode, temperature=temp, w_std=0.2,
+                 base_std=1.0, wconf_std=0.1, seed=1300 + i)
+    wl = make_workload(cfg)
+    hd = make_rnn_head(cfg)
+    dev = H.to_device(wl, DEV)
+    U = H.dev_bf16(hd["U"], DEV)
+    b = torch.from_numpy(hd["b"]).to(DEV)
+    if layout == D.LAYOUT_TILED:
+        base = torch.from_numpy(to_tiled(wl["base"])).to(DEV)
+        unif = None if wl["uniforms"] is None else torch.from_numpy(to_tiled(wl["uniforms"])).to(DEV)
+    else:
+        base, unif = dev["base"], dev.get("uniforms")
+    state = torch.full((R, r), float("nan"), dtype=torch.float32, device=DEV)
+    tok = D.dspark_rnn_draft(dev["W1"], dev["W2"], U, b, base, dev["h"], dev["anchors"], mode, temp,
+                             unif, state_out=state, layout=layout)
+    torch.cuda.synchronize()
+    toks = tok.cpu().numpy()
+    H.check_rnn_draft(wl, hd, toks)
+    ref = O.rnn_draft(wl["W1"], wl["W2"], hd["U"], hd["b"], wl["base"], wl["h"], wl["anchors"],
+                      mode, temp, wl["uniforms"], prev_tokens=toks, keep_state=True)
+    err = np.abs(state.cpu().numpy() - ref["states"][:, -1, :])
+    assert err.max() <= H.rnn_state_tol(hd["U"]), f"state error {err.max():.3g}"
