@@ -21,8 +21,8 @@ from oracle import dspark_oracle as O  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-# The last state is compared within gpu_helpers.rnn_state_tol (fp32 against
-# fp64; bf16 roundings of the state that fall on different sides of a tie).
+# The last state is compared by gpu_helpers.check_rnn_state (fp32 against fp64;
+# bf16 roundings of the state that fall on different sides of a tie).
 
 
 def _say(msg):
@@ -78,8 +78,7 @@ def test_rnn_draft_matches_oracle(R, g, V, r, d, mode, layout):
     ref = O.rnn_draft(wl["W1"], wl["W2"], hd["U"], hd["b"], wl["base"], wl["h"], wl["anchors"],
                       wl["mode"], wl["temperature"], wl["uniforms"], prev_tokens=toks,
                       keep_state=True)
-    err = np.abs(_run.state - ref["states"][:, -1, :])
-    assert err.max() <= H.rnn_state_tol(hd["U"]), f"state error {err.max():.3g}"
+    H.check_rnn_state(_run.state, ref["states"][:, -1, :], hd["U"], wl["W1"])
 
 
 def test_rnn_draft_dsv4_shape():
@@ -96,8 +95,7 @@ def test_rnn_draft_dsv4_shape():
     ref = O.rnn_draft(wl["W1"], wl["W2"], hd["U"], hd["b"], wl["base"], wl["h"], wl["anchors"],
                       wl["mode"], wl["temperature"], wl["uniforms"], prev_tokens=toks, rows=rows,
                       keep_state=True)
-    err = np.abs(_run.state[rows] - ref["states"][:, -1, :])
-    assert err.max() <= H.rnn_state_tol(hd["U"]), f"state error {err.max():.3g}"
+    H.check_rnn_state(_run.state[rows], ref["states"][:, -1, :], hd["U"], wl["W1"])
 
 
 @pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
