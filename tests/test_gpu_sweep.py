@@ -5,7 +5,9 @@ layouts, with and without STS):
   * the fused draft step, compared with the CPU oracle to the bars stated in
     gpu_helpers, and its tokens with those of dspark_markov_draft on the same
     inputs;
-  * the RNN-head draft, tokens on the forced sequence and the last state.
+  * the RNN-head draft, tokens on the forced sequence and the last state;
+  * the verification side (flattening and greedy accept / correct bit-exact,
+    the acceptance probability within 2e-5 as in test_gpu_verify).
 
 The draw is fixed (numpy seed), so a failing case can be re-run by its id.
 """
@@ -124,3 +126,56 @@ def test_rnn_draft_sweep(i, R, g, V, r, d, mode, temp, layout):
     ref = O.rnn_draft(wl["W1"], wl["W2"], hd["U"], hd["b"], wl["base"], wl["h"], wl["anchors"],
                       mode, temp, wl["uniforms"], prev_tokens=toks, keep_state=True)
     H.check_rnn_state(state.cpu().numpy(), ref["states"][:, -1, :], hd["U"], wl["W1"])
+
+
+# ---------------------------------------------------------------- verification side
+def _verify_cases(n=16, seed=2028):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 63, 64, 65, 500, 1025, 2000]))
+        g = int(rng.integers(1, 12))
+        V = int(rng.choice([2, 37, 1000, 4097, 30000]))
+        rate = float(rng.choice([0.0, 0.5, 0.9, 1.0]))
+        T = float(rng.choice([0.6, 1.0, 1.4]))
+        while R * (1 + g) * V > 40_000_000:      # keep the target logits near 160 MB at most
+            V = max(2, V // 4)
+        out.append((i, R, g, V, rate, T))
+    return out
+
+
+VERIFY_CASES = _verify_cases()
+
+
+@pytest.mark.parametrize("i,R,g,V,rate,T", VERIFY_CASES, ids=[f"verify{c[0]}" for c in VERIFY_CASES])
+def test_verify_sweep(i, R, g, V, rate, T):
+    print(f"case verify sweep{i}: R={R} g={g} V={V} rate={rate} T={T}", flush=True)
+    from draft_head_step_amd.inputs import make_accept_workload, make_verify_workload
+    from oracle import dspark_oracle as O
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    wl = make_verify_workload(R, g, V, seed=1700 + i, match_rate=rate)
+    ref = O.verify_pack(wl["anchors"], wl["tokens"], wl["lengths"], wl["pos0"])
+    ft, fp, fr, cu = D.dspark_verify_pack(dev(wl["anchors"]), dev(wl["tokens"]),
+                                          dev(wl["lengths"]), dev(wl["pos0"]))
+    torch.cuda.synchronize()
+    B = ref["B"]
+    assert np.array_equal(cu.cpu().numpy(), ref["cu_seqlens"])
+    assert np.array_equal(ft.cpu().numpy()[:B], ref["tokens"])
+    assert np.array_equal(fp.cpu().numpy()[:B], ref["positions"])
+    assert np.array_equal(fr.cpu().numpy()[:B], ref["request"])
+    # greedy accept / correct on the flattened target rows
+    tl = np.ascontiguousarray(np.concatenate(
+        [wl["target"][r, :ref["cu_seqlens"][r + 1] - ref["cu_seqlens"][r]] for r in range(R)], axis=0))
+    rg = O.verify_greedy(tl, ref["cu_seqlens"], wl["tokens"], wl["lengths"])
+    acc, nxt, amax = D.dspark_verify_greedy(dev(tl), dev(ref["cu_seqlens"]), dev(wl["tokens"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(amax.cpu().numpy()[:B], rg["target_argmax"])
+    assert np.array_equal(acc.cpu().numpy(), rg["accepted"])
+    assert np.array_equal(nxt.cpu().numpy(), rg["next_token"])
+    # acceptance probability on a few row pairs of this vocabulary
+    aw = make_accept_workload(min(B, 16), V, seed=1800 + i)
+    ra = O.accept_prob(aw["draft"], aw["target"], T)
+    ga = D.dspark_accept_prob(dev(aw["draft"]), dev(aw["target"]), T).cpu().numpy()
+    assert np.abs(ga.astype(np.float64) - ra).max() <= 2e-5
