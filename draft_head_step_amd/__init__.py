@@ -10,7 +10,7 @@ raises: there is no fallback path.
 Entry points (same names as the C ABI):
   dspark_markov_draft, dspark_confidence, dspark_survival, dspark_schedule,
   dspark_schedule_ex, dspark_verify_pack, dspark_verify_greedy, dspark_accept_prob,
-  dspark_markov_draft_workspace, dspark_schedule_workspace.
+  dspark_markov_draft_workspace, dspark_schedule_workspace, dspark_w2_store_from_rv.
 """
 from __future__ import annotations
 
@@ -25,7 +25,7 @@ __all__ = [
     "dspark_draft_step_workspace", "dspark_rnn_draft", "dspark_rnn_draft_workspace",
     "dspark_confidence", "dspark_survival", "dspark_schedule",
     "dspark_schedule_ex", "dspark_verify_pack", "dspark_verify_greedy", "dspark_accept_prob",
-    "dspark_markov_draft_workspace", "dspark_schedule_workspace",
+    "dspark_markov_draft_workspace", "dspark_schedule_workspace", "dspark_w2_store_from_rv",
     "ScheduleInfo", "SCHED_GLOBAL", "SCHED_EARLY_STOP", "SCHED_CAPACITY",
 ]
 
@@ -135,6 +135,8 @@ def lib() -> ctypes.CDLL:
     L.dspark_verify_greedy.restype = i32
     L.dspark_accept_prob.argtypes = [vp, vp, i32, i32, f32, vp, vp]
     L.dspark_accept_prob.restype = i32
+    L.dspark_w2_store_from_rv.argtypes = [vp, i32, i32, vp, vp]
+    L.dspark_w2_store_from_rv.restype = i32
     _LIB = L
     return L
 
@@ -437,6 +439,20 @@ def dspark_survival(conf, surv=None, stream=None):
     _check(lib().dspark_survival(_ptr(conf), R, gamma, _ptr(surv), _stream(stream)),
            "dspark_survival")
     return surv
+
+
+def dspark_w2_store_from_rv(w2_rv, out=None, stream=None):
+    """W2 given row by row as [r, V] bf16 -> the [V, r] storage the draft calls take."""
+    torch = _torch()
+    r, V = w2_rv.shape
+    _need(w2_rv, "w2_rv", _bf16_types(), (r, V), w2_rv.device)
+    if out is None:
+        with _on(stream):
+            out = torch.empty((V, r), dtype=w2_rv.dtype, device=w2_rv.device)
+    _need(out, "out", _bf16_types(), (V, r), w2_rv.device)
+    _check(lib().dspark_w2_store_from_rv(_ptr(w2_rv), r, V, _ptr(out), _stream(stream)),
+           "dspark_w2_store_from_rv")
+    return out
 
 
 def dspark_schedule(surv, sps, lengths=None, order=None, want_order: bool = False, info=None,

@@ -26,7 +26,8 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
 SOURCES = ["api.hip", "markov_step.hip", "markov_pick_greedy_row.hip", "markov_pick_greedy_col.hip",
            "markov_pick_sample_row.hip", "markov_pick_sample_col.hip", "markov_pick_bias_only.hip",
-           "confidence.hip", "schedule.hip", "verify.hip", "noalloc.hip", "rnn_head.hip"]
+           "confidence.hip", "schedule.hip", "verify.hip", "noalloc.hip", "rnn_head.hip",
+           "layout.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

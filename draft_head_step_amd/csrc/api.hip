@@ -235,6 +235,24 @@ dspark_status dspark_survival(const float* conf, int R, int gamma, float* surv, 
   return dspark::launch_survival(conf, R, gamma, surv, reinterpret_cast<hipStream_t>(stream));
 }
 
+dspark_status dspark_w2_store_from_rv(const uint16_t* w2_rv, int r, int V, uint16_t* w2_store,
+                                     void* stream) {
+  dspark::g_last_error[0] = 0;
+  if (!w2_rv || !w2_store) return fail(DSPARK_EINVAL, "w2_store_from_rv: NULL required pointer");
+  if (r <= 0 || V <= 0) return fail(DSPARK_EINVAL, "w2_store_from_rv: sizes must be positive");
+  // grid: ceil(V/64) x ceil(r/64) tiles of 256 threads (y at most 65535; the x
+  // dimension's work-items below 2^32)
+  if (r > 64 * 65535 || V >= (1 << 30))
+    return fail(DSPARK_EUNSUPPORTED, "w2_store_from_rv: r above 4194240 or V above 2^30 - 1");
+  const char* a = reinterpret_cast<const char*>(w2_rv);
+  const char* b = reinterpret_cast<const char*>(w2_store);
+  const size_t n = (size_t)r * (size_t)V * 2;
+  if (a < b + n && b < a + n)
+    return fail(DSPARK_EINVAL, "w2_store_from_rv: source and destination may not overlap");
+  return dspark::launch_w2_store_from_rv(w2_rv, w2_store, r, V,
+                                         reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t dspark_schedule_workspace(int R, int gamma) {
   if (R <= 0 || gamma <= 0) return 0;
   if ((long long)R * gamma > DSPARK_MAX_CANDIDATES) return 0;

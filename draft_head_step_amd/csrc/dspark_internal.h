@@ -102,6 +102,8 @@ dspark_status launch_confidence(const uint16_t* h, const uint16_t* W1, const int
                                 int R, int gamma, int d, int V, int r, float* conf, float* surv,
                                 hipStream_t stream);
 dspark_status launch_survival(const float* conf, int R, int gamma, float* surv, hipStream_t stream);
+dspark_status launch_w2_store_from_rv(const uint16_t* w2_rv, uint16_t* w2_store, int r, int V,
+                                      hipStream_t stream);
 
 // ---- verification side ----
 dspark_status launch_verify_pack(const int32_t* anchors, const int32_t* tokens,

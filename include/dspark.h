@@ -257,6 +257,21 @@ dspark_status dspark_confidence(const uint16_t* h, const uint16_t* W1, const int
  */
 dspark_status dspark_survival(const float* conf, int R, int gamma, float* surv, void* stream);
 
+/*
+ * W2 storage conversion.  The draft entry points take the r x V projection of
+ * [P1] section 二 design 1 (Markov-head equation) stored column by column
+ * (element (i, v) at W2[v * r + i]); this converts a row-by-row copy (element
+ * (i, v) at w2_rv[i * V + v]) into that storage, once, when the weights are
+ * loaded.  Off the drafting path.
+ *   w2_rv     [r, V] bf16 device array (read).
+ *   w2_store  [V, r] bf16 device array (written); must not overlap w2_rv.
+ * Enqueued on `stream`; no host sync.  Errors: EINVAL for NULL pointers,
+ * sizes <= 0 or overlapping arrays; EUNSUPPORTED for r above 4194240 or V
+ * above 2^30 - 1; EDEVICE on a launch failure.
+ */
+dspark_status dspark_w2_store_from_rv(const uint16_t* w2_rv, int r, int V, uint16_t* w2_store,
+                                     void* stream);
+
 /* Bytes of workspace dspark_schedule needs (0 if invalid). */
 size_t dspark_schedule_workspace(int R, int gamma);
 

@@ -123,6 +123,20 @@ def test_survival_rejects():
 
 
 @no_gpu
+def test_w2_store_from_rv_rejects():
+    L = D.lib()
+    assert L.dspark_w2_store_from_rv(None, 512, 1000, P + (1 << 24), None) == EINVAL
+    assert L.dspark_w2_store_from_rv(P, 512, 1000, None, None) == EINVAL
+    assert L.dspark_w2_store_from_rv(P, 0, 1000, P + (1 << 24), None) == EINVAL
+    assert L.dspark_w2_store_from_rv(P, 512, -1, P + (1 << 24), None) == EINVAL
+    # the two arrays overlap (1000 x 512 bf16 = 1,024,000 bytes each)
+    assert L.dspark_w2_store_from_rv(P, 512, 1000, P + 1_000_000, None) == EINVAL
+    assert L.dspark_w2_store_from_rv(P + 1_000_000, 512, 1000, P, None) == EINVAL
+    assert L.dspark_w2_store_from_rv(P, 64 * 65535 + 1, 4, P + (1 << 40), None) == EUNSUPPORTED
+    assert L.dspark_w2_store_from_rv(P, 16, 1 << 30, P + (1 << 40), None) == EUNSUPPORTED
+
+
+@no_gpu
 @pytest.mark.parametrize("kw,want", [
     (dict(surv=None), EINVAL), (dict(sps=None), EINVAL), (dict(lengths=None), EINVAL),
     (dict(R=0), EINVAL), (dict(B_max=23), EINVAL),
