@@ -28,6 +28,8 @@ namespace {
 constexpr int kPackT = 1024;
 constexpr int kRowT = 256;
 constexpr int kRowW = kRowT / 64;
+constexpr int kRowU = 4;   // loads in flight per thread in the row argmax
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int clamp_len(int l, int gamma) { return min(max(l, 0), gamma); }
 
@@ -135,10 +137,9 @@ __global__ __launch_bounds__(kPackT) void verify_pack_small_kernel(
 
 // Running (max, smallest index) of one thread, merged in a fixed tree.
 __device__ __forceinline__ void take(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
+  const bool t = (v > bv) | ((v == bv) & (i < bi));   // selects, no branch
+  bv = t ? v : bv;
+  bi = t ? i : bi;
 }
 
 __global__ __launch_bounds__(kRowT) void verify_argmax_kernel(const float* __restrict__ logits,
@@ -154,10 +155,29 @@ __global__ __launch_bounds__(kRowT) void verify_argmax_kernel(const float* __res
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   if (vec) {
-    const float4* z4 = reinterpret_cast<const float4*>(z);
+    // Each row is read once: non-temporal loads, kRowU of them in flight per
+    // thread before any is used (one per thread leaves the memory system
+    // underfed).  take() is a lexicographic max, so the order of the elements
+    // does not matter.
+    const v4f* z4 = reinterpret_cast<const v4f*>(z);
     const int n4 = V >> 2;
-    for (int p = t; p < n4; p += kRowT) {
-      const float4 q = z4[p];
+    int p = t;
+    for (; p + (kRowU - 1) * kRowT < n4; p += kRowU * kRowT) {
+      v4f q[kRowU];
+#pragma unroll
+      for (int u = 0; u < kRowU; ++u) q[u] = __builtin_nontemporal_load(z4 + p + u * kRowT);
+      __builtin_amdgcn_sched_barrier(0);   // all loads issued before the first compare
+#pragma unroll
+      for (int u = 0; u < kRowU; ++u) {
+        const int e = 4 * (p + u * kRowT);
+        take(bv, bi, q[u].x, e);
+        take(bv, bi, q[u].y, e + 1);
+        take(bv, bi, q[u].z, e + 2);
+        take(bv, bi, q[u].w, e + 3);
+      }
+    }
+    for (; p < n4; p += kRowT) {
+      const v4f q = __builtin_nontemporal_load(z4 + p);
       take(bv, bi, q.x, 4 * p);
       take(bv, bi, q.y, 4 * p + 1);
       take(bv, bi, q.z, 4 * p + 2);
