@@ -224,6 +224,7 @@ __global__ __launch_bounds__(256) void verify_accept_kernel(const int32_t* __res
 // sum of 2^(x' - max)) pairs and uses the hardware 2^x.
 constexpr int kAccT = 1024;
 constexpr int kAccW = kAccT / 64;
+constexpr int kAccU = 2;   // loop iterations whose loads are in flight together
 
 struct MaxSum {
   float m;
@@ -276,11 +277,30 @@ __global__ __launch_bounds__(kAccT) void accept_prob_kernel(const float* __restr
     const float* b = zt + (size_t)row * V;
     MaxSum md{-INFINITY, 0.0f}, mt{-INFINITY, 0.0f};
     if (vec) {
-      const float4* a4 = reinterpret_cast<const float4*>(a);
-      const float4* b4 = reinterpret_cast<const float4*>(b);
-      for (int p = t; p < (V >> 2); p += kAccT) {
-        const float4 x = a4[p];
-        const float4 y = b4[p];
+      // kAccU iterations' loads of both rows in flight before the first use
+      // (same element order as one at a time).  The rows are read again by the
+      // second pass, so these loads keep their lines.
+      const v4f* a4 = reinterpret_cast<const v4f*>(a);
+      const v4f* b4 = reinterpret_cast<const v4f*>(b);
+      const int V4 = V >> 2;
+      int p = t;
+      for (; p + (kAccU - 1) * kAccT < V4; p += kAccU * kAccT) {
+        v4f x[kAccU], y[kAccU];
+#pragma unroll
+        for (int u = 0; u < kAccU; ++u) {
+          x[u] = a4[p + u * kAccT];
+          y[u] = b4[p + u * kAccT];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kAccU; ++u) {
+          add4(md, x[u].x * k2, x[u].y * k2, x[u].z * k2, x[u].w * k2);
+          add4(mt, y[u].x * k2, y[u].y * k2, y[u].z * k2, y[u].w * k2);
+        }
+      }
+      for (; p < V4; p += kAccT) {
+        const v4f x = a4[p];
+        const v4f y = b4[p];
         add4(md, x.x * k2, x.y * k2, x.z * k2, x.w * k2);
         add4(mt, y.x * k2, y.y * k2, y.z * k2, y.w * k2);
       }
@@ -299,11 +319,27 @@ __global__ __launch_bounds__(kAccT) void accept_prob_kernel(const float* __restr
       return fminf(exp2_(fmaf(x, k2, -Ld)), exp2_(fmaf(y, k2, -Lt)));
     };
     if (vec) {
-      const float4* a4 = reinterpret_cast<const float4*>(a);
-      const float4* b4 = reinterpret_cast<const float4*>(b);
-      for (int p = t; p < (V >> 2); p += kAccT) {
-        const float4 x = a4[p];
-        const float4 y = b4[p];
+      // The second and last read of the rows: non-temporal, kAccU in flight.
+      const v4f* a4 = reinterpret_cast<const v4f*>(a);
+      const v4f* b4 = reinterpret_cast<const v4f*>(b);
+      const int V4 = V >> 2;
+      int p = t;
+      for (; p + (kAccU - 1) * kAccT < V4; p += kAccU * kAccT) {
+        v4f x[kAccU], y[kAccU];
+#pragma unroll
+        for (int u = 0; u < kAccU; ++u) {
+          x[u] = __builtin_nontemporal_load(a4 + p + u * kAccT);
+          y[u] = __builtin_nontemporal_load(b4 + p + u * kAccT);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kAccU; ++u)
+          acc += (term(x[u].x, y[u].x) + term(x[u].y, y[u].y)) +
+                 (term(x[u].z, y[u].z) + term(x[u].w, y[u].w));
+      }
+      for (; p < V4; p += kAccT) {
+        const v4f x = __builtin_nontemporal_load(a4 + p);
+        const v4f y = __builtin_nontemporal_load(b4 + p);
         acc += (term(x.x, y.x) + term(x.y, y.y)) + (term(x.z, y.z) + term(x.w, y.w));
       }
     } else {
