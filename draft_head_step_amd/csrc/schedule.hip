@@ -598,6 +598,7 @@ constexpr int kGT = 256;                  // threads of a sort workgroup
 constexpr int kGW = kGT / 64;
 constexpr int kGItems = 4;
 constexpr int kGTile = kGT * kGItems;     // candidates per tile
+constexpr int kHistBatch = 32;            // tile counts a scatter thread has in flight
 static_assert(kGT == kDig, "one thread per digit in the tile kernels");
 
 __device__ __forceinline__ int tile_elem(int t, int w, int i, int lane) {
@@ -615,12 +616,22 @@ __global__ __launch_bounds__(kGT) void sched_hist_kernel(const float* __restrict
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   h[threadIdx.x] = 0;
-  __syncthreads();
+  // Every item's key is loaded before the first count (items past N read
+  // element 0 and are not counted), so the loads are in flight together
+  // rather than one round trip each.
+  uint32_t k[kGItems];
+  bool ok[kGItems];
 #pragma unroll
   for (int i = 0; i < kGItems; ++i) {
     const int e = tile_elem(t, w, i, lane);
-    if (e < N) atomicAdd(&h[((FIRST ? key_of(surv[e]) : keys[e]) >> shift) & 0xff], 1);
+    ok[i] = e < N;
+    const int ec = ok[i] ? e : 0;
+    k[i] = FIRST ? key_of(surv[ec]) : keys[ec];
   }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kGItems; ++i)
+    if (ok[i]) atomicAdd(&h[(k[i] >> shift) & 0xff], 1);
   __syncthreads();
   hist[t * kDig + threadIdx.x] = h[threadIdx.x];
 }
@@ -691,22 +702,36 @@ __global__ __launch_bounds__(kGT) void sched_scatter_kernel(
   int id[kGItems];
   bool ok[kGItems];
   int rk[kGItems];
+  // Loads without branches (items past N read element 0, then take the
+  // padding key), so they are in flight together.
 #pragma unroll
   for (int i = 0; i < kGItems; ++i) {
     const int e = tile_elem(t, w, i, lane);
     ok[i] = e < N;
-    ck[i] = ok[i] ? (FIRST ? key_of(surv[e]) : sk[e]) : 0xffffffffu;
-    id[i] = FIRST ? e : (ok[i] ? si[e] : -1);
+    const int ec = ok[i] ? e : 0;
+    const uint32_t kv = FIRST ? key_of(surv[ec]) : sk[ec];
+    const int iv = FIRST ? e : si[ec];
+    ck[i] = ok[i] ? kv : 0xffffffffu;
+    id[i] = ok[i] ? iv : -1;
   }
   // This tile's global base of digit d.
   int base;
   if (INLINE) {
+    // The counts of every tile for digit d: kHistBatch loads in flight at a
+    // time (tiles past the last read the last one and add nothing).
     int total = 0, pre = 0;
-#pragma unroll 8
-    for (int t2 = 0; t2 < ntiles; ++t2) {
-      const int h = hist[t2 * kDig + d];
-      total += h;
-      pre += t2 < t ? h : 0;
+    for (int c0 = 0; c0 < ntiles; c0 += kHistBatch) {
+      int hv[kHistBatch];
+#pragma unroll
+      for (int j = 0; j < kHistBatch; ++j)
+        hv[j] = hist[min(c0 + j, ntiles - 1) * kDig + d];
+#pragma unroll
+      for (int j = 0; j < kHistBatch; ++j) {
+        const int t2 = c0 + j;
+        const int h = t2 < ntiles ? hv[j] : 0;
+        total += h;
+        pre += t2 < t ? h : 0;
+      }
     }
     // exclusive scan of the digit totals over the 256 threads
     int inc = total;
