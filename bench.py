@@ -41,7 +41,7 @@ COUNTERS_FMT = os.path.join(ROOT, "profiles", "markov_step_{cfg}_{layout}_counte
 STEP_SOURCES = ["markov_kernels.h", "markov_types.h", "packed_words.h", "markov_step.hip",
                 "markov_pick_greedy_row.hip", "markov_pick_greedy_col.hip",
                 "markov_pick_sample_row.hip", "markov_pick_sample_col.hip",
-                "markov_pick_bias_only.hip", "dspark_internal.h"]
+                "markov_pick_bias_only.hip", "dspark_internal.h", "sched_lds.h"]
 
 
 def source_hash():
@@ -756,10 +756,17 @@ def main():
     value = R * g / (ms_per_step / 1e3)
     achieved = nbytes / (k_ms / 1e3) / 1e9
     # The library runs rank-512 sampling on the K-split kernel, everything else
-    # on the plain one.
+    # on the plain one; the fused call's last step may be the K-split kernel
+    # that also does the finishing work (the launch count says which).
     kernel = "markov_step_ksplit_kernel" if (r > 256 and wl["mode"]) else "markov_step_kernel"
     whole = whole_step_bytes(wl)
-    launches = g + 2 if args.path == "fused" else g + 4
+    if args.path == "fused":
+        launches = D.dspark_draft_step_launches(R, g, V, r, layouts[args.layout], wl["mode"],
+                                                wl["temperature"])
+        if kernel == "markov_step_ksplit_kernel" and launches == g + 1:
+            kernel = "markov_step_ksplit_kernel (last step: markov_step_ksplit_fin_kernel)"
+    else:
+        launches = g + 4
 
     def summary(ms, dd):
         km = float(np.mean(dd))

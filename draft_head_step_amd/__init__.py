@@ -22,7 +22,8 @@ from typing import Optional
 __all__ = [
     "DsparkError", "GREEDY", "SAMPLE", "LAYOUT_RGV", "LAYOUT_TILED", "lib", "lib_path",
     "dspark_markov_draft", "dspark_markov_draft_noalloc", "dspark_draft_step",
-    "dspark_draft_step_workspace", "dspark_rnn_draft", "dspark_rnn_draft_workspace",
+    "dspark_draft_step_workspace", "dspark_draft_step_launches", "dspark_rnn_draft",
+    "dspark_rnn_draft_workspace",
     "dspark_confidence", "dspark_survival", "dspark_schedule",
     "dspark_schedule_ex", "dspark_verify_pack", "dspark_verify_greedy", "dspark_accept_prob",
     "dspark_markov_draft_workspace", "dspark_schedule_workspace", "dspark_w2_store_from_rv",
@@ -110,6 +111,9 @@ def lib() -> ctypes.CDLL:
     L.dspark_markov_draft_noalloc.restype = i32
     L.dspark_draft_step_workspace.argtypes = [i32, i32, i32, i32]
     L.dspark_draft_step_workspace.restype = sz
+    L.dspark_draft_step_launches.argtypes = [i32, i32, i32, i32, i32, i32, f32,
+                                             ctypes.POINTER(ctypes.c_int)]
+    L.dspark_draft_step_launches.restype = i32
     L.dspark_draft_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp,
                                     vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz,
                                     ctypes.POINTER(StepEvents), vp]
@@ -248,6 +252,17 @@ def dspark_markov_draft(W1, W2, base, anchors, mode: int = GREEDY, temperature: 
 
 def dspark_draft_step_workspace(R: int, gamma: int, V: int, r: int) -> int:
     return int(lib().dspark_draft_step_workspace(R, gamma, V, r))
+
+
+def dspark_draft_step_launches(R: int, gamma: int, V: int, r: int, layout: int = LAYOUT_RGV,
+                               mode: int = SAMPLE, temperature: float = 1.0) -> int:
+    """Kernel launches of one dspark_draft_step call at these sizes (aligned W1
+    and w_conf); planning on the host for the current device."""
+    n = ctypes.c_int(0)
+    _check(lib().dspark_draft_step_launches(R, gamma, V, r, int(layout), int(mode),
+                                            float(temperature), ctypes.byref(n)),
+           "dspark_draft_step_launches")
+    return n.value
 
 
 def _events(events):

@@ -59,10 +59,12 @@ def source_hash() -> str:
 
 
 # Step kernels whose waits count the loads issued after a direct-to-LDS copy
-# (rank 512 without a bias output).  Scratch traffic would count in the same
+# (rank 512 without a bias output, and the fused step's last-step K-split
+# kernel, which never has one).  Scratch traffic would count in the same
 # counter; a spill can only make such a wait stricter, but the build insists on
 # none so that the counted loads are exactly the ones in the source.
-COUNTED_WAIT_KERNEL = re.compile(r"markov_step_(?:ksplit_kernelILi\d+E|kernelILi512E)\S*Lb0E")
+COUNTED_WAIT_KERNEL = re.compile(
+    r"markov_step_(?:(?:ksplit_kernelILi\d+E|kernelILi512E)\S*Lb0E|ksplit_fin_kernelILi\d+E)")
 
 
 def scratch_offenders(remarks: str) -> list:

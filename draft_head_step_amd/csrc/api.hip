@@ -148,6 +148,22 @@ size_t dspark_draft_step_workspace(int R, int gamma, int V, int r) {
   return dspark::draft_step_workspace_bytes(R, gamma, V, r);
 }
 
+dspark_status dspark_draft_step_launches(int R, int gamma, int V, int r, int layout, int mode,
+                                        float temperature, int* count) {
+  dspark::g_last_error[0] = 0;
+  if (!count) return fail(DSPARK_EINVAL, "draft_step_launches: NULL count");
+  if (R <= 0 || gamma <= 0 || V < 2 || r <= 0 || r > DSPARK_MAX_RANK)
+    return fail(DSPARK_EINVAL, "draft_step_launches: bad sizes R=%d gamma=%d V=%d r=%d", R, gamma,
+                V, r);
+  if (layout != DSPARK_LAYOUT_RGV && layout != DSPARK_LAYOUT_TILED)
+    return fail(DSPARK_EINVAL, "draft_step_launches: unknown layout %d", layout);
+  if (mode != DSPARK_GREEDY && mode != DSPARK_SAMPLE)
+    return fail(DSPARK_EINVAL, "draft_step_launches: unknown mode %d", mode);
+  if (mode == DSPARK_SAMPLE && !(temperature > 0.0f))
+    return fail(DSPARK_EINVAL, "draft_step_launches: temperature must be positive");
+  return dspark::draft_step_launch_count(R, gamma, V, r, layout, mode, temperature, count);
+}
+
 dspark_status dspark_draft_step(const uint16_t* W1, const uint16_t* W2, const float* base,
                                 const int32_t* anchors, int R, int gamma, int V, int r,
                                 int layout, int mode, float temperature, const float* uniforms,

@@ -55,6 +55,11 @@ dspark_status launch_draft_step(const uint16_t* W1, const uint16_t* W2, const fl
                                 float* surv, int32_t* lengths, int32_t* order,
                                 dspark_schedule_info* info, void* workspace,
                                 const dspark_step_events* events, hipStream_t stream);
+// Kernel launches of one launch_draft_step (W1 and w_e 16-byte aligned), and
+// of one launch_schedule.
+dspark_status draft_step_launch_count(int R, int gamma, int V, int r, int layout, int mode,
+                                      float temperature, int* count);
+int schedule_launch_count(int R, int gamma);
 // Clears n_words packed words and writes sh[m * gamma + k] = w_h . h[m, k, :].
 dspark_status launch_conf_prologue(const uint16_t* h, const float* w_h, int R, int gamma, int d,
                                    float* sh, unsigned long long* words, size_t n_words,

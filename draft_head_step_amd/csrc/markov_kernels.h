@@ -56,6 +56,7 @@
 
 #include "markov_types.h"
 #include "packed_words.h"
+#include "sched_lds.h"
 
 namespace dspark {
 namespace {
@@ -927,16 +928,30 @@ constexpr size_t ksplit_lds_bytes() {
   return loop > gather ? loop : gather;
 }
 
-// One K-split workgroup (its LDS stages and exchange buffer) fills a CU's LDS:
-// at most two waves per SIMD.
-template <int NP, int MODE, int EPI, bool BIAS>
-__global__ __launch_bounds__(NP * 128)
-__attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
+// The fused draft step's finishing work inside its last step (see StepIO),
+// on a workgroup with no step work: x_{gamma-2} (the anchors when gamma = 1)
+// from the previous step's words, the last position's embedding term from
+// W1 and w_e, then the confidences, survivals and the schedule.
+template <int NW>
+__device__ void finish_in_step(const StepIO& io, const FinParams& fp, const uint16_t* W1, int R,
+                               int V, int r, unsigned char* smem) {
+  const FinishArgs fa{io.prev, io.sub, V, fp.sh, io.se, fp.sts, nullptr, fp.conf, fp.surv,
+                      io.anchors, W1, io.w_e, r};
+  schedule_lds_body<kFinStepItems, kFinInStep, NW>(smem, nullptr, fp.sps, R, io.gamma,
+                                                   R * io.gamma, 0, 0, fp.lengths, fp.order,
+                                                   fp.info, fa);
+}
+
+// The K-split step for one workgroup.  FIN: the fused draft step's last step
+// (see FinParams), instantiated in a kernel of its own so that the other steps
+// run without it.
+template <int NP, int MODE, int EPI, bool BIAS, bool FIN>
+__device__ __forceinline__ void ksplit_step(
     const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
     const float* __restrict__ base, const float* __restrict__ unif,
-    StepIO io, int R, int V, int r, float inv_t, int n_rblocks, int n_vgroups, int cpg,
-    int cstep, int n_chunks, Addr ad, float* __restrict__ bias_out) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const StepIO& io, int R, int V, int r, float inv_t, int n_rblocks, int n_vgroups, int cpg,
+    int cstep, int n_chunks, const Addr& ad, float* __restrict__ bias_out, const FinParams& fp,
+    unsigned char* smem) {
   constexpr bool ROWF = EPI == kEpiRow;
   constexpr int RK = 512;
   constexpr int NW = 2 * NP;
@@ -970,7 +985,15 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
   const int q = id >> 3;
   const int rb = q % n_rblocks;
   const int vg = (q / n_rblocks) * 8 + (id & 7);
-  if (vg >= n_vgroups) return;
+  if (vg >= n_vgroups) {
+    if constexpr (FIN) {
+      static_assert(!BIAS, "the fused step has no bias output");
+      static_assert(sched_lds_bytes<kFinStepItems, NW>() <= ksplit_lds_bytes<NP>(),
+                    "the finishing schedule fits in the step workgroup's LDS");
+      if (rb == 0 && vg == n_vgroups) finish_in_step<NW>(io, fp, W1, R, V, r, smem);
+    }
+    return;
+  }
   const int c0 = cstep == 1 ? vg * cpg : vg;
   const int n_valid = cstep == 1 ? min(cpg, n_chunks - c0) : (n_chunks - 1 - vg) / cstep + 1;
   auto chunk = [&](int i) { return c0 + min(i, n_valid - 1) * cstep; };
@@ -1202,6 +1225,65 @@ __attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
                 x >= 0 ? pack_best(best, best_i) : kPoison);
     }
   }
+  if constexpr (FIN) {
+    // The workgroup that publishes last unpacks x_{gamma-1} of every request.
+    // The results are agent-scope atomics, complete once each wave's memory
+    // counter drains; then one count per workgroup, and the last reads the
+    // words with agent-scope loads (all S of a request in flight together:
+    // past S the last word again, which leaves the maximum unchanged).  No
+    // cache-wide write-back or invalidate, which would cost the workgroups
+    // still streaming their L2 contents.
+    wait_vmcnt<0>();
+    __syncthreads();
+    int* last = reinterpret_cast<int*>(smem);
+    if (tid == 0)
+      last[0] = __hip_atomic_fetch_add(fp.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (unsigned int)(n_rblocks * n_vgroups - 1);
+    __syncthreads();
+    if (last[0]) {
+      for (int m = tid; m < R; m += NW * 64) {
+        const unsigned long long* wm = io.best + (size_t)m * io.sub;
+        unsigned long long w[kMaxSubWords];
+#pragma unroll
+        for (int j = 0; j < kMaxSubWords; ++j)
+          w[j] = __hip_atomic_load(wm + min(j, io.sub - 1), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long b = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxSubWords; ++j) b = w[j] > b ? w[j] : b;
+        io.tokens[(size_t)m * io.gamma + io.k] = unpack_token(b, V);
+      }
+    }
+  }
+}
+
+// One K-split workgroup (its LDS stages and exchange buffer) fills a CU's LDS:
+// at most two waves per SIMD.
+template <int NP, int MODE, int EPI, bool BIAS>
+__global__ __launch_bounds__(NP * 128)
+__attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_kernel(
+    const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
+    const float* __restrict__ base, const float* __restrict__ unif,
+    StepIO io, int R, int V, int r, float inv_t, int n_rblocks, int n_vgroups, int cpg,
+    int cstep, int n_chunks, Addr ad, float* __restrict__ bias_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  ksplit_step<NP, MODE, EPI, BIAS, false>(W1, W2, base, unif, io, R, V, r, inv_t, n_rblocks,
+                                          n_vgroups, cpg, cstep, n_chunks, ad, bias_out,
+                                          FinParams{}, smem);
+}
+
+// The fused draft step's last step: the same, plus the finishing work.
+template <int NP, int MODE, int EPI>
+__global__ __launch_bounds__(NP * 128)
+__attribute__((amdgpu_waves_per_eu(1, 2))) void markov_step_ksplit_fin_kernel(
+    const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
+    const float* __restrict__ base, const float* __restrict__ unif,
+    StepIO io, int R, int V, int r, float inv_t, int n_rblocks, int n_vgroups, int cpg,
+    int cstep, int n_chunks, Addr ad, float* __restrict__ bias_out, FinParams fp) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  ksplit_step<NP, MODE, EPI, false, true>(W1, W2, base, unif, io, R, V, r, inv_t, n_rblocks,
+                                          n_vgroups, cpg, cstep, n_chunks, ad, bias_out, fp,
+                                          smem);
 }
 
 // ---- variant tables ----
@@ -1213,8 +1295,10 @@ StepVariant plain_variant() {
 }
 template <int NP, int MODE, int EPI, bool BIAS>
 StepVariant ksplit_variant() {
+  StepFinKernel fin = nullptr;
+  if constexpr (!BIAS) fin = &markov_step_ksplit_fin_kernel<NP, MODE, EPI>;
   return {&markov_step_ksplit_kernel<NP, MODE, EPI, BIAS>, NP * 128, ksplit_lds_bytes<NP>(),
-          NP * 32, kSplitUnroll};
+          NP * 32, kSplitUnroll, fin};
 }
 
 template <int RK, int MODE, int EPI, bool BIAS>

@@ -60,6 +60,10 @@ int prepare_variant(const StepVariant& v) {
   const void* f = reinterpret_cast<const void*>(v.fn);
   if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)v.lds) != hipSuccess)
     return -1;
+  if (v.fn_fin && hipFuncSetAttribute(reinterpret_cast<const void*>(v.fn_fin),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)v.lds) != hipSuccess)
+    return -1;
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, v.threads, v.lds) != hipSuccess || nb < 1)
     nb = 1;
@@ -92,6 +96,7 @@ struct DraftLaunch {
   bool tiled;
   float inv_t;
   int kmode;
+  int bpc;             // step workgroups that fit on one CU
 };
 
 dspark_status prepare_draft(int R, int gamma, int V, int r, int layout, int mode, float temperature,
@@ -105,6 +110,7 @@ dspark_status prepare_draft(int R, int gamma, int V, int r, int layout, int mode
   p.n_rblocks = (R + L.var.rows - 1) / L.var.rows;   // the variant's requests per workgroup
   const int bpc = prepare_variant(L.var);
   if (bpc < 0) return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the Markov step kernel");
+  L.bpc = bpc;
 
   // One wave of workgroups: as many as fit on the device at once, split between
   // the R blocks (each V group is walked by n_rblocks workgroups).  Groups hold
@@ -150,7 +156,7 @@ dspark_status launch_one_step(const DraftLaunch& L, int k, const uint16_t* W1, c
                               int r, const float* uniforms, int32_t* tokens, float* bias_out,
                               unsigned long long* packed, const float* w_e, float* se,
                               const uint16_t* dense, const dspark_step_events* events,
-                              hipStream_t stream) {
+                              hipStream_t stream, const FinParams* fin = nullptr) {
   Addr ad;
   ad.row_stride = L.tiled ? 1 : (size_t)gamma * V;
   ad.cstride = L.tiled ? (size_t)kChunk * R : (size_t)kChunk;
@@ -167,10 +173,16 @@ dspark_status launch_one_step(const DraftLaunch& L, int k, const uint16_t* W1, c
     if (events->begin) ev_begin = reinterpret_cast<hipEvent_t>(events->begin[k]);
     if (events->end) ev_end = reinterpret_cast<hipEvent_t>(events->end[k]);
   }
-  hipExtLaunchKernelGGL(L.var.fn, L.grid, dim3(L.var.threads), (uint32_t)L.var.lds, stream,
-                        ev_begin, ev_end, 0u, W1, W2, base, uniforms, io, R, V, r, L.inv_t,
-                        L.p.n_rblocks, L.p.n_vgroups, L.p.cpg, L.cstep, L.p.n_chunks, ad,
-                        bias_out);
+  if (fin)
+    hipExtLaunchKernelGGL(L.var.fn_fin, L.grid, dim3(L.var.threads), (uint32_t)L.var.lds, stream,
+                          ev_begin, ev_end, 0u, W1, W2, base, uniforms, io, R, V, r, L.inv_t,
+                          L.p.n_rblocks, L.p.n_vgroups, L.p.cpg, L.cstep, L.p.n_chunks, ad,
+                          bias_out, *fin);
+  else
+    hipExtLaunchKernelGGL(L.var.fn, L.grid, dim3(L.var.threads), (uint32_t)L.var.lds, stream,
+                          ev_begin, ev_end, 0u, W1, W2, base, uniforms, io, R, V, r, L.inv_t,
+                          L.p.n_rblocks, L.p.n_vgroups, L.p.cpg, L.cstep, L.p.n_chunks, ad,
+                          bias_out);
   return check_launch("markov_step_kernel");
 }
 
@@ -252,8 +264,39 @@ dspark_status launch_markov_draft(const uint16_t* W1, const uint16_t* W2, const 
   return check_launch("last_tokens_kernel");
 }
 
+// The fused call's words: the packed per-step results, then the last step's
+// count of finished workgroups (cleared with them).
+size_t draft_step_words_bytes(int R, int gamma, int V, int r) {
+  return plan_markov(R, gamma, V, r, DSPARK_GREEDY, false).ws_bytes + 16;
+}
+
+// The finishing work needs x_0 .. x_{gamma-2} only, so where the last step's
+// launch has a workgroup without step work (a K-split variant with a
+// finishing kernel, an empty V group in R block 0, every workgroup resident at
+// once) it runs there, beside the step; else it is a launch of its own after
+// the last step.  `aligned`: W1 and w_e 16-byte aligned.
+static bool finish_in_last_step(const DraftLaunch& L, int R, int gamma, int r, bool aligned) {
+  const int padded_groups = (int)L.grid.x / L.p.n_rblocks;
+  return L.var.fn_fin && (long)R * gamma <= (long)kFinStepItems * L.var.threads &&
+         padded_groups > L.p.n_vgroups && (long)L.grid.x <= (long)device_cus() * L.bpc &&
+         r % 8 == 0 && aligned;
+}
+
+dspark_status draft_step_launch_count(int R, int gamma, int V, int r, int layout, int mode,
+                                      float temperature, int* count) {
+  DraftLaunch L;
+  const dspark_status st = prepare_draft(R, gamma, V, r, layout, mode, temperature, true, false, L);
+  if (st != DSPARK_OK) return st;
+  const long N = (long)R * gamma;
+  const int finish = finish_in_last_step(L, R, gamma, r, true) ? 0
+                     : N <= 8192                              ? 1
+                                                              : 1 + schedule_launch_count(R, gamma);
+  *count = 1 + gamma + finish;
+  return DSPARK_OK;
+}
+
 size_t draft_step_workspace_bytes(int R, int gamma, int V, int r) {
-  const size_t words = plan_markov(R, gamma, V, r, DSPARK_GREEDY, false).ws_bytes;
+  const size_t words = draft_step_words_bytes(R, gamma, V, r);
   const size_t conf = (size_t)R * gamma * 3 * sizeof(float);   // sh, se (two halves)
   const size_t sched = schedule_workspace_bytes(R, gamma);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -274,21 +317,46 @@ dspark_status launch_draft_step(const uint16_t* W1, const uint16_t* W2, const fl
   if (st != DSPARK_OK) return st;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
-  const size_t words_bytes = plan_markov(R, gamma, V, r, DSPARK_GREEDY, false).ws_bytes;
+  const size_t words_bytes = draft_step_words_bytes(R, gamma, V, r);
   unsigned long long* packed = reinterpret_cast<unsigned long long*>(ws);
+  unsigned int* done = reinterpret_cast<unsigned int*>(packed + (size_t)gamma * L.words);
   float* sh = reinterpret_cast<float*>(ws + up(words_bytes));
   float* se = sh + (size_t)R * gamma;
   void* sched_ws = ws + up(words_bytes) + up((size_t)R * gamma * 3 * sizeof(float));
-  // Prologue: clear the words the steps combine into, and the hidden-state
-  // part of every confidence logit (it does not depend on the draft).
-  st = launch_conf_prologue(h, w_conf, R, gamma, d, sh, packed, (size_t)gamma * L.words, stream);
+  // Prologue: clear the words the steps combine into (and the count after
+  // them), and the hidden-state part of every confidence logit (it does not
+  // depend on the draft).
+  st = launch_conf_prologue(h, w_conf, R, gamma, d, sh, packed, (size_t)gamma * L.words + 2,
+                            stream);
   if (st != DSPARK_OK) return st;
-  st = launch_steps(L, W1, W2, base, anchors, R, gamma, V, r, uniforms, tokens, nullptr, packed,
-                    w_conf + d, se, nullptr, events, stream);
-  if (st != DSPARK_OK) return st;
-  return launch_draft_finish(packed + (size_t)(gamma - 1) * L.words, L.sub, V, sh, se, sts_temp,
-                             R, gamma, tokens, conf, surv, sps, lengths, order, info, sched_ws,
-                             stream);
+  const float* w_e = w_conf + d;
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
+  const bool in_step = finish_in_last_step(L, R, gamma, r, a16(W1) && a16(w_e));
+  if (!in_step) {
+    st = launch_steps(L, W1, W2, base, anchors, R, gamma, V, r, uniforms, tokens, nullptr, packed,
+                      w_e, se, nullptr, events, stream);
+    if (st != DSPARK_OK) return st;
+    return launch_draft_finish(packed + (size_t)(gamma - 1) * L.words, L.sub, V, sh, se,
+                               sts_temp, R, gamma, tokens, conf, surv, sps, lengths, order, info,
+                               sched_ws, stream);
+  }
+  for (int k = 0; k + 1 < gamma; ++k) {
+    st = launch_one_step(L, k, W1, W2, base, anchors, R, gamma, V, r, uniforms, tokens, nullptr,
+                         packed, w_e, se, nullptr, events, stream);
+    if (st != DSPARK_OK) return st;
+  }
+  FinParams fin{};
+  fin.sh = sh;
+  fin.sts = sts_temp;
+  fin.sps = sps;
+  fin.conf = conf;
+  fin.surv = surv;
+  fin.lengths = lengths;
+  fin.order = order;
+  fin.info = info;
+  fin.done = done;
+  return launch_one_step(L, gamma - 1, W1, W2, base, anchors, R, gamma, V, r, uniforms, tokens,
+                         nullptr, packed, w_e, se, nullptr, events, stream, &fin);
 }
 
 dspark_status launch_rnn_draft(const uint16_t* W1, const uint16_t* W2, const uint16_t* U,

@@ -27,6 +27,10 @@ constexpr int kEpiNone = 0;
 constexpr int kEpiCol = 1;
 constexpr int kEpiRow = 2;
 
+// Items per thread of the finishing schedule inside the fused step's last
+// step (see StepIO): it covers R gamma <= 4 x the K-split workgroup's threads.
+constexpr int kFinStepItems = 4;
+
 // Where a step kernel takes its input tokens and leaves its results.
 struct StepIO {
   const int32_t* anchors;              // step 0: x_0
@@ -48,6 +52,23 @@ struct StepIO {
   const uint16_t* dense;
 };
 
+// The fused draft step's last step (a variant's fn_fin): the finishing work
+// (confidences, STS, survivals and the schedule, which need x_0 .. x_{gamma-2}
+// only) runs on the workgroup of R block 0's first empty V group, beside the
+// step workgroups, and the step workgroup that finishes last writes x_{gamma-1}
+// to tokens.  A kernel argument of that launch only.
+struct FinParams {
+  const float* sh;                     // w_h . h [R][gamma]
+  const float* sts;                    // [gamma] or NULL
+  const float* sps;                    // SPS table
+  float* conf;                         // [R][gamma]
+  float* surv;                         // [R][gamma]
+  int32_t* lengths;                    // [R]
+  int32_t* order;                      // [R * gamma] or NULL
+  dspark_schedule_info* info;          // or NULL
+  unsigned int* done;                  // step workgroups finished, 0 before the step
+};
+
 // Element (m, k, v) of base / uniforms / bias_out is at float offset
 // k_off + m * row_stride + (v / 32) * cstride + (v % 32) * vstride in either
 // layout; the kernels' resources cover [block start, total).  Byte offsets
@@ -58,6 +79,9 @@ struct Addr {
 
 using StepKernel = void (*)(const uint16_t*, const uint16_t*, const float*, const float*,
                             StepIO, int, int, int, float, int, int, int, int, int, Addr, float*);
+using StepFinKernel = void (*)(const uint16_t*, const uint16_t*, const float*, const float*,
+                               StepIO, int, int, int, float, int, int, int, int, int, Addr,
+                               float*, FinParams);
 
 struct StepVariant {
   StepKernel fn;
@@ -65,6 +89,7 @@ struct StepVariant {
   size_t lds;
   int rows;     // requests per workgroup
   int unroll;   // chunks per group must be a multiple of this
+  StepFinKernel fn_fin;   // the fused step's last step with its finishing work, or NULL
 };
 
 // Kernel tables, one translation unit each (they compile in parallel).

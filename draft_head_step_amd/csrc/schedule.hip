@@ -24,472 +24,12 @@
 
 #include "dspark_internal.h"
 #include "packed_words.h"
+#include "sched_lds.h"
 
 namespace dspark {
 namespace {
 
-constexpr int kT = 1024;          // threads
-constexpr int kW = kT / 64;       // wavefronts
-constexpr int kDig = 256;         // radix digits per pass
-constexpr double kTauScale = 1099511627776.0;       // 2^40
-constexpr double kTauInv = 1.0 / 1099511627776.0;   // 2^-40
-
-
-struct SchedShared {
-  int cnt[kW * kDig];        // per-wave digit counters, then offsets
-  int base[kDig];            // running global digit offsets
-  int tot[kDig];             // digit totals
-  unsigned long long wsum[kW];
-  unsigned long long wpre[kW];   // exclusive prefix of the wave totals
-  double bval[kW + 1];       // per-wave results, then the block's (slot kW)
-  int bidx[kW + 1];
-  unsigned long long bsum[kW + 1];
-  unsigned long long carry;
-  unsigned long long cin;    // carry before the current chunk
-};
-
-// ---- wavefront scans through DPP ----
-// One step of a 64-lane inclusive scan: lanes read the value `CTRL` names (row
-// shifts inside each 16-lane row, then the broadcasts of lane 15 and lane 31
-// into the following rows, restricted to rows ROWS); a lane with no source, or
-// outside ROWS, reads `ident`.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_read(uint32_t v, uint32_t ident) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROWS, 0xf, false);
-}
-template <int CTRL, int ROWS>
-__device__ __forceinline__ unsigned long long dpp_read(unsigned long long v,
-                                                       unsigned long long ident) {
-  const uint32_t lo = dpp_read<CTRL, ROWS>((uint32_t)v, (uint32_t)ident);
-  const uint32_t hi = dpp_read<CTRL, ROWS>((uint32_t)(v >> 32), (uint32_t)(ident >> 32));
-  return ((unsigned long long)hi << 32) | lo;
-}
-
-// Inclusive scan of v over the wavefront under an associative op with
-// identity ident (Hillis-Steele inside rows, then two row broadcasts).  All 64
-// lanes must be active.
-template <typename T, typename Op>
-__device__ __forceinline__ T wave_iscan(T v, T ident, Op op) {
-  v = op(v, dpp_read<0x111, 0xf>(v, ident));   // row_shr:1
-  v = op(v, dpp_read<0x112, 0xf>(v, ident));   // row_shr:2
-  v = op(v, dpp_read<0x114, 0xf>(v, ident));   // row_shr:4
-  v = op(v, dpp_read<0x118, 0xf>(v, ident));   // row_shr:8
-  v = op(v, dpp_read<0x142, 0xa>(v, ident));   // row_bcast:15 into rows 1 and 3
-  v = op(v, dpp_read<0x143, 0xc>(v, ident));   // row_bcast:31 into rows 2 and 3
-  return v;
-}
-
-__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
-}
-__device__ __forceinline__ unsigned long long lane_u64(unsigned long long v, int lane) {
-  return ((unsigned long long)lane_u32((uint32_t)(v >> 32), lane) << 32) | lane_u32((uint32_t)v, lane);
-}
-
-struct AddU32 { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
-struct AddU64 {
-  __device__ unsigned long long operator()(unsigned long long a, unsigned long long b) const {
-    return a + b;
-  }
-};
-struct MaxU64 {
-  __device__ unsigned long long operator()(unsigned long long a, unsigned long long b) const {
-    return a > b ? a : b;
-  }
-};
-struct MinI32 {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
-    return (uint32_t)min((int)a, (int)b);
-  }
-};
-
-// Survivals are probabilities: a value outside [0, 1] is clamped into it and
-// NaN is taken as 0 (so the fixed-point tau sum stays below R (1 + gamma) 2^40).
-__device__ __forceinline__ float clamp_survival(float a) {
-  return a > 0.0f ? (a < 1.0f ? a : 1.0f) : 0.0f;
-}
-
-__device__ __forceinline__ uint32_t key_of(float a) {
-  // non-negative bits of the clamped value (-0 -> +0), complemented:
-  // ascending = descending a
-  return ~__float_as_uint(clamp_survival(a));
-}
-
-__device__ __forceinline__ float value_of(uint32_t ck) { return __uint_as_float(~ck); }
-
-// Exclusive scan of the 256 digit totals tot[] into base[] (wave 0 does the work).
-__device__ void scan_digits(SchedShared& sh, const int* tot) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int v[4];
-    int s = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = s;
-      s += tot[lane * 4 + j];
-    }
-    // inclusive scan of s across the wave
-    const int inc = (int)wave_iscan((uint32_t)s, 0u, AddU32{});
-    const int ex = inc - s;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sh.base[lane * 4 + j] = ex + v[j];
-  }
-}
-
-// Rank this wave's ITEMS elements by digit; rk[i] = rank among equal digits of
-// this wave in (item, lane) order.  cnt row of this wave must be zero on entry.
-template <int ITEMS>
-__device__ __forceinline__ void rank_items(SchedShared& sh, const uint32_t (&ck)[ITEMS],
-                                           const bool (&ok)[ITEMS], int shift, int (&rk)[ITEMS]) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  int* cnt = sh.cnt + w * kDig;
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int d = (ck[i] >> shift) & 0xff;
-    unsigned long long peers = __ballot(ok[i]);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (d >> b) & 1;
-      const unsigned long long bal = __ballot(ok[i] && bit);
-      peers &= bit ? bal : ~bal;
-    }
-    if (ok[i]) {
-      const int before = cnt[d];
-      rk[i] = before + __popcll(peers & lt);
-      if ((peers & lt) == 0ull) cnt[d] = before + __popcll(peers);
-    }
-  }
-}
-
-// Single tile: per digit d (threads 0..255), cnt[w][d] becomes the count of
-// digit d in waves before w, and tot[d] the digit's total.
-__device__ __forceinline__ void wave_prefix_and_totals(SchedShared& sh) {
-  if (threadIdx.x < kDig) {
-    const int d = threadIdx.x;
-    int c[kW];
-#pragma unroll
-    for (int w = 0; w < kW; ++w) c[w] = sh.cnt[w * kDig + d];
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-      sh.cnt[w * kDig + d] = run;
-      run += c[w];
-    }
-    sh.tot[d] = run;
-  }
-}
-
-__device__ __forceinline__ void zero_my_counters(SchedShared& sh) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < kDig / 64; ++j) sh.cnt[w * kDig + lane + 64 * j] = 0;
-}
-
-// Block-wide exclusive scan of one uint64 per thread; returns the exclusive
-// prefix and adds the block total to sh.carry (after the call, all threads see
-// the old carry in `carry_in`).
-__device__ __forceinline__ unsigned long long block_exscan_u64(SchedShared& sh,
-                                                               unsigned long long v,
-                                                               unsigned long long& carry_in) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const unsigned long long inc = wave_iscan(v, 0ull, AddU64{});
-  if (lane == 63) sh.wsum[w] = inc;
-  __syncthreads();
-  // Wave 0 scans the wave totals and moves the carry on.
-  if (w == 0) {
-    const unsigned long long t = lane < kW ? sh.wsum[lane] : 0ull;
-    const unsigned long long ti = wave_iscan(t, 0ull, AddU64{});
-    if (lane < kW) sh.wpre[lane] = ti - t;
-    const unsigned long long total = lane_u64(ti, 63);
-    if (lane == 0) {
-      const unsigned long long c = sh.carry;
-      sh.cin = c;
-      sh.carry = c + total;
-    }
-  }
-  __syncthreads();
-  carry_in = sh.cin;
-  return sh.wpre[w] + inc - v;
-}
-
-struct Best {
-  double theta;
-  int m;
-  unsigned long long S;   // fixed-point prefix sum at m
-};
-
-__device__ __forceinline__ void better(Best& b, const Best& o) {
-  if (o.theta > b.theta || (o.theta == b.theta && o.m < b.m)) b = o;
-}
-
-// Order-preserving 64-bit key of a double (larger value, larger key; -0 and
-// +0 share one key, as they compare equal).
-__device__ __forceinline__ unsigned long long theta_key(double x) {
-  const unsigned long long b = (unsigned long long)__double_as_longlong(x == 0.0 ? 0.0 : x);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-
-// Argmax over the wavefront: the largest Theta, then the smallest m among the
-// lanes holding it; every lane gets the winner.
-__device__ __forceinline__ Best wave_best(const Best& b) {
-  const unsigned long long key = theta_key(b.theta);
-  const unsigned long long kmax = lane_u64(wave_iscan(key, 0ull, MaxU64{}), 63);
-  const uint32_t mine = key == kmax ? (uint32_t)b.m : 0x7fffffffu;
-  const int mmin = (int)lane_u32(wave_iscan(mine, 0x7fffffffu, MinI32{}), 63);
-  const unsigned long long sel = __ballot(key == kmax && b.m == mmin);
-  const int src = (int)__builtin_ctzll(sel);
-  Best r;
-  r.theta = __longlong_as_double((long long)lane_u64((unsigned long long)__double_as_longlong(b.theta), src));
-  r.m = mmin;
-  r.S = lane_u64(b.S, src);
-  return r;
-}
-
-// Block argmax of Theta (largest Theta, smallest m); every thread gets the
-// result.  Each wave reduces its lanes, wave 0 the per-wave winners.
-__device__ __forceinline__ void block_best(SchedShared& sh, Best& best) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const Best wb = wave_best(best);
-  if (lane == 0) {
-    sh.bval[w] = wb.theta;
-    sh.bidx[w] = wb.m;
-    sh.bsum[w] = wb.S;
-  }
-  __syncthreads();
-  if (w == 0) {
-    Best e{-1.0, 0x7fffffff, 0ull};
-    if (lane < kW) e = Best{sh.bval[lane], sh.bidx[lane], sh.bsum[lane]};
-    const Best bb = wave_best(e);
-    if (lane == 0) {
-      sh.bval[kW] = bb.theta;
-      sh.bidx[kW] = bb.m;
-      sh.bsum[kW] = bb.S;
-    }
-  }
-  __syncthreads();
-  best = Best{sh.bval[kW], sh.bidx[kW], sh.bsum[kW]};
-}
-
-// Block minimum / sum (every thread gets the result; sh's per-wave slots are
-// free again on return).
-__device__ __forceinline__ int block_min_int(SchedShared& sh, int v) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  v = (int)lane_u32(wave_iscan((uint32_t)v, 0x7fffffffu, MinI32{}), 63);
-  if (lane == 0) sh.bidx[w] = v;
-  __syncthreads();
-  if (w == 0) {
-    const uint32_t t = lane < kW ? (uint32_t)sh.bidx[lane] : 0x7fffffffu;
-    const int r = (int)lane_u32(wave_iscan(t, 0x7fffffffu, MinI32{}), 63);
-    if (lane == 0) sh.bidx[kW] = r;
-  }
-  __syncthreads();
-  const int r = sh.bidx[kW];
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ unsigned long long block_sum_sh(SchedShared& sh,
-                                                           unsigned long long v) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  v = lane_u64(wave_iscan(v, 0ull, AddU64{}), 63);
-  if (lane == 0) sh.wsum[w] = v;
-  __syncthreads();
-  if (w == 0) {
-    const unsigned long long t = lane < kW ? sh.wsum[lane] : 0ull;
-    const unsigned long long r = lane_u64(wave_iscan(t, 0ull, AddU64{}), 63);
-    if (lane == 0) sh.bsum[kW] = r;
-  }
-  __syncthreads();
-  const unsigned long long r = sh.bsum[kW];
-  __syncthreads();
-  return r;
-}
-
-// Theta_m with tau from the fixed-point prefix sum S_m (the single definition
-// every mode uses).
-__device__ __forceinline__ double theta_at(int R, unsigned long long S, float sps_b) {
-  return __ull2double_rn(((unsigned long long)R << 40) + S) * kTauInv * (double)sps_b;
-}
-
-// Phase 3 + 4 for a sorted array (keys ck, ids) given in blocked chunks.
-// load(p, ck, id) fetches the element at sorted position p.
-//   mode 0 (global search): first argmax of Theta over every m;
-//   mode 1 (early stop): the first m with Theta_{m+1} <= Theta_m, each element
-//     comparing its Theta with the one before it (tau from S - q, exactly the
-//     value the previous position has); N if Theta keeps rising;
-//   mode 2 (capacity): m = m_cap.
-// Modes 1 and 2 then sum the survivals below m* (tau*) from the sorted keys.
-template <int ITEMS, typename Load, typename SetRank, typename SpsAt>
-__device__ void scan_theta(SchedShared& sh, int N, int R, const float* __restrict__ sps,
-                           float sps0, int mode, int m_cap, int32_t* __restrict__ order,
-                           Load load, SetRank set_rank, SpsAt sps_at, Best& best) {
-  const int tid = threadIdx.x;
-  if (tid == 0) sh.carry = 0ull;
-  best.theta = -1.0;
-  best.m = 0x7fffffff;
-  best.S = 0ull;
-  if (tid == 0 && mode == 0) {
-    best.theta = (double)R * (double)sps0;  // m = 0: tau = R, sps0 = sps[R - 1]
-    best.m = 0;
-  }
-  int brk = 0x7fffffff;
-  __syncthreads();
-  const unsigned long long rfx = (unsigned long long)R << 40;
-  for (int c0 = 0; c0 < N; c0 += kT * ITEMS) {
-    uint32_t ck[ITEMS];
-    int id[ITEMS];
-    unsigned long long q[ITEMS];
-    unsigned long long tsum = 0;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int p = c0 + tid * ITEMS + i;
-      if (p < N) {
-        load(p, ck[i], id[i]);
-        q[i] = __double2ull_rn((double)value_of(ck[i]) * kTauScale);
-      } else {
-        ck[i] = 0xffffffffu;
-        id[i] = -1;
-        q[i] = 0ull;
-      }
-      tsum += q[i];
-    }
-    unsigned long long carry_in;
-    const unsigned long long ex = block_exscan_u64(sh, tsum, carry_in);
-    unsigned long long S = carry_in + ex;
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int p = c0 + tid * ITEMS + i;
-      if (p < N) {
-        S += q[i];
-        if (mode == 0) {
-          const double tau = __ull2double_rn(rfx + S) * kTauInv;
-          const double th = tau * (double)sps_at(p, i);   // sps[R + p]: budget B = R + p + 1
-          if (th > best.theta) {
-            best.theta = th;
-            best.m = p + 1;
-            best.S = S;
-          }
-        } else if (mode == 1) {
-          const double th = theta_at(R, S, sps_at(p, i));
-          const double th_prev = theta_at(R, S - q[i], sps[R + p - 1]);
-          if (!(th > th_prev)) brk = min(brk, p);
-        }
-        if (order) order[p] = id[i];
-      }
-    }
-    __syncthreads();   // every element of this chunk is read before ranks overwrite storage
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int p = c0 + tid * ITEMS + i;
-      if (p < N) set_rank(id[i], p);
-    }
-    __syncthreads();
-  }
-  if (mode == 0) {
-    block_best(sh, best);
-    return;
-  }
-  int m_star = m_cap;
-  if (mode == 1) {
-    m_star = block_min_int(sh, brk);
-    if (m_star > N) m_star = N;
-  }
-  unsigned long long part = 0;
-  for (int p = tid; p < m_star; p += kT) {
-    uint32_t k;
-    int i;
-    load(p, k, i);
-    part += __double2ull_rn((double)value_of(k) * kTauScale);
-  }
-  const unsigned long long Sm = block_sum_sh(sh, part);
-  best.m = m_star;
-  best.S = Sm;
-  best.theta = theta_at(R, Sm, mode == 1 ? sps[R + m_star - 1] : 1.0f);
-}
-
-__device__ void write_results(int R, int gamma, const Best& best, const int* rank,
-                              int32_t* __restrict__ lengths, dspark_schedule_info* info) {
-  const int m_star = best.m;
-  for (int r = threadIdx.x; r < R; r += kT) {
-    int l = 0;
-    for (int j = 0; j < gamma; ++j) l += rank[r * gamma + j] < m_star ? 1 : 0;
-    lengths[r] = l;
-  }
-  if (info && threadIdx.x == 0) {
-    const unsigned long long tau_fx = ((unsigned long long)R << 40) + best.S;
-    info->B_star = R + m_star;
-    info->m_star = m_star;
-    info->tau_fx = tau_fx;
-    info->tau = __ull2double_rn(tau_fx) * kTauInv;
-    info->theta = best.theta;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Single-tile path: N <= kT * ITEMS, everything in LDS.
-// ---------------------------------------------------------------------------
-// Inputs of the fused draft step's finishing launch: the last step's packed
-// words and the two parts of every confidence logit.
-struct FinishArgs {
-  const unsigned long long* words;   // last step's packed words [R][S]
-  int S;
-  int V;
-  const float* sh;                   // w_h . h, [R * gamma]
-  const float* se;                   // w_e . W1[x_{k-1}] in two K halves, [R * gamma][2]
-  const float* sts;                  // [gamma] or NULL
-  int32_t* tokens;                   // [R][gamma]: column gamma - 1 is written here
-  float* conf;                       // [R][gamma]
-  float* surv;                       // [R][gamma]
-};
-
-// Confidence, STS and survival of request m ([P1] section 二 design 2):
-// c_{m,k} = sigmoid((sh + (se_0 + se_1)) / T_k), a_{m,k} = a_{m,k-1} c_{m,k} in
-// fp32; also the last token.  The survivals go to `sv` (by candidate id) too.
-// The loads of up to kFinBatch positions are issued before any of them is
-// used, so a request costs one memory round trip per kFinBatch positions.
-constexpr int kFinBatch = 8;
-
-__device__ __forceinline__ void finish_request(const FinishArgs& fa, int m, int gamma,
-                                               float* __restrict__ sv) {
-  const int32_t last = read_token(fa.words, m, fa.S, fa.V);
-  float a = 1.0f;
-  for (int k0 = 0; k0 < gamma; k0 += kFinBatch) {
-    float s[kFinBatch], t[kFinBatch];
-#pragma unroll
-    for (int j = 0; j < kFinBatch; ++j) {
-      const int k = k0 + j;
-      s[j] = 0.0f;
-      t[j] = 1.0f;
-      if (k < gamma) {
-        const size_t e = (size_t)m * gamma + k;
-        s[j] = fa.sh[e] + (fa.se[2 * e] + fa.se[2 * e + 1]);
-        if (fa.sts) t[j] = fa.sts[k];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kFinBatch; ++j) {
-      const int k = k0 + j;
-      if (k < gamma) {
-        const size_t e = (size_t)m * gamma + k;
-        const float c = 1.0f / (1.0f + expf(-(s[j] / t[j])));
-        fa.conf[e] = c;
-        a = k == 0 ? c : a * c;
-        fa.surv[e] = a;
-        if (sv) sv[e] = a;
-      }
-    }
-  }
-  fa.tokens[(size_t)m * gamma + gamma - 1] = last;
-}
-
-template <int ITEMS, bool FUSED>
+template <int ITEMS, int FIN>
 __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restrict__ surv,
                                                           const float* __restrict__ sps, int R,
                                                           int gamma, int N, int mode,
@@ -499,84 +39,8 @@ __global__ __launch_bounds__(kT) void schedule_lds_kernel(const float* __restric
                                                           dspark_schedule_info* info,
                                                           FinishArgs fa) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  SchedShared& sh = *reinterpret_cast<SchedShared*>(smem_raw);
-  uint32_t* skey = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SchedShared));
-  int* sid = reinterpret_cast<int*>(skey + kT * ITEMS);
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  // Fused draft step: the survivals are made here first (one thread per
-  // request), into the key area of LDS.
-  const float* sv = surv;
-  if constexpr (FUSED) {
-    float* svl = reinterpret_cast<float*>(skey);
-    for (int m = threadIdx.x; m < R; m += kT) finish_request(fa, m, gamma, svl);
-    __syncthreads();
-    sv = svl;
-  }
-  // striped arrangement: wave w owns [w*64*ITEMS, (w+1)*64*ITEMS), item-major inside
-  uint32_t ck[ITEMS];
-  int id[ITEMS];
-  bool ok[ITEMS];
-  int rk[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int e = w * 64 * ITEMS + i * 64 + lane;
-    ok[i] = e < N;
-    ck[i] = ok[i] ? key_of(sv[e]) : 0xffffffffu;
-    id[i] = e;
-  }
-  if constexpr (FUSED) __syncthreads();   // the keys are read before the sort reuses the area
-  // The SPS entries of this thread's sorted positions, fetched now so that the
-  // latency hides behind the sort.
-  float spv[ITEMS];
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int p = threadIdx.x * ITEMS + i;
-    spv[i] = (p < N && mode != 2) ? sps[R + p] : 0.0f;
-  }
-  const float sps0 = (mode == 0 && threadIdx.x == 0) ? sps[R - 1] : 0.0f;
-  // Per pass four barriers: after the ranking, after the per-digit wave
-  // prefixes, after the digit scan, after the scatter.  The reload of the next
-  // pass's keys needs none after it: every wave's next scatter waits behind
-  // that pass's first barrier, and each wave only touches its own counter row
-  // between barriers.
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 8 * pass;
-    zero_my_counters(sh);
-    rank_items<ITEMS>(sh, ck, ok, shift, rk);
-    __syncthreads();
-    wave_prefix_and_totals(sh);
-    __syncthreads();
-    scan_digits(sh, sh.tot);   // base[d]: items with a smaller digit
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      if (ok[i]) {
-        const int d = (ck[i] >> shift) & 0xff;
-        const int dst = sh.base[d] + sh.cnt[w * kDig + d] + rk[i];
-        skey[dst] = ck[i];
-        sid[dst] = id[i];
-      }
-    }
-    __syncthreads();
-    if (pass < 3) {
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        const int e = w * 64 * ITEMS + i * 64 + lane;
-        if (ok[i]) {
-          ck[i] = skey[e];
-          id[i] = sid[e];
-        }
-      }
-    }
-  }
-  Best best;
-  scan_theta<ITEMS>(
-      sh, N, R, sps, sps0, mode, m_cap, order,
-      [&](int p, uint32_t& k, int& i) { k = skey[p]; i = sid[p]; },
-      [&](int i, int p) { sid[i] = p; }, [&](int, int i) { return spv[i]; }, best);
-  write_results(R, gamma, best, sid, lengths, info);
+  schedule_lds_body<ITEMS, FIN, kW>(smem_raw, surv, sps, R, gamma, N, mode, m_cap, lengths, order,
+                                    info, fa);
 }
 
 // ---------------------------------------------------------------------------
@@ -1072,26 +536,26 @@ __global__ __launch_bounds__(256) void sched_finish_kernel(
 // Fused draft step beyond the LDS path: the survivals go to memory first.
 __global__ __launch_bounds__(256) void finish_kernel(FinishArgs fa, int R, int gamma) {
   const int m = blockIdx.x * 256 + threadIdx.x;
-  if (m < R) finish_request(fa, m, gamma, nullptr);
+  if (m < R) finish_request<kFinAfter>(fa, m, gamma, nullptr, nullptr);
 }
 
-template <int ITEMS, bool FUSED>
+template <int ITEMS, int FIN>
 dspark_status launch_lds(const float* surv, const float* sps, int R, int gamma, int N, int mode,
                          int m_cap, int32_t* lengths, int32_t* order, dspark_schedule_info* info,
                          const FinishArgs& fa, hipStream_t stream) {
-  const size_t lds = sizeof(SchedShared) + (size_t)kT * ITEMS * 8;
+  const size_t lds = sched_lds_bytes<ITEMS, kW>();
   // The dynamic-LDS attribute, set once per device (bit d of `done`).
   static std::atomic<unsigned long long> done{0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(DSPARK_EDEVICE, "hipGetDevice failed");
   const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
   if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_lds_kernel<ITEMS, FUSED>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_lds_kernel<ITEMS, FIN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for the schedule kernel");
     done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((schedule_lds_kernel<ITEMS, FUSED>), dim3(1), dim3(kT), lds, stream, surv,
+  hipLaunchKernelGGL((schedule_lds_kernel<ITEMS, FIN>), dim3(1), dim3(kT), lds, stream, surv,
                      sps, R, gamma, N, mode, m_cap, lengths, order, info, fa);
   return check_launch("schedule_lds_kernel");
 }
@@ -1112,6 +576,15 @@ size_t schedule_workspace_bytes(int R, int gamma) {
          ntiles * (sizeof(unsigned long long) + sizeof(TileBest)) + 256;
 }
 
+// Launches of launch_schedule: one in LDS, else per pass a histogram and a
+// scatter (and a digit scan beyond kInlineTiles tiles), then three.
+int schedule_launch_count(int R, int gamma) {
+  const long N = (long)R * gamma;
+  if (N <= kLdsMaxN) return 1;
+  const long ntiles = (N + kGTile - 1) / kGTile;
+  return 4 * (ntiles <= kInlineTiles ? 2 : 3) + 3;
+}
+
 template <bool FIRST, bool INLINE>
 void launch_scatter(int ntiles, hipStream_t stream, const float* surv, const uint32_t* sk,
                     const int* si, uint32_t* dk, int* di, int N, int shift, const int* hist) {
@@ -1124,7 +597,7 @@ dspark_status launch_schedule(const float* surv, const float* sps, int R, int ga
                               dspark_schedule_info* info, void* workspace, hipStream_t stream) {
   const int N = R * gamma;
 #define DSPARK_LDS(I) \
-  launch_lds<I, false>(surv, sps, R, gamma, N, mode, m_cap, lengths, order, info, FinishArgs{}, stream)
+  launch_lds<I, kFinNone>(surv, sps, R, gamma, N, mode, m_cap, lengths, order, info, FinishArgs{}, stream)
   if (N <= kT * 1) return DSPARK_LDS(1);
   if (N <= kT * 2) return DSPARK_LDS(2);
   if (N <= kT * 4) return DSPARK_LDS(4);
@@ -1190,10 +663,10 @@ dspark_status launch_draft_finish(const unsigned long long* words_last, int S, i
                                   dspark_schedule_info* info, void* sched_ws, hipStream_t stream) {
   const FinishArgs fa{words_last, S, V, sh, se, sts_temp, tokens, conf, surv};
   const int N = R * gamma;
-  if (N <= kT * 1) return launch_lds<1, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
-  if (N <= kT * 2) return launch_lds<2, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
-  if (N <= kT * 4) return launch_lds<4, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
-  if (N <= kT * 8) return launch_lds<8, true>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  if (N <= kT * 1) return launch_lds<1, kFinAfter>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  if (N <= kT * 2) return launch_lds<2, kFinAfter>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  if (N <= kT * 4) return launch_lds<4, kFinAfter>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
+  if (N <= kT * 8) return launch_lds<8, kFinAfter>(nullptr, sps, R, gamma, N, 0, 0, lengths, order, info, fa, stream);
   hipLaunchKernelGGL(finish_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, fa, R, gamma);
   const dspark_status st = check_launch("finish_kernel");
   if (st != DSPARK_OK) return st;

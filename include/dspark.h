@@ -337,19 +337,35 @@ dspark_status dspark_schedule_ex(const float* surv, const float* sps, int R, int
 size_t dspark_draft_step_workspace(int R, int gamma, int V, int r);
 
 /*
+ * Number of kernel launches one dspark_draft_step call makes for these sizes,
+ * layout, mode and temperature, with W1 and w_conf + d 16-byte aligned (a
+ * misaligned one can add the separate finishing launch).  Host-side planning
+ * only (it reads the current device's properties); nothing is launched.
+ * Errors: EINVAL for NULL count, bad sizes, unknown layout or mode, or a
+ * non-positive sampling temperature.
+ */
+dspark_status dspark_draft_step_launches(int R, int gamma, int V, int r, int layout, int mode,
+                                         float temperature, int* count);
+
+/*
  * One whole drafting step of the head in one call: the gamma-step Markov-head
  * draft ([P1] section 二 design 1, as dspark_markov_draft), the confidence head
  * with STS and the prefix survivals ([P1] section 二 design 2, as
  * dspark_confidence), and the global-search schedule ([P1] section 二 design 2
  * and section 三 challenge 2, as dspark_schedule).  The results are those of
  * the three calls in sequence (up to the rounding order of the confidence
- * dot products).  It runs as gamma + 2 launches: a prologue that clears the
- * draft's packed words and computes the token-independent part w_h . h of
- * every confidence logit, the gamma step kernels (whose first V group also
- * computes w_e . W1[x_{k-1}] from the rows it gathered), and one launch that
- * unpacks the last tokens, applies the sigmoid with STS, takes the survival
- * products and schedules (up to 8192 candidates; beyond that the schedule's
- * global path follows it).
+ * dot products).  It runs as a prologue that clears the draft's packed words
+ * and computes the token-independent part w_h . h of every confidence logit,
+ * then the gamma step kernels (whose first V group also computes
+ * w_e . W1[x_{k-1}] from the rows it gathered), then the finishing work: the
+ * sigmoid with STS, the survival products and the schedule.  That work needs
+ * x_0 .. x_{gamma-2} only; where the last step's launch has a workgroup with
+ * no step work (the rank-512 sampling kernel, whose V groups rarely fill the
+ * launch), that workgroup does it beside the step, and the step workgroup
+ * that finishes last unpacks the last tokens: gamma + 1 launches.  Otherwise
+ * it is one launch after the last step (up to 8192 candidates; beyond that the
+ * schedule's global path follows it): gamma + 2 or more.
+ * dspark_draft_step_launches gives the count for given sizes.
  *   W1 ... uniforms   as for dspark_markov_draft (no bias output).
  *   h, w_conf, sts_temp, d   as for dspark_confidence; w_conf must be 16-byte
  *                            aligned and d a multiple of 4.

@@ -46,6 +46,20 @@ def test_status_strings():
     assert L.dspark_status_string(99) == b"unknown status"
 
 
+@no_gpu
+@pytest.mark.parametrize("args,want", [
+    ((0, 5, 4096, 64, 0, GREEDY, 1.0), EINVAL), ((4, 5, 1, 64, 0, GREEDY, 1.0), EINVAL),
+    ((4, 5, 4096, 513, 0, GREEDY, 1.0), EINVAL), ((4, 5, 4096, 64, 7, GREEDY, 1.0), EINVAL),
+    ((4, 5, 4096, 64, 0, 3, 1.0), EINVAL), ((4, 5, 4096, 64, 0, SAMPLE, 0.0), EINVAL),
+])
+def test_draft_step_launches_rejects(args, want):
+    L = D.lib()
+    n = ctypes.c_int(-1)
+    assert L.dspark_draft_step_launches(*args, ctypes.byref(n)) == want
+    assert L.dspark_draft_step_launches(4, 5, 4096, 64, 0, GREEDY, 1.0, None) == EINVAL
+    assert n.value == -1
+
+
 def test_workspace_queries():
     assert D.dspark_markov_draft_workspace(0, 5, 100, 64) == 0
     assert D.dspark_markov_draft_workspace(4, 5, 1, 64) == 0
@@ -299,11 +313,15 @@ def test_scratch_check_recognises_counted_wait_kernels():
            "x.hip:1:1: remark: Function Name: _ZN6dspark12_GLOBAL__N_118markov_step_kernelILi256ELi8ELi1ELi2ELb0ELi1EEEvPKt [-Rpass-analysis=kernel-resource-usage]\n"
            "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 32 [-Rpass-analysis=kernel-resource-usage]\n"
            "x.hip:1:1: remark: Function Name: _ZN6dspark12_GLOBAL__N_118markov_step_kernelILi512ELi4ELi0ELi2ELb0ELi1EEEvPKt [-Rpass-analysis=kernel-resource-usage]\n"
-           "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass-analysis=kernel-resource-usage]\n")
+           "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark: Function Name: _ZN6dspark12_GLOBAL__N_129markov_step_ksplit_fin_kernelILi4ELi1ELi2EEEvPKt [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 4 [-Rpass-analysis=kernel-resource-usage]\n")
     bad = B.scratch_offenders(rem)
-    # the K-split and the rank-512 plain kernel without bias output count their
-    # waits; the bias-output (Lb1E) and register-staged rank-256 ones do not
-    assert len(bad) == 2 and "ksplit" in bad[0] and "ILi512ELi4E" in bad[1]
+    # the K-split (also the fused step's last-step one) and the rank-512 plain
+    # kernel without bias output count their waits; the bias-output (Lb1E) and
+    # register-staged rank-256 ones do not
+    assert len(bad) == 3 and "ksplit" in bad[0] and "ILi512ELi4E" in bad[1]
+    assert "ksplit_fin" in bad[2]
 
 
 def _step(**kw):

@@ -89,6 +89,71 @@ def test_draft_step_matches_oracle(name, R, g, V, r, d, mode, layout):
     _check_fused(make_workload(cfg), layout, None if R <= 300 else _tile_rows(R, 1, R))
 
 
+# Rank-512 sampling runs on the K-split kernel, whose last step does the
+# finishing work on a workgroup without step work when it has one and
+# R gamma <= 4 x its threads (gamma + 1 launches); else a launch follows the
+# last step (gamma + 2).  launches: the count the library reports for the
+# row-major layout on MI355X.
+FIN_CASES = [
+    # name, R, gamma, V, r, d, launches
+    ("fin_g1", 64, 1, 5000, 512, 64, 2),         # x_{-1} is the anchor
+    ("fin_two_blocks", 70, 3, 3000, 384, 48, 4),  # R block 0 of two
+    ("fin_at_limit", 100, 20, 4000, 512, 32, 21),  # 2000 candidates, 512 threads x 4
+    ("fin_past_limit", 100, 21, 4000, 512, 32, 23),  # 2100: the launch after the last step
+    ("fin_one_wave", 20, 6, 2600, 512, 16, 7),    # 128 threads
+]
+
+
+@pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
+@pytest.mark.parametrize("name,R,g,V,r,d,launches", FIN_CASES)
+def test_draft_step_finishing_in_last_step(name, R, g, V, r, d, launches, layout):
+    _say(f"case draft_step {name} R={R} g={g} V={V} r={r} layout={layout}")
+    if layout == D.LAYOUT_RGV:
+        assert D.dspark_draft_step_launches(R, g, V, r, layout, SAMPLE, 0.8) == launches
+    cfg = Config("fin", R=R, gamma=g, V=V, r=r, d=d, mode=SAMPLE, temperature=0.8, w_std=0.2,
+                 base_std=1.0, wconf_std=0.1, sts=tuple(1.0 + 0.05 * k for k in range(g)),
+                 seed=500 + R + g)
+    _check_fused(make_workload(cfg), layout)
+
+
+def test_draft_step_launch_counts():
+    # The DeepSeek-V4 shape: the last step's spare workgroup (127 V groups in a
+    # launch of 128) does the finishing work; the tiled layout's strided groups
+    # fill the launch, and rank 256 greedy runs the plain kernel.
+    dsv4 = (256, 5, 129280, 512)
+    assert D.dspark_draft_step_launches(*dsv4, D.LAYOUT_RGV, SAMPLE, 1.0) == 6
+    assert D.dspark_draft_step_launches(*dsv4, D.LAYOUT_TILED, SAMPLE, 1.0) == 7
+    assert D.dspark_draft_step_launches(64, 5, 151936, 256, D.LAYOUT_RGV, GREEDY, 1.0) == 7
+    # 16384 candidates: a finishing launch, then the schedule's global path
+    # (four passes of histogram + scatter, then three).
+    assert D.dspark_draft_step_launches(1024, 16, 129280, 256, D.LAYOUT_RGV, GREEDY, 1.0) == 29
+
+
+def test_draft_step_finishing_in_last_step_bad_anchors():
+    # Bad anchors on the in-step path: -1 tokens, NaN confidences (also at the
+    # last position, whose embedding term the finishing workgroup computes
+    # itself), survivals taken as 0 by the schedule.
+    _say("case draft_step finishing in last step, bad anchors")
+    cfg = Config("edge", R=70, gamma=3, V=3000, r=512, d=32, mode=SAMPLE, temperature=1.1,
+                 w_std=0.2, base_std=1.0, wconf_std=0.1, seed=77)
+    wl = make_workload(cfg)
+    assert D.dspark_draft_step_launches(70, 3, 3000, 512, D.LAYOUT_RGV, SAMPLE, 1.1) == 4
+    bad = np.array([0, 5, 33, 69])
+    anchors = wl["anchors"].copy()
+    anchors[bad] = np.array([-1, 3000, 1 << 30, -(1 << 31)], np.int32)
+    g = H.to_device(wl, DEV)
+    tok, conf, surv, lengths, order, info = D.dspark_draft_step(
+        g["W1"], g["W2"], g["base"], torch.from_numpy(anchors).to(DEV), g["h"], g["w_conf"],
+        g["sps"], SAMPLE, 1.1, g["uniforms"], want_order=True, want_info=True)
+    torch.cuda.synchronize()
+    t, c, s = tok.cpu().numpy(), conf.cpu().numpy(), surv.cpu().numpy()
+    assert np.all(t[bad] == -1) and np.all(np.isnan(c[bad])) and np.all(np.isnan(s[bad]))
+    keep = np.setdiff1d(np.arange(70), bad)
+    assert not np.isnan(c[keep]).any()
+    H.check_schedule(s, wl["sps"], lengths.cpu().numpy(), order.cpu().numpy(), D.schedule_info(info))
+    assert np.all(lengths.cpu().numpy()[bad] == 0)
+
+
 @pytest.mark.parametrize("layout", [D.LAYOUT_RGV, D.LAYOUT_TILED])
 def test_draft_step_qwen3_8b_full(layout):
     _say(f"case draft_step qwen3_8b layout={layout}")
