@@ -159,21 +159,38 @@ __global__ __launch_bounds__(kRowT) void verify_argmax_kernel(const float* __res
     // thread before any is used (one per thread leaves the memory system
     // underfed).  take() is a lexicographic max, so the order of the elements
     // does not matter.
+    // The next batch's loads are issued before this batch is compared, so a
+    // thread's loads never drain between batches.
     const v4f* z4 = reinterpret_cast<const v4f*>(z);
     const int n4 = V >> 2;
     int p = t;
-    for (; p + (kRowU - 1) * kRowT < n4; p += kRowU * kRowT) {
+    constexpr int kStep = kRowU * kRowT;
+    if (p + (kRowU - 1) * kRowT < n4) {
       v4f q[kRowU];
 #pragma unroll
       for (int u = 0; u < kRowU; ++u) q[u] = __builtin_nontemporal_load(z4 + p + u * kRowT);
-      __builtin_amdgcn_sched_barrier(0);   // all loads issued before the first compare
+      for (;;) {
+        const int pn = p + kStep;
+        const bool more = pn + (kRowU - 1) * kRowT < n4;
+        v4f qn[kRowU];
+        // past the last whole batch the next loads re-read this batch (in
+        // bounds) and are not used
+        const int pl = more ? pn : p;
 #pragma unroll
-      for (int u = 0; u < kRowU; ++u) {
-        const int e = 4 * (p + u * kRowT);
-        take(bv, bi, q[u].x, e);
-        take(bv, bi, q[u].y, e + 1);
-        take(bv, bi, q[u].z, e + 2);
-        take(bv, bi, q[u].w, e + 3);
+        for (int u = 0; u < kRowU; ++u) qn[u] = __builtin_nontemporal_load(z4 + pl + u * kRowT);
+        __builtin_amdgcn_sched_barrier(0);   // next loads issued before the compares
+#pragma unroll
+        for (int u = 0; u < kRowU; ++u) {
+          const int e = 4 * (p + u * kRowT);
+          take(bv, bi, q[u].x, e);
+          take(bv, bi, q[u].y, e + 1);
+          take(bv, bi, q[u].z, e + 2);
+          take(bv, bi, q[u].w, e + 3);
+        }
+        p = pn;
+        if (!more) break;
+#pragma unroll
+        for (int u = 0; u < kRowU; ++u) q[u] = qn[u];
       }
     }
     for (; p < n4; p += kRowT) {
