@@ -616,8 +616,9 @@ def main():
                 "greedy_frac_of_hbm": round(b_greedy / (us_greedy / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
                 "accept_prob_us": round(us_acc, 1),
                 "accept_prob_frac_of_hbm": round(b_acc / (us_acc / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
-                "note": "fractions use one read of the logits (the accept-prob kernel reads "
-                        "each row pair twice: max/sum, then the min-sum)"}
+                "note": "fractions use one read of the logits (the accept-prob kernel keeps "
+                        "about half of each row pair on chip between its max/sum and min-sum "
+                        "passes and reads the rest twice)"}
 
     def confidence_side(calls=50):
         """dspark_confidence (with survival) on the default workload's tokens, timed

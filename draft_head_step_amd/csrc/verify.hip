@@ -14,10 +14,16 @@
 //                  (16-byte loads, per-thread running max in increasing v,
 //                  smallest id on ties), then one thread per request walks
 //                  its drafts against those argmaxes;
-//   accept_prob:   one 1024-thread workgroup per row pair, two passes over V
-//                  in base 2: online (max, sum of 2^x) of both rows, four
-//                  values per rescale, then sum_v min(p, q).
-//                  Reductions use a fixed tree, so results are deterministic.
+//   accept_prob:   one workgroup per row pair, two passes over V in base 2:
+//                  online (max, sum of 2^x) of both rows, four values per
+//                  rescale, then sum_v min(p, q).  With aligned rows (V a
+//                  multiple of 4) 512 threads keep the first part of the pair
+//                  in registers and LDS between the passes (about half of it
+//                  at the DeepSeek-V4 vocabulary), so the second pass reads
+//                  only the rest from memory; else 1024 threads read both rows
+//                  twice.  Reductions use a fixed tree, so results are
+//                  deterministic.
+#include <atomic>
 #include <math.h>
 
 #include "dspark_internal.h"
@@ -280,6 +286,168 @@ __device__ __forceinline__ MaxSum block_ms(MaxSum v, MaxSum* sh) {
   return r;
 }
 
+// Holding variant for 16-byte aligned rows: 512 threads (one workgroup per
+// CU), and each thread keeps its first kAccReg iterations of both rows in
+// registers and the next kAccLds in LDS between the two passes, so the second
+// pass re-reads only the rest of the row pair.
+constexpr int kAccRT = 512;
+constexpr int kAccRW = kAccRT / 64;
+constexpr int kAccReg = 24;   // iterations per thread held in registers
+constexpr int kAccLds = 8;    // iterations per thread held in LDS
+constexpr int kAccRU = 4;     // streamed iterations whose loads are in flight together
+static_assert(kAccLds % kAccRU == 0, "the LDS-held iterations go in whole batches");
+constexpr size_t kAccLdsBytes = (size_t)kAccLds * 2 * kAccRT * sizeof(v4f);
+
+template <int NW>
+__device__ __forceinline__ MaxSum block_ms_w(MaxSum v, MaxSum* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    MaxSum o{__shfl_xor(v.m, off), __shfl_xor(v.s, off)};
+    v = merge_ms(v, o);
+  }
+  const int t = threadIdx.x;
+  if ((t & 63) == 0) sh[t >> 6] = v;
+  __syncthreads();
+  MaxSum r = sh[0];
+#pragma unroll
+  for (int j = 1; j < NW; ++j) r = merge_ms(r, sh[j]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kAccRT) void accept_prob_hold_kernel(const float* __restrict__ zd,
+                                                                 const float* __restrict__ zt,
+                                                                 int V, float k2,
+                                                                 float* __restrict__ out) {
+  __shared__ MaxSum shd[kAccRW];
+  __shared__ MaxSum sht[kAccRW];
+  __shared__ float ssum[kAccRW];
+  extern __shared__ v4f held[];   // [kAccLds][2][kAccRT]: a thread's own slots only
+  const int t = threadIdx.x;
+  const int row = blockIdx.x;
+  const v4f* a4 = reinterpret_cast<const v4f*>(zd + (size_t)row * V);
+  const v4f* b4 = reinterpret_cast<const v4f*>(zt + (size_t)row * V);
+  const int V4 = V >> 2;
+  const v4f ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  // The held part: entry t + u * kAccRT of each row for u < kAccReg (past the
+  // row: entry 0 read and replaced by -inf, which adds nothing to either pass).
+  v4f xr[kAccReg], yr[kAccReg];
+#pragma unroll
+  for (int u = 0; u < kAccReg; ++u) {
+    const int p = t + u * kAccRT;
+    const int pc = p < V4 ? p : 0;
+    xr[u] = a4[pc];
+    yr[u] = b4[pc];
+  }
+#pragma unroll
+  for (int u = 0; u < kAccReg; ++u) {
+    const bool in = t + u * kAccRT < V4;
+    xr[u] = in ? xr[u] : ninf;
+    yr[u] = in ? yr[u] : ninf;
+  }
+  MaxSum md{-INFINITY, 0.0f}, mt{-INFINITY, 0.0f};
+#pragma unroll
+  for (int u = 0; u < kAccReg; ++u) {
+    add4(md, xr[u].x * k2, xr[u].y * k2, xr[u].z * k2, xr[u].w * k2);
+    add4(mt, yr[u].x * k2, yr[u].y * k2, yr[u].z * k2, yr[u].w * k2);
+  }
+  // The LDS-held part: batches of kAccRU iterations, kept after their use.
+#pragma unroll
+  for (int u0 = kAccReg; u0 < kAccReg + kAccLds; u0 += kAccRU) {
+    v4f x[kAccRU], y[kAccRU];
+#pragma unroll
+    for (int u = 0; u < kAccRU; ++u) {
+      const int p = t + (u0 + u) * kAccRT;
+      const int pc = p < V4 ? p : 0;
+      x[u] = a4[pc];
+      y[u] = b4[pc];
+    }
+#pragma unroll
+    for (int u = 0; u < kAccRU; ++u) {
+      const bool in = t + (u0 + u) * kAccRT < V4;
+      x[u] = in ? x[u] : ninf;
+      y[u] = in ? y[u] : ninf;
+      add4(md, x[u].x * k2, x[u].y * k2, x[u].z * k2, x[u].w * k2);
+      add4(mt, y[u].x * k2, y[u].y * k2, y[u].z * k2, y[u].w * k2);
+      held[((u0 - kAccReg + u) * 2) * kAccRT + t] = x[u];
+      held[((u0 - kAccReg + u) * 2 + 1) * kAccRT + t] = y[u];
+    }
+  }
+  // The streamed rest, read twice (kept in the caches after the first read).
+  const int p0 = t + (kAccReg + kAccLds) * kAccRT;
+  {
+    int p = p0;
+    for (; p + (kAccRU - 1) * kAccRT < V4; p += kAccRU * kAccRT) {
+      v4f x[kAccRU], y[kAccRU];
+#pragma unroll
+      for (int u = 0; u < kAccRU; ++u) {
+        x[u] = a4[p + u * kAccRT];
+        y[u] = b4[p + u * kAccRT];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kAccRU; ++u) {
+        add4(md, x[u].x * k2, x[u].y * k2, x[u].z * k2, x[u].w * k2);
+        add4(mt, y[u].x * k2, y[u].y * k2, y[u].z * k2, y[u].w * k2);
+      }
+    }
+    for (; p < V4; p += kAccRT) {
+      const v4f x = a4[p];
+      const v4f y = b4[p];
+      add4(md, x.x * k2, x.y * k2, x.z * k2, x.w * k2);
+      add4(mt, y.x * k2, y.y * k2, y.z * k2, y.w * k2);
+    }
+  }
+  md = block_ms_w<kAccRW>(md, shd);
+  mt = block_ms_w<kAccRW>(mt, sht);
+  const float Ld = md.m + __log2f(md.s);
+  const float Lt = mt.m + __log2f(mt.s);
+  auto term = [&](float x, float y) {
+    return fminf(exp2_(fmaf(x, k2, -Ld)), exp2_(fmaf(y, k2, -Lt)));
+  };
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kAccReg; ++u)
+    acc += (term(xr[u].x, yr[u].x) + term(xr[u].y, yr[u].y)) +
+           (term(xr[u].z, yr[u].z) + term(xr[u].w, yr[u].w));
+#pragma unroll
+  for (int u = 0; u < kAccLds; ++u) {
+    const v4f x = held[(u * 2) * kAccRT + t];
+    const v4f y = held[(u * 2 + 1) * kAccRT + t];
+    acc += (term(x.x, y.x) + term(x.y, y.y)) + (term(x.z, y.z) + term(x.w, y.w));
+  }
+  {
+    int p = p0;
+    for (; p + (kAccRU - 1) * kAccRT < V4; p += kAccRU * kAccRT) {
+      v4f x[kAccRU], y[kAccRU];
+#pragma unroll
+      for (int u = 0; u < kAccRU; ++u) {
+        x[u] = __builtin_nontemporal_load(a4 + p + u * kAccRT);
+        y[u] = __builtin_nontemporal_load(b4 + p + u * kAccRT);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kAccRU; ++u)
+        acc += (term(x[u].x, y[u].x) + term(x[u].y, y[u].y)) +
+               (term(x[u].z, y[u].z) + term(x[u].w, y[u].w));
+    }
+    for (; p < V4; p += kAccRT) {
+      const v4f x = __builtin_nontemporal_load(a4 + p);
+      const v4f y = __builtin_nontemporal_load(b4 + p);
+      acc += (term(x.x, y.x) + term(x.y, y.y)) + (term(x.z, y.z) + term(x.w, y.w));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((t & 63) == 0) ssum[t >> 6] = acc;
+  __syncthreads();
+  if (t == 0) {
+    float s = 0.0f;
+    for (int j = 0; j < kAccRW; ++j) s += ssum[j];
+    out[row] = s;
+  }
+}
+
 __global__ __launch_bounds__(kAccT) void accept_prob_kernel(const float* __restrict__ zd,
                                                             const float* __restrict__ zt, int V,
                                                             float k2, int vec,
@@ -411,10 +579,29 @@ dspark_status launch_accept_prob(const float* draft_logits, const float* target_
                                  int V, float temperature, float* out, hipStream_t stream) {
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; };
   const int vec = (V % 4 == 0) && a16(draft_logits) && a16(target_logits);
-  // One 1024-thread workgroup per row pair.  (Measured: capping the grid so
-  // that workgroups loop over rows, or limiting workgroups per CU, was slower
-  // or no faster.)
+  // One workgroup per row pair: aligned rows of a multiple of four entries
+  // take the holding variant (about half of each row pair stays on chip
+  // between the passes); others the 1024-thread kernel, which reads both rows
+  // twice.  (Measured on the latter: capping the grid so that workgroups loop
+  // over rows, or limiting workgroups per CU, was slower or no faster.)
   const float k2 = 1.44269504088896341f / temperature;   // log2(e) / T
+  if (vec) {
+    // The dynamic-LDS attribute, set once per device (bit d of `done`).
+    static std::atomic<unsigned long long> done{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(DSPARK_EDEVICE, "hipGetDevice failed");
+    const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+    if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&accept_prob_hold_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kAccLdsBytes) != hipSuccess)
+        return fail(DSPARK_EDEVICE, "hipFuncSetAttribute failed for accept_prob_hold_kernel");
+      done.fetch_or(bit, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(accept_prob_hold_kernel, dim3(n), dim3(kAccRT), kAccLdsBytes, stream,
+                       draft_logits, target_logits, V, k2, out);
+    return check_launch("accept_prob_hold_kernel");
+  }
   hipLaunchKernelGGL(accept_prob_kernel, dim3(n), dim3(kAccT), 0, stream, draft_logits,
                      target_logits, V, k2, vec, out);
   return check_launch("accept_prob_kernel");

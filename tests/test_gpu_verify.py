@@ -104,14 +104,39 @@ def test_verify_greedy_ties_take_the_smallest_id():
     assert np.array_equal(nxt.cpu().numpy(), ref["next_token"])
 
 
+# Aligned rows of a multiple of four entries take the holding kernel: 512
+# threads keep 24 groups of four entries each in registers (49152 entries per
+# row) and 8 more in LDS (65536 in all) between the passes; the rest is read
+# twice.  The cases put V below, at and just past those boundaries; 4099 takes
+# the other kernel.
 @pytest.mark.parametrize("n,V,T", [(64, 4099, 1.0), (64, 4096, 0.7), (37, 129280, 1.0),
-                                   (8, 151936, 1.3)])
+                                   (8, 151936, 1.3), (16, 49152, 1.0), (16, 49156, 0.9),
+                                   (16, 65532, 1.1), (16, 65536, 1.0), (16, 65540, 0.8)])
 def test_accept_prob(n, V, T):
     _say(f"case accept prob n={n} V={V} T={T}")
     wl = make_accept_workload(n, V, seed=n + V)
     ref = O.accept_prob(wl["draft"], wl["target"], T)
     got = D.dspark_accept_prob(_dev(wl["draft"]), _dev(wl["target"]), T).cpu().numpy()
     assert np.abs(got.astype(np.float64) - ref).max() <= ACCEPT_ATOL
+
+
+def test_accept_prob_special_rows_across_held_regions():
+    # The special rows at V = 70000: identical, unrelated, disjoint supports
+    # split inside the LDS-held region, and a mask of every third entry.
+    _say("case accept prob special rows across the held regions")
+    V = 70000
+    rng = np.random.default_rng(6)
+    d = rng.normal(size=(4, V)).astype(np.float32)
+    t = d.copy()
+    t[1] = rng.normal(size=V)
+    d[2, 60000:] = -np.inf
+    t[2, :60000] = -np.inf
+    d[3, ::3] = -np.inf
+    ref = O.accept_prob(d, t)
+    got = D.dspark_accept_prob(_dev(d), _dev(t)).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.abs(got.astype(np.float64) - ref).max() <= ACCEPT_ATOL
+    assert abs(got[0] - 1.0) <= ACCEPT_ATOL and got[2] == 0.0
 
 
 def test_accept_prob_special_rows():
