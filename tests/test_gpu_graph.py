@@ -121,3 +121,24 @@ def test_rnn_draft_replays_in_a_graph(r, mode):
 
     _replay_and_compare(call, outs, ws)
     H.check_rnn_draft(wl, hd, outs[0].cpu().numpy())
+
+
+@pytest.mark.parametrize("V", [70000, 4099])
+def test_accept_prob_replays_in_a_graph(V):
+    # 70000: the kernel that holds part of each row pair on chip (LDS attribute
+    # set by the eager call before capture); 4099: the two-read kernel.
+    _say(f"case graph accept_prob V={V}")
+    from draft_head_step_amd.inputs import make_accept_workload
+    from oracle import dspark_oracle as O
+    wl = make_accept_workload(24, V, seed=V)
+    d = torch.from_numpy(wl["draft"]).to(DEV)
+    t = torch.from_numpy(wl["target"]).to(DEV)
+    out = torch.empty((24,), dtype=torch.float32, device=DEV)
+    scratch = torch.empty((16,), dtype=torch.uint8, device=DEV)   # no workspace: a stand-in
+
+    def call():
+        D.dspark_accept_prob(d, t, 0.9, out=out)
+
+    _replay_and_compare(call, [out], scratch)
+    ref = O.accept_prob(wl["draft"], wl["target"], 0.9)
+    assert np.abs(out.cpu().numpy().astype(np.float64) - ref).max() <= 2e-5
