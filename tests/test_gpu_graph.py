@@ -1,4 +1,5 @@
-"""The fused draft step and the RNN-head draft captured in a HIP graph.
+"""The fused draft step, the RNN-head draft and the acceptance probability
+captured in a HIP graph.
 
 The calls enqueue kernels only (no host synchronisation, no allocation, no
 memset nodes: every clear is a kernel), so a captured call can be replayed.
