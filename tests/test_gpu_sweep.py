@@ -7,7 +7,9 @@ layouts, with and without STS):
     inputs;
   * the RNN-head draft, tokens on the forced sequence and the last state;
   * the verification side (flattening and greedy accept / correct bit-exact,
-    the acceptance probability within 2e-5 as in test_gpu_verify).
+    the acceptance probability within 2e-5 as in test_gpu_verify);
+  * the acceptance probability alone at vocabularies up to 200000, across the
+    parts of a row pair its holding kernel keeps on chip.
 
 The draw is fixed (numpy seed), so a failing case can be re-run by its id.
 """
@@ -178,4 +180,35 @@ def test_verify_sweep(i, R, g, V, rate, T):
     aw = make_accept_workload(min(B, 16), V, seed=1800 + i)
     ra = O.accept_prob(aw["draft"], aw["target"], T)
     ga = D.dspark_accept_prob(dev(aw["draft"]), dev(aw["target"]), T).cpu().numpy()
+    assert np.abs(ga.astype(np.float64) - ra).max() <= 2e-5
+
+
+def _accept_cases(n_cases=12, seed=2024):
+    # V up to 200000, so the row pairs cross the parts the holding kernel keeps
+    # in registers (49152 entries) and LDS (65536) and stream the rest; about
+    # one V in four is not a multiple of four (the two-read kernel).
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n_cases):
+        V = int(rng.integers(2, 200_001))
+        if rng.random() < 0.75:
+            V = max(4, V // 4 * 4)
+        n = int(rng.integers(1, 13))
+        T = float(rng.choice([0.5, 0.8, 1.0, 1.7]))
+        out.append((i, n, V, T))
+    return out
+
+
+ACCEPT_CASES = _accept_cases()
+
+
+@pytest.mark.parametrize("i,n,V,T", ACCEPT_CASES, ids=[f"accept{c[0]}" for c in ACCEPT_CASES])
+def test_accept_prob_sweep(i, n, V, T):
+    print(f"case accept sweep{i}: n={n} V={V} T={T}", flush=True)
+    from draft_head_step_amd.inputs import make_accept_workload
+    from oracle import dspark_oracle as O
+    aw = make_accept_workload(n, V, seed=1900 + i)
+    ra = O.accept_prob(aw["draft"], aw["target"], T)
+    ga = D.dspark_accept_prob(torch.from_numpy(aw["draft"]).to(DEV),
+                              torch.from_numpy(aw["target"]).to(DEV), T).cpu().numpy()
     assert np.abs(ga.astype(np.float64) - ra).max() <= 2e-5
